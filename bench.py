@@ -1,0 +1,224 @@
+"""Throughput of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+
+A step is one moe_forward call over the whole hot path (router GEMM, routing, dispatch,
+grouped expert GEMMs with the shared expert, combine, aux loss) on one batch of seeded
+synthetic input already resident in HBM. The default workload is T=16384 tokens,
+d_model 2048, 256 SwiGLU experts (intermediate 512) at top-8 plus one shared SwiGLU
+expert, bf16 data with fp32 routing, capacity factor 1.0.
+
+Prints one JSON line: throughput (tokens/s), a roofline entry for the dominant kernel
+(the gated grouped GEMM: routed experts plus the shared expert), whose duration comes
+from HIP events recorded around that kernel on its own stream over a second timed pass,
+and the CPU oracle timed on a bounded token sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
+    return ap.parse_args()
+
+
+def gemm1_flops(w, kept):
+    """Algorithmic FLOPs of the first (gated) expert GEMM launch: 2*D*F per output per
+    matrix, two matrices (gate and up) for SwiGLU, one for GELU/linear, over the kept
+    rows; plus the shared expert over all T rows."""
+    mats = 2 if w.kind == "swiglu" else 1
+    F = w.F if w.kind != "linear" else w.D
+    fl = 2.0 * kept * w.D * F * mats
+    if w.shared_F:
+        fl += 2.0 * w.T * w.D * w.shared_F * 2
+    return fl
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_stable_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel, workload_name, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        recs = json.load(open(p))
+    except Exception:
+        return None
+    r = recs.get(f"{kernel}:{workload_name}")
+    if not r or r.get("source_hash") != src_hash:
+        return None
+    return r.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, n_tokens):
+    """The oracle (float64 NumPy) on the first n_tokens tokens of the workload, as a batch
+    of its own (its capacity recomputed for that batch size)."""
+    import numpy as np
+    import oracle.moe_oracle as om
+    from workloads import to_numpy_f32
+
+    x = to_numpy_f32(inp["x"][:n_tokens])
+    wts = {k: to_numpy_f32(inp[k]) for k in ("w_in", "w_up", "w_out", "b_in", "b_out") if k in inp}
+    shared = None
+    if "shared_w_in" in inp:
+        shared = {"w_in": to_numpy_f32(inp["shared_w_in"]), "w_up": to_numpy_f32(inp["shared_w_up"]),
+                  "w_out": to_numpy_f32(inp["shared_w_out"])}
+    kw = {}
+    if "logits" in inp:
+        kw["logits"] = to_numpy_f32(inp["logits"][:n_tokens])
+    else:
+        kw["w_router"] = to_numpy_f32(inp["w_router"])
+    t0 = time.perf_counter()
+    om.forward(x, w.k, w.kind, wts, cf=w.cf, residual=w.residual, shared=shared,
+               bf16=(w.dtype == "bf16"), **kw)
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    return n_tokens / dt, dt, threads
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "expert-parallel path is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_stable_amd import ops
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    inp = make_inputs(w)
+    g = {k: v.to("cuda") for k, v in inp.items()}
+    gen_s = time.perf_counter() - t_gen
+    ex = {"kind": w.kind}
+    for key in ("w_in", "w_up", "w_out", "b_in", "b_out"):
+        if key in g:
+            ex[key] = g[key]
+    shared = None
+    if w.shared_F:
+        shared = {"kind": "swiglu", "w_in": g["shared_w_in"][None], "w_up": g["shared_w_up"][None],
+                  "w_out": g["shared_w_out"][None]}
+    C = ops.capacity(w.T, w.k, w.E, w.cf)
+    kw = {"logits": g["logits"]} if "logits" in g else {"w_router": g["w_router"]}
+    out = ops.forward(g["x"], ex, k=w.k, capacity=C, shared=shared, use_residual=w.residual, **kw)
+    call = out["_call"]
+    torch.cuda.synchronize()
+    kept = int(out["kept"].sum().item())
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # second timed pass: HIP events around every kernel, recorded by the library on the
+    # stream each kernel is launched on
+    ops.profile_enable(True)
+    torch.cuda.synchronize()
+    p0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    prof_ms = (time.perf_counter() - p0) * 1e3 / args.steps
+    ops.profile_enable(False)
+    kern = ops.profile_read()
+
+    dom = "expert_gemm1_swiglu" if w.kind == "swiglu" else (
+        "expert_gemm1" if w.dtype == "bf16" else "expert_gemm1_f32")
+    cnt, tot = kern.get(dom, (0, 0.0))
+    dom_ms = tot / max(cnt, 1)
+    flops = gemm1_flops(w, kept)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
+    src_hash = source_hash("gemm_bf16.hip" if w.dtype == "bf16" else "gemm_f32.hip")
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic_record(dom, w.name, src_hash),
+                "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(dom_ms, 4)}
+
+    kernels = {k: {"launches_per_step": round(c / args.steps, 2), "avg_ms": round(t / c, 4)}
+               for k, (c, t) in kern.items()}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens or (256 if w.E >= 128 else 512)
+        n = min(n, w.T)
+        v, dt, threads = cpu_baseline(w, inp, n)
+        cpu = {"value": round(v, 2), "unit": "tokens/s", "cores": threads or os.cpu_count(),
+               "kind": "oracle", "seconds": round(dt, 2),
+               "sample": f"oracle forward (float64 NumPy) on the first {n} tokens of the "
+                         f"workload as a batch of their own"}
+
+    rec = {
+        "metric": "MoE layer fwd tokens/s (E=256,k=8,D=2048) + MFMA % / HBM GB/s of peak",
+        "value": round(w.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded normal inputs and random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.D, "experts": w.E, "top_k": w.k,
+                   "expert": w.kind, "d_hidden": w.F, "shared_hidden": w.shared_F,
+                   "capacity": C, "capacity_factor": w.cf, "kept_assignments": kept,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "profiled_ms_per_step": round(prof_ms, 4),
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,281 @@
+/*
+ * moe.h -- C ABI of libmoe.so, a capacity-limited sparse mixture-of-experts layer
+ * (forward and backward) for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as defined on the source pages:
+ *   router scores       s = x W_r                      ("Top-k MoE Router with Load
+ *                                                        Statistics", score equation)
+ *   fp32 softmax, top-k by score with exact ties to the lower expert index, gates
+ *   renormalised over the k choices                    (same page, alpha equation;
+ *                                                        "Sparse MoE Layer in NumPy",
+ *                                                        section 1 traps 1 and 7)
+ *   capacity C = ceil(T k cf / E)                       ("Sparse MoE Layer in NumPy",
+ *                                                        trap 2; "Module 7", expert_capacity)
+ *   position-priority slots: token order, then choice order; over-capacity
+ *   assignments are dropped and counted               ("Sparse MoE Layer in NumPy",
+ *                                                        trap 3, position_priority_dispatch)
+ *   expert MLP on each expert's slot buffer            ("Module 7", swiglu_expert;
+ *                                                        llm-atlas "Mixture of Experts",
+ *                                                        Expert module)
+ *   y = r x + shared(x) + sum over kept choices of gate * expert(x)
+ *                                                      ("Sparse MoE Layer in NumPy", trap 4;
+ *                                                        router page, y equation)
+ *   Switch aux loss E sum_e f_e P_e before any drop, f_e = count_e / (T k),
+ *   P_e = mean_t p[t, e]                               ("Sparse MoE Layer in NumPy", trap 6)
+ *   backward: dgate, dW, dx and the router-logit gradient through the quotient
+ *   rule and the softmax Jacobian, drops held constant ("Sparse MoE Layer in NumPy",
+ *                                                        trap 7 and section 2)
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked "device" are HIP device pointers (16-byte aligned); the others
+ *     are host pointers. The caller allocates every buffer, including the workspace;
+ *     the library never allocates or frees device memory.
+ *   - Tensors are row-major with unit inner stride; x and dy take a leading dimension
+ *     (elements). Expert weights are [E, in, out] row-major; biases [E, out].
+ *   - Inputs are never modified. Outputs are fully overwritten, except that rows
+ *     c >= used[e] of expert_out / hidden_cache are left unspecified.
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t, NULL = the default
+ *     stream) and returns without synchronising. Calls on different streams with
+ *     different workspaces are independent.
+ *   - Arguments are validated on the host before anything is launched; on failure
+ *     nothing is written and a status code is returned. MOE_ERR_HIP reports a failed
+ *     launch. Caller-supplied expert indices outside [0, E) are data errors found on
+ *     the device: moe_dispatch skips them and sets bit 0 of the device error word,
+ *     readable with moe_read_error.
+ *   - Index outputs are int32; the kept mask is one byte per assignment. An
+ *     assignment a = t*k + j is token t's j-th choice.
+ *   - Shape limits: 1 <= E <= 1024, 1 <= k <= min(E, 256). bf16 expert GEMMs need
+ *     d_model and d_hidden to be multiples of 64; fp32 ones multiples of 16.
+ *     Anything else returns MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* bad size, NULL required pointer, k outside [1, E]     */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (shape limits, MLP backward) */
+  MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the matching *_workspace_size    */
+  MOE_ERR_HIP = 4           /* a HIP launch or call failed                            */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_EXPERT_LINEAR = 0,    /* o = x W                        ("Sparse MoE Layer in
+                               NumPy", section 2 forward einsum); W [E, D, D]          */
+  MOE_EXPERT_GELU_MLP = 1,  /* o = GELU_erf(x W1 + b1) W2 + b2 (llm-atlas "Mixture of
+                               Experts", Expert); W1 [E,D,F], W2 [E,F,D], b1 [E,F],
+                               b2 [E,D]                                                */
+  MOE_EXPERT_SWIGLU = 2     /* o = (silu(x Wg) * (x Wu)) Wd   ("Module 7",
+                               swiglu_expert); Wg, Wu [E,D,F], Wd [E,F,D], no bias     */
+} moe_expert_kind_t;
+
+/* A set of experts of one kind and dtype. All pointers are device pointers. */
+typedef struct {
+  int32_t kind;         /* moe_expert_kind_t                                        */
+  int32_t dtype;        /* moe_dtype_t of weights, activations and expert outputs   */
+  int32_t num_experts;  /* E (1 for a shared expert)                                */
+  int32_t d_model;      /* D                                                        */
+  int32_t d_hidden;     /* F; must equal D for LINEAR                               */
+  const void* w_in;     /* LINEAR W, GELU W1, SWIGLU Wg                             */
+  const void* w_up;     /* SWIGLU Wu, else NULL                                     */
+  const void* w_out;    /* GELU W2, SWIGLU Wd, LINEAR NULL                          */
+  const void* b_in;     /* GELU b1 (may be NULL = no bias), else NULL               */
+  const void* b_out;    /* GELU b2 (may be NULL = no bias), else NULL               */
+} moe_experts_t;
+
+/* Library version string, e.g. "moe-gfx950 0.1". */
+const char* moe_version(void);
+
+/* Human-readable name of a status code. */
+const char* moe_status_string(int status);
+
+/*
+ * Capacity C = ceil(T * k * capacity_factor / E), computed exactly on the given double
+ * ("Sparse MoE Layer in NumPy", trap 2). No clamp: capacity_factor = 0 gives 0.
+ * Returns -1 if T < 1, k not in [1, E], capacity_factor negative or not finite, or
+ * the result does not fit in int32.
+ */
+int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double capacity_factor);
+
+/*
+ * Routing ("Top-k MoE Router with Load Statistics"; "Sparse MoE Layer in NumPy",
+ * top_k_gating and trap 6).
+ *   x         device, [T, ldx] of x_dtype; read only when w_router != NULL.
+ *   w_router  device, [D, E] of x_dtype, or NULL when the logits are supplied.
+ *   logits    device, [T, E] fp32. Written (= x W_r, fp32 accumulate) when w_router
+ *             is given, else read as the caller's scores.
+ *   topk_idx  device, [T, k] int32: experts in descending logit order, exact ties to
+ *             the lower index (-0.0 ties +0.0).
+ *   topk_gate device, [T, k] fp32: p[idx] / sum over the k of p[idx], p = fp32 softmax.
+ *   expert_count device, [E] int32: choices per expert before any drop.
+ *   prob_sum  device, [E] fp32: sum over tokens of p[t, e].
+ *   aux_loss  device, [1] fp32: E * sum_e (count_e / (T k)) * (prob_sum_e / T).
+ *   ws        device workspace of at least moe_route_workspace_size(T, E) bytes.
+ * Non-finite logits violate the precondition; results are then undefined.
+ */
+size_t moe_route_workspace_size(int32_t T, int32_t E);
+moe_status_t moe_route(const void* x, int32_t x_dtype, int64_t ldx, const void* w_router,
+                       float* logits, int32_t T, int32_t D, int32_t E, int32_t k,
+                       int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
+                       float* prob_sum, float* aux_loss, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * Position-priority dispatch ("Sparse MoE Layer in NumPy", trap 3 and
+ * position_priority_dispatch; "32. Sparse MoE Token Dispatch & Combine", step 2).
+ * Equal to visiting assignments a = t*k + j in increasing a and keeping each while its
+ * expert has fewer than C kept rows; computed with a device-wide prefix scan.
+ *   topk_idx    device, [T, k] int32 (indices outside [0, E) are skipped, flagged).
+ *   slot        device, [T, k] int32: position in the expert's buffer, -1 if dropped.
+ *   kept        device, [T, k] uint8: 1 if kept.
+ *   slot_assign device, [E, C] int32: the assignment a held by each slot, -1 if empty.
+ *   expert_used device, [E] int32: min(count, C).
+ *   expert_overflow device, [E] int32: count - used.
+ *   token_drops device, [T] int32: k minus the number of kept choices of the token.
+ *   ws          device workspace, >= moe_dispatch_workspace_size(T, k, E) bytes.
+ */
+size_t moe_dispatch_workspace_size(int32_t T, int32_t k, int32_t E);
+moe_status_t moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                          int32_t C, int32_t* slot, uint8_t* kept, int32_t* slot_assign,
+                          int32_t* expert_used, int32_t* expert_overflow,
+                          int32_t* token_drops, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Expert MLPs on the slot buffers ("Module 7", EducationalMoE expert loop and
+ * swiglu_expert; llm-atlas "Mixture of Experts", Expert), as grouped GEMMs.
+ * Row r < expert_used[e] of expert e is x[slot_assign[e, r] / k]. With
+ * slot_assign == NULL the experts run densely on all T rows (a shared expert:
+ * num_experts must be 1, expert_used ignored, outputs are [T, ...]).
+ *   x            device, [T, ldx] of ex->dtype.
+ *   hidden_cache device, [E, C, F] of ex->dtype (the activation fed to the second
+ *                GEMM), or NULL to keep it in the workspace. Ignored for LINEAR.
+ *   expert_out   device, [E, C, D] of ex->dtype, ungated.
+ *   ws           >= moe_expert_mlp_workspace_size(ex, rows) bytes, rows = C or T.
+ */
+size_t moe_expert_mlp_workspace_size(const moe_experts_t* ex, int32_t rows);
+moe_status_t moe_expert_mlp(const moe_experts_t* ex, const void* x, int64_t ldx, int32_t T,
+                            int32_t k, int32_t C, const int32_t* slot_assign,
+                            const int32_t* expert_used, void* hidden_cache,
+                            void* expert_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Gate-weighted combine ("Sparse MoE Layer in NumPy", trap 4; router page, y
+ * equation; "32. Sparse MoE Token Dispatch & Combine", step 6):
+ *   y[t] = residual[t] + shared_out[t] + sum_{j = 0..k-1, slot[t,j] >= 0}
+ *          topk_gate[t,j] * expert_out[topk_idx[t,j], slot[t,j]]
+ * accumulated in fp32 in exactly that order, rounded once to dt.
+ *   residual, shared_out  device, [T, D] of dt, each may be NULL (term omitted).
+ *   expert_out            device, [E, C, D] of dt.
+ * Precondition: 0 <= topk_idx < E and slot < C (violations are skipped).
+ */
+moe_status_t moe_combine(int32_t dt, const void* residual, const void* shared_out,
+                         const void* expert_out, const int32_t* topk_idx,
+                         const int32_t* slot, const float* topk_gate, int32_t T,
+                         int32_t k, int32_t E, int32_t C, int32_t D, void* y, void* stream);
+
+/* The whole forward pass in one call: routing, dispatch, experts, shared expert,
+ * combine and aux loss, all enqueued on one stream with no host synchronisation. */
+typedef struct {
+  const void* x;            /* device [T, ldx], experts.dtype                          */
+  int64_t ldx;
+  int32_t T;
+  const void* w_router;     /* device [D, E] experts.dtype, or NULL: logits are input   */
+  float* logits;            /* device [T, E] fp32, written or read (see moe_route)      */
+  moe_experts_t experts;    /* routed experts                                          */
+  moe_experts_t shared;     /* one always-on SWIGLU expert, or shared.w_in == NULL      */
+  int32_t k;
+  int32_t capacity;         /* C, e.g. from moe_capacity                               */
+  int32_t use_residual;     /* 1: y includes x                                         */
+  /* outputs (device) */
+  int32_t* topk_idx;        /* [T, k]   */
+  float* topk_gate;         /* [T, k]   */
+  int32_t* expert_count;    /* [E]      */
+  float* prob_sum;          /* [E]      */
+  float* aux_loss;          /* [1]      */
+  int32_t* slot;            /* [T, k]   */
+  uint8_t* kept;            /* [T, k]   */
+  int32_t* slot_assign;     /* [E, C]   */
+  int32_t* expert_used;     /* [E]      */
+  int32_t* expert_overflow; /* [E]      */
+  int32_t* token_drops;     /* [T]      */
+  void* hidden_cache;       /* [E, C, F] or NULL                                      */
+  void* expert_out;         /* [E, C, D], kept for the backward                       */
+  void* shared_out;         /* [T, D] or NULL (then kept in the workspace)            */
+  void* y;                  /* [T, D]   */
+} moe_forward_args_t;
+
+size_t moe_forward_workspace_size(const moe_forward_args_t* a);
+moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * Backward for single-linear experts ("Sparse MoE Layer in NumPy", section 2
+ * moe_backward and trap 7), discrete choices held constant:
+ *   dgate[a]  = kept_a <dy_t, expert_out[e_a, slot_a]>
+ *   dW[e]     = sum over kept a -> e of gate_a x_t^T dy_t  ([E, D, D]; 0 if unused)
+ *   dx[t]     = r dy_t + sum over kept a in t of gate_a dy_t W_e^T
+ *   dlogits   = p * (dp - <p, dp>), dp[t, idx_tj] = (dgate_tj - sum_r g_tr dgate_tr) / S_t,
+ *               S_t = sum_r p[t, idx_tr]; plus aux_grad_scale * (E/T) p (f - <p, f>),
+ *               f_e = count_e / (T k)
+ * Other expert kinds return MOE_ERR_UNSUPPORTED.
+ */
+typedef struct {
+  const void* dy;           /* device [T, ld]  */
+  const void* x;            /* device [T, ld]  */
+  int64_t ld;
+  int32_t T;
+  const float* logits;      /* device [T, E]   */
+  moe_experts_t experts;
+  int32_t k;
+  int32_t capacity;
+  int32_t use_residual;
+  float aux_grad_scale;
+  const int32_t* topk_idx;
+  const float* topk_gate;
+  const int32_t* expert_count;
+  const int32_t* slot;
+  const int32_t* slot_assign;
+  const int32_t* expert_used;
+  const void* expert_out;   /* [E, C, D] from the forward */
+  /* outputs (device) */
+  void* dx;                 /* [T, D]    */
+  void* dW;                 /* [E, D, D] */
+  float* dgate;             /* [T, k]    */
+  float* dlogits;           /* [T, E]    */
+} moe_backward_args_t;
+
+size_t moe_backward_workspace_size(const moe_backward_args_t* a);
+moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * Reads (synchronously: waits for `stream`) and returns the device error word kept in
+ * a workspace used by moe_dispatch or moe_forward; 0 means no data error. Bit 0: an
+ * expert index outside [0, E) was skipped. Returns -1 if the copy failed.
+ */
+int32_t moe_read_error(const void* ws, void* stream);
+
+/*
+ * Per-kernel timing for measurement. When enabled, every entry point brackets each
+ * kernel it launches with HIP events recorded on the same stream. moe_profile_read
+ * waits for those events and returns, per kernel name, the number of launches and
+ * the summed milliseconds; it then clears the record. Not thread-safe.
+ */
+void moe_profile_enable(int32_t on);
+int32_t moe_profile_read(char* names, int32_t name_stride, int32_t* counts, double* total_ms,
+                         int32_t max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

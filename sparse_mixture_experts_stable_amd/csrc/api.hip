@@ -1,0 +1,721 @@
+// C ABI of libmoe.so: host-side validation, workspace carve-up and the launch sequence of
+// every entry point. No entry point allocates device memory or synchronises (except
+// moe_read_error and moe_profile_read, which exist to wait).
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using namespace moe;
+
+// ------------------------------------------------------------------------------------
+// profiling hooks
+// ------------------------------------------------------------------------------------
+namespace {
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+hipEvent_t g_pending = nullptr;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+namespace moe_prof {
+void before(const char*, hipStream_t s) {
+  if (!g_prof) return;
+  g_pending = take_event();
+  if (g_pending) (void)hipEventRecord(g_pending, s);
+}
+void after(const char* name, hipStream_t s) {
+  if (!g_prof || !g_pending) return;
+  hipEvent_t stop = take_event();
+  if (!stop) return;
+  (void)hipEventRecord(stop, s);
+  g_recs.push_back({name, g_pending, stop});
+  g_pending = nullptr;
+}
+}  // namespace moe_prof
+
+// ------------------------------------------------------------------------------------
+// helpers
+// ------------------------------------------------------------------------------------
+namespace {
+
+inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+int elem_size(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+bool valid_kind(int k) {
+  return k == MOE_EXPERT_LINEAR || k == MOE_EXPERT_GELU_MLP || k == MOE_EXPERT_SWIGLU;
+}
+
+// Validates an expert set. Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED.
+moe_status_t check_experts(const moe_experts_t* ex) {
+  if (!ex) return MOE_ERR_INVALID_ARG;
+  if (!valid_kind(ex->kind) || !valid_dtype(ex->dtype)) return MOE_ERR_INVALID_ARG;
+  if (ex->num_experts < 1 || ex->d_model < 1 || ex->d_hidden < 1) return MOE_ERR_INVALID_ARG;
+  if (!ex->w_in) return MOE_ERR_INVALID_ARG;
+  if (ex->kind == MOE_EXPERT_LINEAR && ex->d_hidden != ex->d_model) return MOE_ERR_INVALID_ARG;
+  if (ex->kind == MOE_EXPERT_SWIGLU && (!ex->w_up || !ex->w_out)) return MOE_ERR_INVALID_ARG;
+  if (ex->kind == MOE_EXPERT_GELU_MLP && !ex->w_out) return MOE_ERR_INVALID_ARG;
+  const int q = ex->dtype == MOE_BF16 ? 64 : 16;
+  if (ex->d_model % q || ex->d_hidden % q) return MOE_ERR_UNSUPPORTED;
+  if (ex->dtype == MOE_F32 && ex->kind == MOE_EXPERT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t hidden_bytes(const moe_experts_t* ex, int rows) {
+  if (ex->kind == MOE_EXPERT_LINEAR) return 0;
+  return size_t(ex->num_experts) * rows * ex->d_hidden * elem_size(ex->dtype);
+}
+
+// The expert GEMM problems for one expert set. dense: slot_assign == NULL (all T rows).
+struct ExpertPlan {
+  GemmProblem g1, g2;       // bf16
+  GemmF32Problem f1, f2;    // fp32
+  bool two_stage;
+};
+
+void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, int k, int C,
+                  const int32_t* slot_assign, const int32_t* used, void* hidden, void* out,
+                  ExpertPlan& pl) {
+  const bool dense = slot_assign == nullptr;
+  const int rows = dense ? T : C;
+  const int E = ex->num_experts, D = ex->d_model, F = ex->d_hidden;
+  pl.two_stage = ex->kind != MOE_EXPERT_LINEAR;
+  if (ex->dtype == MOE_BF16) {
+    GemmProblem a{};
+    a.A = x;
+    a.lda = ldx;
+    a.a_gstride = 0;
+    a.row_map = slot_assign;
+    a.row_map_ld = C;
+    a.row_div = k;
+    a.m_count = dense ? nullptr : used;
+    a.m_const = T;
+    a.m_tiles = (rows + kBf16BM - 1) / kBf16BM;
+    a.B0 = ex->w_in;
+    a.B1 = ex->kind == MOE_EXPERT_SWIGLU ? ex->w_up : nullptr;
+    a.b_gstride = int64_t(D) * (pl.two_stage ? F : D);
+    a.bias = ex->kind == MOE_EXPERT_GELU_MLP ? ex->b_in : nullptr;
+    a.bias_gstride = F;
+    a.K = D;
+    a.N = pl.two_stage ? F : D;
+    a.groups = E;
+    a.epi = ex->kind == MOE_EXPERT_GELU_MLP ? EPI_GELU_BIAS
+          : ex->kind == MOE_EXPERT_SWIGLU  ? EPI_SWIGLU
+                                           : EPI_STORE;
+    a.out_f32 = 0;
+    a.C = pl.two_stage ? hidden : out;
+    a.ldc = a.N;
+    a.c_gstride = int64_t(rows) * a.N;
+    pl.g1 = a;
+    if (pl.two_stage) {
+      GemmProblem b{};
+      b.A = hidden;
+      b.lda = F;
+      b.a_gstride = int64_t(rows) * F;
+      b.row_map = nullptr;
+      b.row_div = 1;
+      b.m_count = dense ? nullptr : used;
+      b.m_const = T;
+      b.m_tiles = a.m_tiles;
+      b.B0 = ex->w_out;
+      b.b_gstride = int64_t(F) * D;
+      b.bias = ex->kind == MOE_EXPERT_GELU_MLP ? ex->b_out : nullptr;
+      b.bias_gstride = D;
+      b.K = F;
+      b.N = D;
+      b.groups = E;
+      b.epi = ex->kind == MOE_EXPERT_GELU_MLP ? EPI_BIAS : EPI_STORE;
+      b.C = out;
+      b.ldc = D;
+      b.c_gstride = int64_t(rows) * D;
+      pl.g2 = b;
+    }
+  } else {
+    GemmF32Problem a{};
+    a.A = static_cast<const float*>(x);
+    a.lda = ldx;
+    a.row_map = slot_assign;
+    a.row_map_ld = C;
+    a.row_div = k;
+    a.g_count = dense ? nullptr : used;
+    a.g_const = T;
+    a.m_tiles = (rows + kF32BM - 1) / kF32BM;
+    a.B = static_cast<const float*>(ex->w_in);
+    a.N = pl.two_stage ? F : D;
+    a.ldb = a.N;
+    a.b_gstride = int64_t(D) * a.N;
+    a.bias = static_cast<const float*>(ex->kind == MOE_EXPERT_GELU_MLP ? ex->b_in : nullptr);
+    a.bias_gstride = F;
+    a.K = D;
+    a.groups = E;
+    a.epi = ex->kind == MOE_EXPERT_GELU_MLP ? EPI_GELU_BIAS : EPI_STORE;
+    a.C = static_cast<float*>(pl.two_stage ? hidden : out);
+    a.ldc = a.N;
+    a.c_gstride = int64_t(rows) * a.N;
+    pl.f1 = a;
+    if (pl.two_stage) {
+      GemmF32Problem b{};
+      b.A = static_cast<const float*>(hidden);
+      b.lda = F;
+      b.a_gstride = int64_t(rows) * F;
+      b.row_div = 1;
+      b.g_count = dense ? nullptr : used;
+      b.g_const = T;
+      b.m_tiles = a.m_tiles;
+      b.B = static_cast<const float*>(ex->w_out);
+      b.ldb = D;
+      b.b_gstride = int64_t(F) * D;
+      b.bias = static_cast<const float*>(ex->b_out);
+      b.bias_gstride = D;
+      b.K = F;
+      b.N = D;
+      b.groups = E;
+      b.epi = EPI_BIAS;
+      b.C = static_cast<float*>(out);
+      b.ldc = D;
+      b.c_gstride = int64_t(rows) * D;
+      pl.f2 = b;
+    }
+  }
+}
+
+// Runs one or two expert sets (routed + shared) with shared launches per stage.
+moe_status_t run_experts(const ExpertPlan* plans, const moe_experts_t* const* exs, int n,
+                         hipStream_t s) {
+  if (exs[0]->dtype == MOE_BF16) {
+    GemmBatch b1{};
+    b1.nprob = n;
+    for (int i = 0; i < n; ++i) b1.p[i] = plans[i].g1;
+    const bool gated = exs[0]->kind == MOE_EXPERT_SWIGLU;
+    if (n == 2 && (exs[1]->kind == MOE_EXPERT_SWIGLU) != gated) {
+      // different kinds cannot share a launch
+      for (int i = 0; i < n; ++i) {
+        GemmBatch one{};
+        one.nprob = 1;
+        one.p[0] = plans[i].g1;
+        moe_status_t st = launch_gemm_bf16(one, exs[i]->kind == MOE_EXPERT_SWIGLU, "expert_gemm1", s);
+        if (st != MOE_OK) return st;
+      }
+    } else {
+      moe_status_t st = launch_gemm_bf16(b1, gated, gated ? "expert_gemm1_swiglu" : "expert_gemm1", s);
+      if (st != MOE_OK) return st;
+    }
+    GemmBatch b2{};
+    for (int i = 0; i < n; ++i)
+      if (plans[i].two_stage) b2.p[b2.nprob++] = plans[i].g2;
+    if (b2.nprob) return launch_gemm_bf16(b2, false, "expert_gemm2", s);
+    return MOE_OK;
+  }
+  for (int i = 0; i < n; ++i) {
+    ExpertPlan p = plans[i];
+    moe_status_t st = launch_gemm_f32(p.f1, A_ROWS, B_KN, "expert_gemm1_f32", s);
+    if (st != MOE_OK) return st;
+    if (p.two_stage) {
+      st = launch_gemm_f32(p.f2, A_ROWS, B_KN, "expert_gemm2_f32", s);
+      if (st != MOE_OK) return st;
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status_t router_gemm(const void* x, int dt, int64_t ldx, const void* w, int T, int D, int E,
+                         float* logits, hipStream_t s) {
+  if (dt == MOE_BF16 && D % kBf16BK == 0 && E % 8 == 0) {
+    GemmBatch b{};
+    b.nprob = 1;
+    GemmProblem& p = b.p[0];
+    p.A = x;
+    p.lda = ldx;
+    p.row_div = 1;
+    p.m_const = T;
+    p.m_tiles = (T + kBf16BM - 1) / kBf16BM;
+    p.B0 = w;
+    p.K = D;
+    p.N = E;
+    p.groups = 1;
+    p.epi = EPI_STORE;
+    p.out_f32 = 1;
+    p.C = logits;
+    p.ldc = E;
+    return launch_gemm_bf16(b, false, "router_gemm", s);
+  }
+  if (dt == MOE_F32 && D % kF32BK == 0 && E % 4 == 0 && ldx % 4 == 0) {
+    GemmF32Problem p{};
+    p.A = static_cast<const float*>(x);
+    p.lda = ldx;
+    p.row_div = 1;
+    p.g_const = T;
+    p.m_tiles = (T + kF32BM - 1) / kF32BM;
+    p.B = static_cast<const float*>(w);
+    p.ldb = E;
+    p.K = D;
+    p.N = E;
+    p.groups = 1;
+    p.epi = EPI_STORE;
+    p.C = logits;
+    p.ldc = E;
+    return launch_gemm_f32(p, A_ROWS, B_KN, "router_gemm_f32", s);
+  }
+  return launch_router_simt(x, dt, ldx, w, T, D, E, logits, s);
+}
+
+bool route_shape_ok(int T, int E, int k) {
+  return T >= 1 && E >= 1 && E <= 1024 && k >= 1 && k <= E;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------
+// SIMT router GEMM for shapes the MFMA tiles do not cover
+// ------------------------------------------------------------------------------------
+namespace moe {
+template <typename TX>
+__global__ __launch_bounds__(64) void router_simt_kernel(const TX* __restrict__ x, int64_t ldx,
+                                                         const TX* __restrict__ w, int D, int E,
+                                                         float* __restrict__ logits) {
+  const int t = blockIdx.x;
+  const int e = blockIdx.y * 64 + threadIdx.x;
+  if (e >= E) return;
+  float acc = 0.f;
+  for (int d = 0; d < D; ++d) {
+    float xv, wv;
+    if constexpr (sizeof(TX) == 2) {
+      xv = bf16_to_f32(x[size_t(t) * ldx + d]);
+      wv = bf16_to_f32(w[size_t(d) * E + e]);
+    } else {
+      xv = x[size_t(t) * ldx + d];
+      wv = w[size_t(d) * E + e];
+    }
+    acc = fmaf(xv, wv, acc);
+  }
+  logits[size_t(t) * E + e] = acc;
+}
+
+moe_status_t launch_router_simt(const void* x, int dtype, int64_t ldx, const void* w, int T,
+                                int D, int E, float* logits, hipStream_t s) {
+  const dim3 grid(T, (E + 63) / 64), block(64);
+  if (dtype == MOE_BF16) {
+    MOE_LAUNCH("router_simt", router_simt_kernel<bf16_t>, grid, block, 0, s,
+               static_cast<const bf16_t*>(x), ldx, static_cast<const bf16_t*>(w), D, E, logits);
+  } else {
+    MOE_LAUNCH("router_simt", router_simt_kernel<float>, grid, block, 0, s,
+               static_cast<const float*>(x), ldx, static_cast<const float*>(w), D, E, logits);
+  }
+  return MOE_OK;
+}
+}  // namespace moe
+
+// ------------------------------------------------------------------------------------
+// C ABI
+// ------------------------------------------------------------------------------------
+extern "C" {
+
+const char* moe_version(void) { return "moe-gfx950 0.1"; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double cf) {
+  if (T < 1 || T >= (int64_t(1) << 40) || E < 1 || k < 1 || k > E) return -1;
+  if (!std::isfinite(cf) || cf < 0.0) return -1;
+  if (cf == 0.0) return 0;
+  // cf = mant * 2^ex exactly, mant a 53-bit integer
+  int ex = 0;
+  const double fr = std::frexp(cf, &ex);
+  const uint64_t mant = static_cast<uint64_t>(std::ldexp(fr, 53));
+  ex -= 53;
+  unsigned __int128 num = static_cast<unsigned __int128>(T) * static_cast<unsigned>(k) * mant;
+  if (ex > 0) {
+    if (ex > 40) return -1;
+    num <<= ex;
+  }
+  unsigned __int128 q = (num + static_cast<unsigned>(E) - 1) / static_cast<unsigned>(E);
+  if (ex < 0) {
+    const int sh = -ex;
+    if (sh >= 127) {
+      q = q > 0 ? 1 : 0;
+    } else {
+      const unsigned __int128 one = 1;
+      q = (q + (one << sh) - 1) >> sh;
+    }
+  }
+  if (q > static_cast<unsigned __int128>(INT32_MAX)) return -1;
+  return static_cast<int64_t>(q);
+}
+
+size_t moe_route_workspace_size(int32_t T, int32_t E) {
+  if (T < 1 || E < 1) return 0;
+  return carve_route_ws(nullptr, T, E).bytes;
+}
+
+moe_status_t moe_route(const void* x, int32_t x_dtype, int64_t ldx, const void* w_router,
+                       float* logits, int32_t T, int32_t D, int32_t E, int32_t k,
+                       int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
+                       float* prob_sum, float* aux_loss, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!route_shape_ok(T, E, k)) return k > 256 && k <= E ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG;
+  if (k > 256) return MOE_ERR_UNSUPPORTED;
+  if (!logits || !topk_idx || !topk_gate || !expert_count || !prob_sum || !aux_loss || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (w_router) {
+    if (!x || !valid_dtype(x_dtype) || D < 1 || ldx < D) return MOE_ERR_INVALID_ARG;
+  }
+  if (ws_bytes < moe_route_workspace_size(T, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  RouteWs w = carve_route_ws(ws, T, E);
+  moe_status_t st;
+  if (w_router) {
+    st = router_gemm(x, x_dtype, ldx, w_router, T, D, E, logits, s);
+    if (st != MOE_OK) return st;
+  }
+  st = launch_route(logits, T, E, k, topk_idx, topk_gate, w, s);
+  if (st != MOE_OK) return st;
+  return launch_reduce_scan(T, k, E, -1, true, expert_count, prob_sum, aux_loss, nullptr, nullptr,
+                            nullptr, w, s);
+}
+
+size_t moe_dispatch_workspace_size(int32_t T, int32_t k, int32_t E) {
+  if (T < 1 || E < 1 || k < 1) return 0;
+  return carve_route_ws(nullptr, T, E).bytes;
+}
+
+moe_status_t moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t C,
+                          int32_t* slot, uint8_t* kept, int32_t* slot_assign,
+                          int32_t* expert_used, int32_t* expert_overflow,
+                          int32_t* token_drops, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 1 || E < 1 || E > 1024 || k < 1 || C < 0) return MOE_ERR_INVALID_ARG;
+  if (!topk_idx || !slot || !kept || !expert_used || !expert_overflow || !token_drops || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (C > 0 && !slot_assign) return MOE_ERR_INVALID_ARG;
+  if (int64_t(T) * k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < moe_dispatch_workspace_size(T, k, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  RouteWs w = carve_route_ws(ws, T, E);
+  moe_status_t st = launch_count(topk_idx, T, k, E, w, s);
+  if (st != MOE_OK) return st;
+  // expert_count is not an output of moe_dispatch; the totals land in fp scratch space
+  st = launch_reduce_scan(T, k, E, C, false, reinterpret_cast<int32_t*>(w.fp), nullptr, nullptr,
+                          expert_used, expert_overflow, slot_assign, w, s);
+  if (st != MOE_OK) return st;
+  return launch_assign(topk_idx, T, k, E, C, slot, kept, slot_assign, token_drops, w, s);
+}
+
+size_t moe_expert_mlp_workspace_size(const moe_experts_t* ex, int32_t rows) {
+  if (!ex || rows < 0) return 0;
+  return align_up(hidden_bytes(ex, rows), 256) + 256;
+}
+
+moe_status_t moe_expert_mlp(const moe_experts_t* ex, const void* x, int64_t ldx, int32_t T,
+                            int32_t k, int32_t C, const int32_t* slot_assign,
+                            const int32_t* expert_used, void* hidden_cache, void* expert_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_experts(ex);
+  if (st != MOE_OK) return st;
+  if (!x || !expert_out || T < 1 || ldx < ex->d_model) return MOE_ERR_INVALID_ARG;
+  const bool dense = slot_assign == nullptr;
+  if (dense && ex->num_experts != 1) return MOE_ERR_INVALID_ARG;
+  if (!dense && (k < 1 || C < 0 || !expert_used)) return MOE_ERR_INVALID_ARG;
+  if (ldx % (ex->dtype == MOE_BF16 ? 8 : 4)) return MOE_ERR_UNSUPPORTED;
+  const int rows = dense ? T : C;
+  void* hidden = hidden_cache;
+  if (!hidden && hidden_bytes(ex, rows)) {
+    if (!ws || ws_bytes < moe_expert_mlp_workspace_size(ex, rows)) return MOE_ERR_WORKSPACE;
+    hidden = ws;
+  }
+  if (rows == 0) return MOE_OK;
+  ExpertPlan pl;
+  plan_experts(ex, x, ldx, T, k, C, slot_assign, expert_used, hidden, expert_out, pl);
+  const moe_experts_t* exs[1] = {ex};
+  return run_experts(&pl, exs, 1, S(stream));
+}
+
+moe_status_t moe_combine(int32_t dt, const void* residual, const void* shared_out,
+                         const void* expert_out, const int32_t* topk_idx, const int32_t* slot,
+                         const float* topk_gate, int32_t T, int32_t k, int32_t E, int32_t C,
+                         int32_t D, void* y, void* stream) {
+  if (!valid_dtype(dt) || T < 1 || k < 1 || E < 1 || C < 0 || D < 1) return MOE_ERR_INVALID_ARG;
+  if (!topk_idx || !slot || !topk_gate || !y || (C > 0 && !expert_out)) return MOE_ERR_INVALID_ARG;
+  const int V = dt == MOE_BF16 ? 8 : 4;
+  const int per_row = D / V;
+  if (D % V || (per_row > 256 && per_row % 256) || (per_row < 256 && 256 % per_row))
+    return MOE_ERR_UNSUPPORTED;
+  return launch_combine(dt, residual, D, shared_out, expert_out, topk_idx, slot, topk_gate, T, k,
+                        E, C, D, y, S(stream));
+}
+
+// ---- forward ------------------------------------------------------------------------
+namespace {
+struct FwdWs {
+  RouteWs rw;
+  void* hidden;
+  void* shared_hidden;
+  void* shared_out;
+  size_t bytes;
+};
+
+FwdWs carve_fwd(const moe_forward_args_t* a, void* ws) {
+  FwdWs f{};
+  const int E = a->experts.num_experts;
+  f.rw = carve_route_ws(ws, a->T, E);
+  size_t off = f.rw.bytes;
+  char* base = static_cast<char*>(ws);
+  f.hidden = nullptr;
+  if (!a->hidden_cache) {
+    const size_t hb = hidden_bytes(&a->experts, a->capacity);
+    if (hb) {
+      f.hidden = base ? base + off : nullptr;
+      off = align_up(off + hb, 256);
+    }
+  }
+  f.shared_hidden = nullptr;
+  f.shared_out = nullptr;
+  if (a->shared.w_in) {
+    f.shared_hidden = base ? base + off : nullptr;
+    off = align_up(off + hidden_bytes(&a->shared, a->T), 256);
+    if (!a->shared_out) {
+      f.shared_out = base ? base + off : nullptr;
+      off = align_up(off + size_t(a->T) * a->experts.d_model * elem_size(a->experts.dtype), 256);
+    }
+  }
+  f.bytes = off;
+  return f;
+}
+
+moe_status_t check_forward(const moe_forward_args_t* a) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = check_experts(&a->experts);
+  if (st != MOE_OK) return st;
+  const int T = a->T, E = a->experts.num_experts, k = a->k, C = a->capacity;
+  const int D = a->experts.d_model;
+  if (!route_shape_ok(T, E, k) || C < 0) return MOE_ERR_INVALID_ARG;
+  if (k > 256 || int64_t(T) * k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!a->x || a->ldx < D || !a->logits || !a->y) return MOE_ERR_INVALID_ARG;
+  if (!a->topk_idx || !a->topk_gate || !a->expert_count || !a->prob_sum || !a->aux_loss ||
+      !a->slot || !a->kept || !a->expert_used || !a->expert_overflow || !a->token_drops ||
+      !a->expert_out || (C > 0 && !a->slot_assign))
+    return MOE_ERR_INVALID_ARG;
+  if (a->ldx % (a->experts.dtype == MOE_BF16 ? 8 : 4)) return MOE_ERR_UNSUPPORTED;
+  if (a->shared.w_in) {
+    st = check_experts(&a->shared);
+    if (st != MOE_OK) return st;
+    if (a->shared.kind != MOE_EXPERT_SWIGLU || a->shared.num_experts != 1 ||
+        a->shared.dtype != a->experts.dtype || a->shared.d_model != D)
+      return MOE_ERR_UNSUPPORTED;
+  }
+  const int V = a->experts.dtype == MOE_BF16 ? 8 : 4;
+  const int per_row = D / V;
+  if ((per_row > 256 && per_row % 256) || (per_row < 256 && 256 % per_row)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+}  // namespace
+
+size_t moe_forward_workspace_size(const moe_forward_args_t* a) {
+  if (!a || a->T < 1 || a->experts.num_experts < 1) return 0;
+  return carve_fwd(a, nullptr).bytes;
+}
+
+moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_forward(a);
+  if (st != MOE_OK) return st;
+  if (!ws || ws_bytes < moe_forward_workspace_size(a)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  const int T = a->T, E = a->experts.num_experts, k = a->k, C = a->capacity;
+  const int D = a->experts.d_model;
+  FwdWs f = carve_fwd(a, ws);
+  if (a->w_router) {
+    st = router_gemm(a->x, a->experts.dtype, a->ldx, a->w_router, T, D, E, a->logits, s);
+    if (st != MOE_OK) return st;
+  }
+  st = launch_route(a->logits, T, E, k, a->topk_idx, a->topk_gate, f.rw, s);
+  if (st != MOE_OK) return st;
+  st = launch_reduce_scan(T, k, E, C, true, a->expert_count, a->prob_sum, a->aux_loss,
+                          a->expert_used, a->expert_overflow, a->slot_assign, f.rw, s);
+  if (st != MOE_OK) return st;
+  st = launch_assign(a->topk_idx, T, k, E, C, a->slot, a->kept, a->slot_assign, a->token_drops,
+                     f.rw, s);
+  if (st != MOE_OK) return st;
+
+  ExpertPlan plans[2];
+  const moe_experts_t* exs[2] = {&a->experts, &a->shared};
+  int n = 0;
+  if (C > 0) {
+    plan_experts(&a->experts, a->x, a->ldx, T, k, C, a->slot_assign, a->expert_used,
+                 a->hidden_cache ? a->hidden_cache : f.hidden, a->expert_out, plans[n]);
+    exs[n++] = &a->experts;
+  }
+  void* shared_out = nullptr;
+  if (a->shared.w_in) {
+    shared_out = a->shared_out ? a->shared_out : f.shared_out;
+    plan_experts(&a->shared, a->x, a->ldx, T, 1, 0, nullptr, nullptr, f.shared_hidden,
+                 shared_out, plans[n]);
+    exs[n++] = &a->shared;
+  }
+  if (n) {
+    st = run_experts(plans, exs, n, s);
+    if (st != MOE_OK) return st;
+  }
+  return launch_combine(a->experts.dtype, a->use_residual ? a->x : nullptr, a->ldx, shared_out,
+                        a->expert_out, a->topk_idx, a->slot, a->topk_gate, T, k, E, C, D, a->y,
+                        s);
+}
+
+// ---- backward -----------------------------------------------------------------------
+size_t moe_backward_workspace_size(const moe_backward_args_t* a) {
+  if (!a || a->T < 1 || a->experts.num_experts < 1) return 0;
+  return align_up(size_t(a->experts.num_experts) * a->capacity * a->experts.d_model * 4, 256) + 256;
+}
+
+moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = check_experts(&a->experts);
+  if (st != MOE_OK) return st;
+  if (a->experts.kind != MOE_EXPERT_LINEAR || a->experts.dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  const int T = a->T, E = a->experts.num_experts, k = a->k, C = a->capacity;
+  const int D = a->experts.d_model;
+  if (!route_shape_ok(T, E, k) || C < 0) return MOE_ERR_INVALID_ARG;
+  if (k > 256) return MOE_ERR_UNSUPPORTED;
+  if (!a->dy || !a->x || a->ld < D || !a->logits || !a->topk_idx || !a->topk_gate ||
+      !a->expert_count || !a->slot || !a->expert_used || !a->dx || !a->dW || !a->dgate ||
+      !a->dlogits || (C > 0 && (!a->slot_assign || !a->expert_out)))
+    return MOE_ERR_INVALID_ARG;
+  if (a->ld != D) return MOE_ERR_UNSUPPORTED;
+  const int per_row = D / 4;
+  if ((per_row > 256 && per_row % 256) || (per_row < 256 && 256 % per_row)) return MOE_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < moe_backward_workspace_size(a)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  const float* dy = static_cast<const float*>(a->dy);
+  const float* x = static_cast<const float*>(a->x);
+  float* dxe = static_cast<float*>(ws);
+
+  st = launch_dgate_router_bwd(dy, static_cast<const float*>(a->expert_out), a->logits,
+                               a->topk_idx, a->topk_gate, a->slot, a->expert_count, T, k, E, C,
+                               D, a->aux_grad_scale, a->dgate, a->dlogits, s);
+  if (st != MOE_OK) return st;
+
+  // dX_e = dY_e W_e^T on the slot rows, then the gate-weighted scatter-sum (+ dy)
+  GemmF32Problem px{};
+  px.A = dy;
+  px.lda = a->ld;
+  px.row_map = a->slot_assign;
+  px.row_map_ld = C;
+  px.row_div = k;
+  px.g_count = a->expert_used;
+  px.m_tiles = (C + kF32BM - 1) / kF32BM;
+  px.B = static_cast<const float*>(a->experts.w_in);
+  px.ldb = D;
+  px.b_gstride = int64_t(D) * D;
+  px.K = D;
+  px.N = D;
+  px.groups = E;
+  px.epi = EPI_STORE;
+  px.C = dxe;
+  px.ldc = D;
+  px.c_gstride = int64_t(C) * D;
+  if (C > 0) {
+    st = launch_gemm_f32(px, A_ROWS, B_NK, "bwd_dx_gemm", s);
+    if (st != MOE_OK) return st;
+  }
+  st = launch_combine(MOE_F32, a->use_residual ? a->dy : nullptr, a->ld, nullptr, dxe, a->topk_idx,
+                      a->slot, a->topk_gate, T, k, E, C, D, a->dx, s);
+  if (st != MOE_OK) return st;
+
+  // dW_e = X_e^T (gate * dY_e), K = used_e gathered rows; unused experts get 0
+  GemmF32Problem pw{};
+  pw.A = x;
+  pw.lda = a->ld;
+  pw.row_map = a->slot_assign;
+  pw.row_map_ld = C;
+  pw.row_div = k;
+  pw.g_count = C > 0 ? a->expert_used : nullptr;
+  pw.g_const = 0;
+  pw.M = D;
+  pw.m_tiles = (D + kF32BM - 1) / kF32BM;
+  pw.B = dy;
+  pw.ldb = a->ld;
+  pw.gate = a->topk_gate;
+  pw.N = D;
+  pw.groups = E;
+  pw.epi = EPI_STORE;
+  pw.C = static_cast<float*>(a->dW);
+  pw.ldc = D;
+  pw.c_gstride = int64_t(D) * D;
+  return launch_gemm_f32(pw, A_KROWS, B_KROWS_GATE, "bwd_dw_gemm", s);
+}
+
+// ---- errors and profiling -------------------------------------------------------------
+int32_t moe_read_error(const void* ws, void* stream) {
+  if (!ws) return -1;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, S(stream)) != hipSuccess) return -1;
+  if (hipStreamSynchronize(S(stream)) != hipSuccess) return -1;
+  return v;
+}
+
+void moe_profile_enable(int32_t on) { g_prof = on != 0; }
+
+int32_t moe_profile_read(char* names, int32_t name_stride, int32_t* counts, double* total_ms,
+                         int32_t max_entries) {
+  std::vector<std::string> order;
+  std::map<std::string, std::pair<int, double>> acc;
+  for (auto& r : g_recs) {
+    float ms = 0.f;
+    (void)hipEventSynchronize(r.stop);
+    (void)hipEventElapsedTime(&ms, r.start, r.stop);
+    auto it = acc.find(r.name);
+    if (it == acc.end()) {
+      order.push_back(r.name);
+      acc[r.name] = {1, double(ms)};
+    } else {
+      it->second.first += 1;
+      it->second.second += ms;
+    }
+    g_pool.push_back(r.start);
+    g_pool.push_back(r.stop);
+  }
+  g_recs.clear();
+  int n = 0;
+  for (auto& nm : order) {
+    if (n >= max_entries) break;
+    if (names && name_stride > 0) {
+      std::strncpy(names + size_t(n) * name_stride, nm.c_str(), name_stride - 1);
+      names[size_t(n) * name_stride + name_stride - 1] = 0;
+    }
+    if (counts) counts[n] = acc[nm].first;
+    if (total_ms) total_ms[n] = acc[nm].second;
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+// Gate-weighted combine and the router-side backward, both HBM-bound.
+//
+// combine_kernel: y_t = residual_t + shared_t + sum_{j kept} gate_tj * o[e_tj, slot_tj]
+// ("Sparse MoE Layer in NumPy", trap 4: dropped choices leave the residual untouched;
+// "Top-k MoE Router with Load Statistics", y equation; "32. Sparse MoE Token Dispatch &
+// Combine", step 6), accumulated in fp32 in that fixed order and rounded once. Each
+// thread owns 16 bytes of one output row; a row's expert outputs are gathered straight
+// from the [E, C, D] slot buffers, so no token-ordered copy of them is ever written.
+//
+// dgate_router_kernel: one wavefront per token ("Sparse MoE Layer in NumPy", section 2
+// moe_backward and trap 7):
+//   dgate_tj = kept_tj <dy_t, o[e_tj, slot_tj]>
+//   dq_j = (dgate_j - sum_r g_r dgate_r) / S_t,  S_t = sum_r p[t, e_tr]
+//   dlogits[t, i] = p_i (dp_i - sum_l p_l dp_l), dp[t, e_tj] = dq_j
+//   (+ aux_scale * (E / T) p_i (f_i - sum_l f_l p_l), f = count / (T k))
+
+#include "internal.h"
+
+namespace moe {
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const void* p, float* v) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  }
+  __device__ static void store(void* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <>
+struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const void* p, float* v) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(void* p, const float* v) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ residual,
+                                                      const T* __restrict__ shared_out,
+                                                      const T* __restrict__ expert_out,
+                                                      const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ slot,
+                                                      const float* __restrict__ gate, int T_,
+                                                      int k, int E, int C, int D, int64_t ldr,
+                                                      T* __restrict__ y) {
+  constexpr int V = Vec<T>::N;
+  const int per_row = D / V;
+  const int rows_per_block = 256 / per_row;  // >= 1 (per_row <= 256 or a multiple)
+  int t, col;
+  if (per_row >= 256) {
+    const int chunks = per_row / 256;
+    t = blockIdx.x / chunks;
+    col = ((blockIdx.x % chunks) * 256 + threadIdx.x) * V;
+  } else {
+    t = blockIdx.x * rows_per_block + threadIdx.x / per_row;
+    col = (threadIdx.x % per_row) * V;
+    if (threadIdx.x >= rows_per_block * per_row) return;
+  }
+  if (t >= T_) return;
+  float acc[V];
+  if (residual) {
+    Vec<T>::load(residual + size_t(t) * ldr + col, acc);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  }
+  if (shared_out) {
+    float v[V];
+    Vec<T>::load(shared_out + size_t(t) * D + col, v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] += v[i];
+  }
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[size_t(t) * k + j];
+    const int s = slot[size_t(t) * k + j];
+    if (s < 0 || s >= C || e < 0 || e >= E) continue;
+    const float g = gate[size_t(t) * k + j];
+    float v[V];
+    Vec<T>::load(expert_out + (size_t(e) * C + s) * D + col, v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+  }
+  Vec<T>::store(y + size_t(t) * D + col, acc);
+}
+
+moe_status_t launch_combine(int dt, const void* residual, int64_t ldr, const void* shared_out,
+                            const void* expert_out, const int32_t* idx, const int32_t* slot,
+                            const float* gate, int T, int k, int E, int C, int D, void* y,
+                            hipStream_t s) {
+  const int V = dt == MOE_BF16 ? 8 : 4;
+  const int per_row = D / V;
+  int blocks;
+  if (per_row >= 256) {
+    blocks = T * (per_row / 256);
+  } else {
+    const int rpb = 256 / per_row;
+    blocks = (T + rpb - 1) / rpb;
+  }
+  if (dt == MOE_BF16) {
+    MOE_LAUNCH("combine", combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s,
+               static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(shared_out),
+               static_cast<const bf16_t*>(expert_out), idx, slot, gate, T, k, E, C, D,
+               ldr, static_cast<bf16_t*>(y));
+  } else {
+    MOE_LAUNCH("combine", combine_kernel<float>, dim3(blocks), dim3(256), 0, s,
+               static_cast<const float*>(residual), static_cast<const float*>(shared_out),
+               static_cast<const float*>(expert_out), idx, slot, gate, T, k, E, C, D,
+               ldr, static_cast<float*>(y));
+  }
+  return MOE_OK;
+}
+
+// One wavefront per token (4 tokens per block). EPL = experts per lane (E <= 64*EPL).
+template <int EPL>
+__global__ __launch_bounds__(256) void dgate_router_kernel(
+    const float* __restrict__ dy, const float* __restrict__ o, const float* __restrict__ logits,
+    const int32_t* __restrict__ idx, const float* __restrict__ gate,
+    const int32_t* __restrict__ slot, const int32_t* __restrict__ count, int T, int k, int E,
+    int C, int D, float aux_scale, float* __restrict__ dgate, float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  // softmax row
+  const float* row = logits + size_t(t) * E;
+  float s[EPL], p[EPL], dp[EPL];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    s[i] = e < E ? row[e] : -INFINITY;
+    mx = fmaxf(mx, s[i]);
+    dp[i] = 0.f;
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    p[i] = e < E ? __expf(s[i] - mx) : 0.f;
+    sum += p[i];
+  }
+  sum = wave_sum(sum);
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) p[i] *= inv;
+
+  // dgate_j, S_t, G_t = sum_r g_r dgate_r. dgate_j is kept in lane (j % 64), register
+  // slot j / 64 (k <= 256).
+  const float* dyr = dy + size_t(t) * D;
+  float S = 0.f, G = 0.f;
+  float dreg[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[size_t(t) * k + j];
+    const int sl = slot[size_t(t) * k + j];
+    float d = 0.f;
+    if (sl >= 0 && sl < C) {
+      const float* orow = o + (size_t(e) * C + sl) * D;
+      for (int c = lane * 4; c < D; c += 256) {
+        const float4 a = *reinterpret_cast<const float4*>(dyr + c);
+        const float4 b = *reinterpret_cast<const float4*>(orow + c);
+        d = fmaf(a.x, b.x, d);
+        d = fmaf(a.y, b.y, d);
+        d = fmaf(a.z, b.z, d);
+        d = fmaf(a.w, b.w, d);
+      }
+      d = wave_sum(d);
+    }
+    if (lane == 0) dgate[size_t(t) * k + j] = d;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (lane == (j & 63) && r == (j >> 6)) dreg[r] = d;
+    float pe = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (i == (e >> 6)) pe = p[i];
+    pe = __shfl(pe, e & 63, kWave);
+    S += pe;
+    G += gate[size_t(t) * k + j] * d;
+  }
+  // dp at the selected experts
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[size_t(t) * k + j];
+    float dv = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r == (j >> 6)) dv = dreg[r];
+    const float d = __shfl(dv, j & 63, kWave);
+    const float dq = (d - G) / S;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i == e) dp[i] += dq;
+  }
+  float pdp = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) pdp += p[i] * dp[i];
+  pdp = wave_sum(pdp);
+  float pf = 0.f;
+  float f[EPL];
+  if (aux_scale != 0.f) {
+    const float inv_tk = 1.0f / (float(T) * float(k));
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      f[i] = e < E ? float(count[e]) * inv_tk : 0.f;
+      pf += p[i] * f[i];
+    }
+    pf = wave_sum(pf);
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e >= E) continue;
+    float v = p[i] * (dp[i] - pdp);
+    if (aux_scale != 0.f) v += aux_scale * (float(E) / float(T)) * p[i] * (f[i] - pf);
+    dlogits[size_t(t) * E + e] = v;
+  }
+}
+
+moe_status_t launch_dgate_router_bwd(const float* dy, const float* expert_out,
+                                     const float* logits, const int32_t* idx,
+                                     const float* gate, const int32_t* slot,
+                                     const int32_t* count, int T, int k, int E, int C, int D,
+                                     float aux_scale, float* dgate, float* dlogits,
+                                     hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+#define MOE_DG(EPLV)                                                                      \
+  MOE_LAUNCH("dgate_router_bwd", dgate_router_kernel<EPLV>, grid, block, 0, s, dy,          \
+             expert_out, logits, idx, gate, slot, count, T, k, E, C, D, aux_scale, dgate,  \
+             dlogits)
+  if (E <= 64) {
+    MOE_DG(1);
+  } else if (E <= 128) {
+    MOE_DG(2);
+  } else if (E <= 256) {
+    MOE_DG(4);
+  } else if (E <= 512) {
+    MOE_DG(8);
+  } else {
+    MOE_DG(16);
+  }
+#undef MOE_DG
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -1,0 +1,140 @@
+// Internal launch interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// ---- routing / dispatch ---------------------------------------------------------
+// Tokens per routing block. The per-block partial counts and probability sums are
+// stored expert-major, [E][nb], nb = ceil(T / kRouteTokens).
+constexpr int kRouteTokens = 16;
+inline int route_blocks(int T) { return (T + kRouteTokens - 1) / kRouteTokens; }
+// Routing blocks per dispatch (slot assignment) block.
+inline int assign_group(int k) {
+  int g = 512 / (kRouteTokens * k);
+  return g < 1 ? 1 : g;
+}
+
+// Workspace carve-up shared by route and dispatch.
+struct RouteWs {
+  int32_t* flags;      // [0] error word, [1] finished-block ticket
+  int32_t* cnt_part;   // [E][nb]
+  int32_t* off_part;   // [E][nb]
+  float* prob_part;    // [E][nb]
+  float* fp;           // [E] f_e * P_e
+  size_t bytes;
+};
+RouteWs carve_route_ws(void* ws, int T, int E);
+
+moe_status_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* gate,
+                          const RouteWs& w, hipStream_t s);
+moe_status_t launch_count(const int32_t* idx, int T, int k, int E, const RouteWs& w,
+                          hipStream_t s);
+// with_prob: prob_part is valid (computes prob_sum and aux); C < 0: routing only
+moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int32_t* count,
+                                float* prob_sum, float* aux, int32_t* used, int32_t* overflow,
+                                int32_t* slot_assign, const RouteWs& w, hipStream_t s);
+moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32_t* slot,
+                           uint8_t* kept, int32_t* slot_assign, int32_t* drops,
+                           const RouteWs& w, hipStream_t s);
+
+// ---- grouped GEMMs ----------------------------------------------------------------
+enum Epi : int32_t {
+  EPI_STORE = 0,      // C = acc (output dtype of the kernel)
+  EPI_BIAS = 1,       // C = acc + bias[n]
+  EPI_GELU_BIAS = 2,  // C = gelu(acc + bias[n]) (bias may be NULL)
+  EPI_SWIGLU = 3,     // C = silu(acc_gate) * acc_up
+  EPI_SCALE_ROW = 4   // C = acc * rowscale (unused)
+};
+
+// One grouped problem: for group g and row r < M_g, C[g, r, :] = A_row(g, r) . B[g].
+// A_row(g, r) = A + g*a_gstride + src*lda, src = row_map ? row_map[g*row_map_ld + r] /
+// row_div : r. M_g = m_count ? m_count[g] : m_const. B[g] = B + g*b_gstride, [K][N].
+struct GemmProblem {
+  const void* A;
+  int64_t lda;
+  int64_t a_gstride;
+  const int32_t* row_map;
+  int32_t row_map_ld;
+  int32_t row_div;
+  const int32_t* m_count;
+  int32_t m_const;
+  int32_t m_tiles;
+  const void* B0;
+  const void* B1;  // SwiGLU up projection (gated kernel only)
+  int64_t b_gstride;
+  const void* bias;
+  int64_t bias_gstride;
+  void* C;
+  int64_t ldc;
+  int64_t c_gstride;
+  int32_t K;
+  int32_t N;
+  int32_t n_tiles;
+  int32_t groups;
+  int32_t epi;
+  int32_t out_f32;  // bf16 kernel: 1 = store fp32 (router logits)
+  int32_t tiles;    // groups * m_tiles * n_tiles (filled by the launcher)
+};
+
+struct GemmBatch {
+  GemmProblem p[2];
+  int32_t nprob;
+  int32_t total;
+};
+
+constexpr int kBf16BM = 128, kBf16BN = 128, kBf16BK = 64;
+moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStream_t s);
+
+// fp32 grouped GEMM (fp32 MFMA). Modes select the operand layouts.
+enum AMode : int32_t { A_ROWS = 0, A_KROWS = 1 };
+enum BMode : int32_t { B_KN = 0, B_NK = 1, B_KROWS_GATE = 2 };
+struct GemmF32Problem {
+  const float* A;
+  int64_t lda;
+  int64_t a_gstride;
+  const int32_t* row_map;   // A_ROWS: maps M rows; A_KROWS: maps K rows
+  int32_t row_map_ld;
+  int32_t row_div;
+  const int32_t* g_count;   // A_ROWS: M per group; A_KROWS: K per group
+  int32_t g_const;
+  int32_t M;                // A_KROWS: fixed M
+  int32_t m_tiles;
+  const float* B;
+  int64_t ldb;
+  int64_t b_gstride;
+  const float* gate;        // B_KROWS_GATE: scale of each gathered row (by assignment)
+  const float* bias;
+  int64_t bias_gstride;
+  float* C;
+  int64_t ldc;
+  int64_t c_gstride;
+  int32_t K;                // A_ROWS: inner size
+  int32_t N;
+  int32_t n_tiles;
+  int32_t groups;
+  int32_t epi;
+  int32_t tiles;
+};
+constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
+moe_status_t launch_gemm_f32(GemmF32Problem& p, int amode, int bmode, const char* name,
+                             hipStream_t s);
+
+// Plain SIMT router GEMM for shapes the MFMA kernels do not tile (any E).
+moe_status_t launch_router_simt(const void* x, int dtype, int64_t ldx, const void* w, int T,
+                                int D, int E, float* logits, hipStream_t s);
+
+// ---- combine / backward --------------------------------------------------------------
+moe_status_t launch_combine(int dt, const void* residual, int64_t ldr, const void* shared_out,
+                            const void* expert_out, const int32_t* idx, const int32_t* slot,
+                            const float* gate, int T, int k, int E, int C, int D, void* y,
+                            hipStream_t s);
+moe_status_t launch_dgate_router_bwd(const float* dy, const float* expert_out,
+                                     const float* logits, const int32_t* idx,
+                                     const float* gate, const int32_t* slot,
+                                     const int32_t* count, int T, int k, int E, int C, int D,
+                                     float aux_scale, float* dgate, float* dlogits,
+                                     hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,291 @@
+"""Thin torch binding over libmoe.so: argument marshalling only.
+
+Each function here has the name of a C entry point without its ``moe_`` prefix. It
+checks shapes and dtypes, allocates the outputs and the workspace with torch (device
+memory), and enqueues the library call on torch's current stream. Every step of the
+layer runs in the HIP kernels; nothing here computes.
+
+Experts are passed as a dict: {"kind": "linear"|"gelu"|"swiglu", "w_in": [E,D,F],
+"w_up": [E,D,F], "w_out": [E,F,D], "b_in": [E,F], "b_out": [E,D]} (absent keys = None),
+all of one dtype (float32 or bfloat16) on the GPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+_KIND = {"linear": L.MOE_EXPERT_LINEAR, "gelu": L.MOE_EXPERT_GELU_MLP,
+         "swiglu": L.MOE_EXPERT_SWIGLU}
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return L.MOE_F32
+    if t.dtype == torch.bfloat16:
+        return L.MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _c(t):
+    return None if t is None else t.contiguous()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def version():
+    return L.lib().moe_version().decode()
+
+
+def capacity(T, k, E, capacity_factor):
+    c = L.lib().moe_capacity(int(T), int(k), int(E), float(capacity_factor))
+    if c < 0:
+        raise ValueError("invalid capacity arguments")
+    return int(c)
+
+
+def _experts_struct(ex):
+    w_in = _c(ex["w_in"])
+    E, D = w_in.shape[0], w_in.shape[1]
+    F = w_in.shape[2]
+    keep = {k: _c(ex.get(k)) for k in ("w_in", "w_up", "w_out", "b_in", "b_out")}
+    s = L.Experts(kind=_KIND[ex["kind"]], dtype=_dt(w_in), num_experts=E, d_model=D, d_hidden=F,
+                  w_in=_p(keep["w_in"]), w_up=_p(keep["w_up"]), w_out=_p(keep["w_out"]),
+                  b_in=_p(keep["b_in"]), b_out=_p(keep["b_out"]))
+    return s, keep
+
+
+def route(*, k, logits=None, x=None, w_router=None):
+    """moe_route. Either logits [T,E] fp32, or x [T,D] and w_router [D,E]."""
+    if w_router is not None:
+        x = _c(x)
+        w_router = _c(w_router)
+        T, D = x.shape
+        E = w_router.shape[1]
+        dev = x.device
+        logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+        xdt = _dt(x)
+    else:
+        logits = _c(logits)
+        T, E = logits.shape
+        D = 0
+        dev = logits.device
+        xdt = L.MOE_F32
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    gate = torch.empty(T, k, dtype=torch.float32, device=dev)
+    count = torch.empty(E, dtype=torch.int32, device=dev)
+    prob = torch.empty(E, dtype=torch.float32, device=dev)
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = _ws(L.lib().moe_route_workspace_size(T, E), dev)
+    st = L.lib().moe_route(_p(x) if w_router is not None else None, xdt, D, _p(w_router), _p(logits),
+                           T, D, E, k, _p(idx), _p(gate), _p(count), _p(prob), _p(aux), _p(ws),
+                           ws.numel(), _stream())
+    L.check("moe_route", st)
+    return {"logits": logits, "topk_idx": idx, "topk_gate": gate, "expert_count": count,
+            "prob_sum": prob, "aux_loss": aux}
+
+
+def dispatch(topk_idx, E, C, *, return_ws=False):
+    """moe_dispatch: position-priority slots for topk_idx [T,k] int32."""
+    idx = _c(topk_idx)
+    if idx.dtype != torch.int32:
+        idx = idx.to(torch.int32)
+    T, k = idx.shape
+    dev = idx.device
+    slot = torch.empty(T, k, dtype=torch.int32, device=dev)
+    kept = torch.empty(T, k, dtype=torch.uint8, device=dev)
+    sa = torch.empty(E, max(C, 0), dtype=torch.int32, device=dev)
+    used = torch.empty(E, dtype=torch.int32, device=dev)
+    over = torch.empty(E, dtype=torch.int32, device=dev)
+    drops = torch.empty(T, dtype=torch.int32, device=dev)
+    ws = _ws(L.lib().moe_dispatch_workspace_size(T, k, E), dev)
+    st = L.lib().moe_dispatch(_p(idx), T, k, E, C, _p(slot), _p(kept), _p(sa), _p(used), _p(over),
+                              _p(drops), _p(ws), ws.numel(), _stream())
+    L.check("moe_dispatch", st)
+    out = {"slot": slot, "kept": kept, "slot_assign": sa, "expert_used": used,
+           "expert_overflow": over, "token_drops": drops}
+    if return_ws:
+        out["ws"] = ws
+    return out
+
+
+def read_error(ws):
+    return int(L.lib().moe_read_error(_p(ws), _stream()))
+
+
+def expert_mlp(experts, x, *, k=1, C=0, slot_assign=None, expert_used=None, keep_hidden=False):
+    """moe_expert_mlp. Routed: slot_assign [E,C] and expert_used [E]; dense (shared
+    expert, E = 1): slot_assign None. Returns expert_out ([E,C,D] or [T,D]) and, with
+    keep_hidden, the hidden activations."""
+    s, keep = _experts_struct(experts)
+    x = _c(x)
+    T = x.shape[0]
+    dev = x.device
+    dense = slot_assign is None
+    rows = T if dense else C
+    E, D, F = s.num_experts, s.d_model, s.d_hidden
+    out = torch.empty((T, D) if dense else (E, C, D), dtype=x.dtype, device=dev)
+    hidden = None
+    if keep_hidden and experts["kind"] != "linear":
+        hidden = torch.empty((T, F) if dense else (E, C, F), dtype=x.dtype, device=dev)
+    ws = _ws(L.lib().moe_expert_mlp_workspace_size(ctypes.byref(s), rows), dev)
+    st = L.lib().moe_expert_mlp(ctypes.byref(s), _p(x), x.stride(0), T, k, C, _p(slot_assign),
+                                _p(expert_used), _p(hidden), _p(out), _p(ws), ws.numel(),
+                                _stream())
+    L.check("moe_expert_mlp", st)
+    return {"expert_out": out, "hidden": hidden}
+
+
+def combine(expert_out, topk_idx, slot, topk_gate, *, residual=None, shared_out=None):
+    """moe_combine: y = residual + shared + sum_kept gate * expert_out[idx, slot]."""
+    eo = _c(expert_out)
+    E, C, D = eo.shape
+    T, k = topk_idx.shape
+    ref = residual if residual is not None else eo
+    y = torch.empty(T, D, dtype=eo.dtype, device=eo.device)
+    st = L.lib().moe_combine(_dt(eo), _p(_c(residual)), _p(_c(shared_out)), _p(eo),
+                             _p(_c(topk_idx)), _p(_c(slot)), _p(_c(topk_gate)), T, k, E, C, D,
+                             _p(y), _stream())
+    L.check("moe_combine", st)
+    del ref
+    return y
+
+
+def forward(x, experts, *, k, capacity, w_router=None, logits=None, shared=None,
+            use_residual=True, keep_hidden=False, keep_shared_out=False, _ws_cache=None):
+    """moe_forward: the whole layer. Returns every output of the call (see moe.h)."""
+    x = _c(x)
+    T, D = x.shape
+    dev = x.device
+    es, keep = _experts_struct(experts)
+    E, F = es.num_experts, es.d_hidden
+    C = int(capacity)
+    if w_router is not None:
+        w_router = _c(w_router)
+        logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    else:
+        logits = _c(logits)
+    shs, shkeep = (_experts_struct(shared) if shared is not None else (L.Experts(), {}))
+    o = {
+        "logits": logits,
+        "topk_idx": torch.empty(T, k, dtype=torch.int32, device=dev),
+        "topk_gate": torch.empty(T, k, dtype=torch.float32, device=dev),
+        "expert_count": torch.empty(E, dtype=torch.int32, device=dev),
+        "prob_sum": torch.empty(E, dtype=torch.float32, device=dev),
+        "aux_loss": torch.empty(1, dtype=torch.float32, device=dev),
+        "slot": torch.empty(T, k, dtype=torch.int32, device=dev),
+        "kept": torch.empty(T, k, dtype=torch.uint8, device=dev),
+        "slot_assign": torch.empty(E, C, dtype=torch.int32, device=dev),
+        "expert_used": torch.empty(E, dtype=torch.int32, device=dev),
+        "expert_overflow": torch.empty(E, dtype=torch.int32, device=dev),
+        "token_drops": torch.empty(T, dtype=torch.int32, device=dev),
+        "expert_out": torch.empty(E, C, D, dtype=x.dtype, device=dev),
+        "y": torch.empty(T, D, dtype=x.dtype, device=dev),
+        "hidden": (torch.empty(E, C, F, dtype=x.dtype, device=dev)
+                   if keep_hidden and experts["kind"] != "linear" else None),
+        "shared_out": (torch.empty(T, D, dtype=x.dtype, device=dev)
+                       if keep_shared_out and shared is not None else None),
+        "capacity": C,
+    }
+    a = L.ForwardArgs(
+        x=_p(x), ldx=x.stride(0), T=T, w_router=_p(w_router), logits=_p(logits), experts=es,
+        shared=shs, k=k, capacity=C, use_residual=1 if use_residual else 0,
+        topk_idx=_p(o["topk_idx"]), topk_gate=_p(o["topk_gate"]),
+        expert_count=_p(o["expert_count"]), prob_sum=_p(o["prob_sum"]),
+        aux_loss=_p(o["aux_loss"]), slot=_p(o["slot"]), kept=_p(o["kept"]),
+        slot_assign=_p(o["slot_assign"]), expert_used=_p(o["expert_used"]),
+        expert_overflow=_p(o["expert_overflow"]), token_drops=_p(o["token_drops"]),
+        hidden_cache=_p(o["hidden"]), expert_out=_p(o["expert_out"]),
+        shared_out=_p(o["shared_out"]), y=_p(o["y"]))
+    need = L.lib().moe_forward_workspace_size(ctypes.byref(a))
+    if _ws_cache is not None and _ws_cache.numel() >= need:
+        ws = _ws_cache
+    else:
+        ws = _ws(need, dev)
+    st = L.lib().moe_forward(ctypes.byref(a), _p(ws), ws.numel(), _stream())
+    L.check("moe_forward", st)
+    o["ws"] = ws
+    # everything a repeat call needs, kept alive together
+    o["_call"] = ForwardCall(a, ws, (x, w_router, keep, shkeep))
+    return o
+
+
+class ForwardCall:
+    """A prepared moe_forward: the argument struct and workspace of an earlier call, so
+    that the same layer can be re-run on the same buffers without re-marshalling."""
+
+    def __init__(self, args, ws, keepalive):
+        self.args = args
+        self.ws = ws
+        self._keep = keepalive
+        self._fn = L.lib().moe_forward
+        self._ref = ctypes.byref(self.args)
+        self._ws_p = _p(ws)
+        self._ws_n = ws.numel()
+
+    def __call__(self, stream=None):
+        s = ctypes.c_void_p(stream) if stream is not None else _stream()
+        st = self._fn(self._ref, self._ws_p, self._ws_n, s)
+        if st != L.MOE_OK:
+            L.check("moe_forward", st)
+
+
+def backward(dy, x, experts, fwd, *, k, use_residual=True, aux_grad_scale=0.0):
+    """moe_backward for single-linear fp32 experts. ``fwd`` is the dict returned by
+    forward(). Returns dx, dW, dgate, dlogits."""
+    dy = _c(dy)
+    x = _c(x)
+    T, D = x.shape
+    dev = x.device
+    es, keep = _experts_struct(experts)
+    E = es.num_experts
+    C = int(fwd["capacity"])
+    out = {
+        "dx": torch.empty(T, D, dtype=x.dtype, device=dev),
+        "dW": torch.empty(E, D, D, dtype=x.dtype, device=dev),
+        "dgate": torch.empty(T, k, dtype=torch.float32, device=dev),
+        "dlogits": torch.empty(T, E, dtype=torch.float32, device=dev),
+    }
+    a = L.BackwardArgs(
+        dy=_p(dy), x=_p(x), ld=x.stride(0), T=T, logits=_p(fwd["logits"]), experts=es, k=k,
+        capacity=C, use_residual=1 if use_residual else 0, aux_grad_scale=float(aux_grad_scale),
+        topk_idx=_p(fwd["topk_idx"]), topk_gate=_p(fwd["topk_gate"]),
+        expert_count=_p(fwd["expert_count"]), slot=_p(fwd["slot"]),
+        slot_assign=_p(fwd["slot_assign"]), expert_used=_p(fwd["expert_used"]),
+        expert_out=_p(fwd["expert_out"]), dx=_p(out["dx"]), dW=_p(out["dW"]),
+        dgate=_p(out["dgate"]), dlogits=_p(out["dlogits"]))
+    ws = _ws(L.lib().moe_backward_workspace_size(ctypes.byref(a)), dev)
+    st = L.lib().moe_backward(ctypes.byref(a), _p(ws), ws.numel(), _stream())
+    L.check("moe_backward", st)
+    return out
+
+
+def profile_enable(on=True):
+    L.lib().moe_profile_enable(1 if on else 0)
+
+
+def profile_read(max_entries=64):
+    """Per-kernel launch counts and summed milliseconds since the last read."""
+    stride = 64
+    names = ctypes.create_string_buffer(stride * max_entries)
+    counts = (ctypes.c_int32 * max_entries)()
+    ms = (ctypes.c_double * max_entries)()
+    n = L.lib().moe_profile_read(names, stride, counts, ms, max_entries)
+    out = {}
+    for i in range(n):
+        nm = names.raw[i * stride:(i + 1) * stride].split(b"\0", 1)[0].decode()
+        out[nm] = (int(counts[i]), float(ms[i]))
+    return out

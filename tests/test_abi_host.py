@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every symbol
+the header declares, computes the capacity exactly, and rejects bad arguments before
+launching anything."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as om
+from sparse_mixture_experts_stable_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.lib()
+    decl = declared_functions()
+    assert len(decl) >= 17
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(L.EXPORTED) == decl
+
+
+def test_version_and_status_strings():
+    lib = L.lib()
+    assert lib.moe_version().decode().startswith("moe-gfx950")
+    assert lib.moe_status_string(L.MOE_ERR_WORKSPACE) == b"MOE_ERR_WORKSPACE"
+
+
+def test_capacity_matches_oracle():
+    lib = L.lib()
+    rng = np.random.default_rng(0)
+    for _ in range(5000):
+        T = int(rng.integers(1, 10 ** 7)); E = int(rng.integers(1, 1025)); k = int(rng.integers(1, E + 1))
+        cf = float(rng.choice([rng.random() * 3, round(rng.random() * 4, 2), 1e-300, 0.1, 1 / 3, 0.0]))
+        want = om.capacity(T, k, E, cf)
+        if want > 2 ** 31 - 1:
+            want = -1
+        assert lib.moe_capacity(T, k, E, cf) == want, (T, k, E, cf)
+    for bad in [(8, 2, 4, -0.5), (8, 2, 4, float("nan")), (8, 2, 4, float("inf")), (8, 5, 4, 1.0),
+                (0, 1, 4, 1.0)]:
+        assert lib.moe_capacity(*bad) == -1
+
+
+def _null():
+    return None
+
+
+def test_route_rejects_bad_arguments():
+    lib = L.lib()
+    ws = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    p = ctypes.c_void_p(1 << 21)
+    common = dict(x=None, dt=L.MOE_F32, ldx=0, w=None, logits=p)
+
+    def call(T, E, k, ws_bytes=1 << 30, idx=p):
+        return lib.moe_route(common["x"], common["dt"], common["ldx"], common["w"], common["logits"],
+                             T, 0, E, k, idx, p, p, p, p, ws, ws_bytes, None)
+    assert call(8, 4, 0) == L.MOE_ERR_INVALID_ARG
+    assert call(8, 4, 5) == L.MOE_ERR_INVALID_ARG
+    assert call(0, 4, 1) == L.MOE_ERR_INVALID_ARG
+    assert call(8, 2000, 1) == L.MOE_ERR_INVALID_ARG
+    assert call(8, 4, 2, idx=None) == L.MOE_ERR_INVALID_ARG
+    assert call(8, 4, 2, ws_bytes=16) == L.MOE_ERR_WORKSPACE
+
+
+def test_dispatch_and_forward_reject_bad_arguments():
+    lib = L.lib()
+    p = ctypes.c_void_p(1 << 21)
+    assert lib.moe_dispatch(p, 8, 2, 4, -1, p, p, p, p, p, p, p, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(p, 8, 2, 4, 4, p, p, None, p, p, p, p, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(p, 8, 2, 4, 4, p, p, p, p, p, p, p, 8, None) == L.MOE_ERR_WORKSPACE
+    ex = L.Experts(kind=L.MOE_EXPERT_SWIGLU, dtype=L.MOE_BF16, num_experts=4, d_model=100,
+                   d_hidden=64, w_in=p, w_up=p, w_out=p)
+    a = L.ForwardArgs(x=p, ldx=100, T=8, logits=p, experts=ex, k=2, capacity=4)
+    assert lib.moe_forward(ctypes.byref(a), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    ex.d_model = 128
+    a = L.ForwardArgs(x=p, ldx=128, T=8, logits=p, experts=ex, k=5, capacity=4)
+    assert lib.moe_forward(ctypes.byref(a), p, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    bex = L.Experts(kind=L.MOE_EXPERT_SWIGLU, dtype=L.MOE_BF16, num_experts=4, d_model=128,
+                    d_hidden=128, w_in=p, w_up=p, w_out=p)
+    b = L.BackwardArgs(dy=p, x=p, ld=128, T=8, logits=p, experts=bex, k=2, capacity=4)
+    assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_positive():
+    lib = L.lib()
+    assert lib.moe_route_workspace_size(16384, 256) > 16384 // 16 * 256 * 4
+    assert lib.moe_dispatch_workspace_size(16384, 8, 256) > 0
