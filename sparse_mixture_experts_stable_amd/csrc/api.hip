@@ -523,7 +523,7 @@ moe_status_t check_forward(const moe_forward_args_t* a) {
   if (!a->x || a->ldx < D || !a->logits || !a->y) return MOE_ERR_INVALID_ARG;
   if (!a->topk_idx || !a->topk_gate || !a->expert_count || !a->prob_sum || !a->aux_loss ||
       !a->slot || !a->kept || !a->expert_used || !a->expert_overflow || !a->token_drops ||
-      !a->expert_out || (C > 0 && !a->slot_assign))
+      (C > 0 && (!a->slot_assign || !a->expert_out)))
     return MOE_ERR_INVALID_ARG;
   if (a->ldx % (a->experts.dtype == MOE_BF16 ? 8 : 4)) return MOE_ERR_UNSUPPORTED;
   if (a->shared.w_in) {
