@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before warmup, run one plain device copy of this many MiB (a "
+                         "known-size reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -142,6 +145,15 @@ def main():
     torch.cuda.synchronize()
     kept = int(out["kept"].sum().item())
     stream = torch.cuda.current_stream()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         call()

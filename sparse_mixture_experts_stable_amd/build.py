@@ -36,6 +36,8 @@ def compile_flags():
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in arch VGPRs: avoids AGPR copy chains around the MFMA loops
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"),
     ]
 

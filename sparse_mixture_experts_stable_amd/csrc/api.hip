@@ -113,7 +113,7 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
     a.row_div = k;
     a.m_count = dense ? nullptr : used;
     a.m_const = T;
-    a.m_tiles = (rows + kBf16BM - 1) / kBf16BM;
+    a.m_tiles_rows = rows;
     a.B0 = ex->w_in;
     a.B1 = ex->kind == MOE_EXPERT_SWIGLU ? ex->w_up : nullptr;
     a.b_gstride = int64_t(D) * (pl.two_stage ? F : D);
@@ -139,7 +139,7 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
       b.row_div = 1;
       b.m_count = dense ? nullptr : used;
       b.m_const = T;
-      b.m_tiles = a.m_tiles;
+      b.m_tiles_rows = rows;
       b.B0 = ex->w_out;
       b.b_gstride = int64_t(F) * D;
       b.bias = ex->kind == MOE_EXPERT_GELU_MLP ? ex->b_out : nullptr;
@@ -251,7 +251,7 @@ moe_status_t router_gemm(const void* x, int dt, int64_t ldx, const void* w, int 
     p.lda = ldx;
     p.row_div = 1;
     p.m_const = T;
-    p.m_tiles = (T + kBf16BM - 1) / kBf16BM;
+    p.m_tiles_rows = T;
     p.B0 = w;
     p.K = D;
     p.N = E;

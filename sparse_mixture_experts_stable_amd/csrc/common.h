@@ -28,9 +28,12 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
-// Two floats -> packed bf16 pair (low half = a).
+// Two floats -> packed bf16 pair (low half = a), round-to-nearest-even, one
+// v_cvt_pk_bf16_f32 on gfx950.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  const bf16x2 r = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -6,16 +6,29 @@
 // (slot -> assignment -> token), so each expert's input rows are assembled directly in
 // LDS tiles from x without a separate gather pass.
 //
-// Tile: 128 x 128 x 64 per 256-thread block, four waves in a 2 x 2 grid, each wave a
-// 64 x 64 patch of 4 x 4 MFMA tiles. The gated (SwiGLU) variant carries a second B
-// operand and a second accumulator set so that silu(x Wg) * (x Wu) is formed in the
-// epilogue and only the product is written.
+// Data movement. Both operands go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no register staging), through a three-stage ring: the tile
+// for step k+2 is requested while step k is multiplied (ring depth S: step k+S-1), so
+// S-1 steps of MFMA cover the memory latency and one barrier per step publishes the
+// next tile.
+//   A (expert rows, k contiguous) is stored [m][k], 128 bytes per row (BK = 64), and
+//   read as one 16-byte fragment per lane. Each lane fetches the source chunk
+//   c ^ f(m), f(m) = (m ^ m/8) % 8, so that the 16 lanes of a fragment read hit distinct
+//   bank groups.
+//   B (weights, n contiguous: [k][n] per expert, as stored) is copied unchanged apart
+//   from a per-row XOR of the 16-byte chunk index (hswz); the k-major fragment
+//   each MFMA needs is assembled with two ds_read_b64_tr_b16 transpose reads. Within a
+//   16-lane group that instruction hands lane l element l % 4 of the 8-byte pieces
+//   addressed by lanes l/4 + 4v (v = 0..3), so lane s of group g points at row
+//   8g + (s%16)/4 (+4 for the second read) and column 4 (s % 4) of its 16-column slice.
 //
-// Operand layouts in LDS: A is [m][k] and B is [n][k] (k contiguous), 128 bytes per
-// row, with the 16-byte chunk index XOR-swizzled by (row / 2) % 8 so that the 16 lanes
-// reading one MFMA fragment hit 16 distinct bank groups. B arrives from HBM as [k][n]
-// (n contiguous); each thread loads a 4 x 8 or 8 x 8 sub-block and transposes it in
-// registers before the LDS store.
+// Tiles: the large tile is 256 rows x 256 staged B columns (SwiGLU: 128 gate + 128 up
+// columns of the same outputs) on 16 waves (4 x 4, four per SIMD, each 64 rows x 64
+// staged columns) with a two-stage ring (128 KiB of LDS): large enough that each byte
+// staged feeds 128 FLOPs. The small tile (128 x 128, 4 waves, three stages) serves
+// narrow problems. The gated variant holds gate and up accumulators of the same outputs
+// in one lane, so silu(x Wg) * (x Wu) is formed in the epilogue and only the product is
+// written.
 //
 // The MFMA is issued with the B fragment as its first operand, which yields C^T per
 // tile: each lane then holds 4 consecutive output columns of one row, so the epilogue
@@ -32,12 +45,20 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = kBf16BM, BN = kBf16BN, BK = kBf16BK;
-constexpr int kRowBytes = BK * 2;  // 128
-constexpr int kTileBytes = BM * kRowBytes;  // 16 KiB
+constexpr int BK = kBf16BK;  // 64
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int fswz(int m) { return (m ^ (m >> 3)) & 7; }
+// B rows: the 16-byte chunk index is XORed with an even value that differs for the four
+// rows one 16-lane group reads together and, in addition, between groups 0 and 1 (rows
+// k and k + 8), so that both 16 and 32 lanes per LDS cycle are conflict free.
+template <int RB>
+__device__ __forceinline__ int hswz(int k) {
+  if constexpr (RB == 128) return ((k ^ (k >> 3)) & 3) << 1;
+  return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
 }
 
 __device__ __forceinline__ int logical_block(int bid, int nblk) {
@@ -46,26 +67,118 @@ __device__ __forceinline__ int logical_block(int bid, int nblk) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
 
-// 2 bf16 (16-bit halves h of words a and b) -> one word: low = a's half, high = b's half.
-__device__ __forceinline__ uint32_t pick2(uint32_t a, uint32_t b, int hi) {
-  return hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <bool GATED>
-struct Stage {
-  static constexpr int KR = GATED ? 8 : 4;  // k rows per B sub-block
-  uint4 a[4];
-  uint4 b[KR];
+template <int BM_, int BNE_, bool GATED_, int WGM_ = 2, int WGN_ = 2, int STAGES_ = 3>
+struct TileCfg {
+  static constexpr int STAGES = STAGES_;           // LDS ring depth
+  static constexpr int BM = BM_;                 // rows per block
+  static constexpr int BNE = BNE_;               // B columns staged per step (all matrices)
+  static constexpr bool GATED = GATED_;
+  static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid (rows x columns)
+  static constexpr int WAVES = WGM * WGN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int NB = GATED ? 2 : 1;       // B matrices
+  static constexpr int BNQ = BNE / NB;           // columns per B matrix = output columns
+  static constexpr int WROWS = BM / WGM;         // rows per wave
+  static constexpr int WCOLS = BNQ / WGN;        // output columns per wave
+  static constexpr int TM = WROWS / 16;          // MFMA tiles per wave, rows
+  static constexpr int TN = WCOLS / 16;          // MFMA tiles per wave, columns per matrix
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int BQ_BYTES = BK * BNQ * 2;  // one B matrix
+  static constexpr int STAGE = A_BYTES + NB * BQ_BYTES;
+  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int A_INST = BM / 8 / WAVES;  // 1 KiB DMA loads of A per wave per step
+  static constexpr int B_RB = BNQ * 2;           // bytes per B row
+  static constexpr int B_RPI = 1024 / B_RB;      // B rows per 1 KiB load
+  static constexpr int B_IPQ = BK / B_RPI;       // loads per B matrix per step
+  static constexpr int B_INST = NB * B_IPQ / WAVES;  // per wave per step
+  static constexpr int LOADS = A_INST + B_INST;  // vector-memory ops per thread per step
+  static_assert(BM % (8 * WAVES) == 0, "A loads split evenly over the waves");
+  static_assert(NB * B_IPQ % WAVES == 0, "B loads split evenly over the waves");
 };
+
+// Requests the tiles of step kt into the LDS slot `dst` (one 1 KiB DMA per instruction).
+template <class CF>
+__device__ __forceinline__ void step_issue(char* __restrict__ dst, const bf16_t* const* a_src,
+                                           const bf16_t* const* b_src, int kt, int N, int wv) {
+  const int k0 = kt * BK;
+#pragma unroll
+  for (int t = 0; t < CF::A_INST; ++t)
+    __builtin_amdgcn_global_load_lds(a_src[t] + k0, (lds_void*)(dst + (wv * CF::A_INST + t) * 1024),
+                                     16, 0, 0);
+#pragma unroll
+  for (int t = 0; t < CF::B_INST; ++t) {
+    const int u = wv * CF::B_INST + t;
+    __builtin_amdgcn_global_load_lds(
+        b_src[t] + size_t(k0) * N,
+        (lds_void*)(dst + CF::A_BYTES + (u / CF::B_IPQ) * CF::BQ_BYTES + (u % CF::B_IPQ) * 1024),
+        16, 0, 0);
+  }
+}
+
+// One K step: request step `nxt` into slot `nxt_slot`, then multiply the tiles in slot
+// `cur`. The two slots are distinct, which the restrict qualifiers state; that lets the
+// compiler order the LDS reads of `cur` freely against the DMA writes still in flight.
+template <class CF>
+__device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
+                                                   char* __restrict__ nxt_slot,
+                                                   const bf16_t* const* a_src,
+                                                   const bf16_t* const* b_src, int nxt, int N,
+                                                   int wv, int wm, int wn, int lane,
+                                                   f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
+  step_issue<CF>(nxt_slot, a_src, b_src, nxt, N, wv);
+  const int fr = lane & 15, fc = lane >> 4;
+  const int arow = wm * CF::WROWS + fr;
+  // B transpose-read coordinates of this lane: k row within the 32-wide k step and the
+  // column offset inside a 16-column fragment
+  const int bk = 8 * fc + (fr >> 2);
+  const int bcol = 4 * (fr & 3);
+  const char* As = cur;
+  const char* Bs = cur + CF::A_BYTES;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8 bfr[NB][TN];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = wn * CF::WCOLS + j * 16 + bcol;
+        const int k0 = ks * 32 + bk;
+        const int k1 = k0 + 4;
+        const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k0 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k0)) + 2 * (col & 7)));
+        const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k1 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k1)) + 2 * (col & 7)));
+        bfr[q][j] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = arow + i * 16;
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(As + m * (BK * 2) + 16 * ((ks * 4 + fc) ^ fswz(m)));
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[q][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[q][j], af, acc[q][i][j], 0, 0, 0);
+    }
+  }
+}
 
 }  // namespace
 
-template <bool GATED>
-__global__ __launch_bounds__(256, GATED ? 1 : 2) void gemm_bf16_kernel(GemmBatch batch) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int NB = GATED ? 2 : 1;
-  constexpr int KR = Stage<GATED>::KR;
-  constexpr int kStageBytes = kTileBytes * (1 + NB);
+// EPI: EPI_STORE / EPI_BIAS / EPI_GELU_BIAS / EPI_SWIGLU; OF32: store fp32 instead of bf16
+template <class CF, int EPI, bool OF32>
+__global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch batch) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  constexpr int BM = CF::BM, BNQ = CF::BNQ, NB = CF::NB, TM = CF::TM, TN = CF::TN;
 
   const int lid = logical_block(blockIdx.x, gridDim.x);
   const int pi = (batch.nprob > 1 && lid >= batch.p[0].tiles) ? 1 : 0;
@@ -79,150 +192,119 @@ __global__ __launch_bounds__(256, GATED ? 1 : 2) void gemm_bf16_kernel(GemmBatch
   const int M = P.m_count ? P.m_count[g] : P.m_const;
   const int m0 = mt * BM;
   if (m0 >= M) return;
-  const int n0 = nt * BN;
+  const int n0 = nt * BNQ;
   const int N = P.N;
   const int K = P.K;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int wm = wv & 1, wn = wv >> 1;
+  const int wm = wv % CF::WGM, wn = wv / CF::WGM;
 
-  // ---- A row sources (4 rows per thread, 16 bytes each per stage) ----
-  const bf16_t* a_src[4];
-  const int a_chunk = tid & 7;
+  // ---- per-lane DMA sources ----
+  // A: load t of wave wv fills LDS rows (wv*A_INST + t)*8 .. +8; this lane's row and
+  // its physical chunk p = lane % 8, which holds source chunk p ^ f(row).
+  const bf16_t* a_src[CF::A_INST];
   {
     const bf16_t* Ab = static_cast<const bf16_t*>(P.A) + size_t(g) * P.a_gstride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int r = m0 + (tid >> 3) + 32 * i;
+    for (int t = 0; t < CF::A_INST; ++t) {
+      const int row = (wv * CF::A_INST + t) * 8 + (lane >> 3);
+      int r = m0 + row;
       if (r >= M) r = m0;
       int src = r;
       if (P.row_map) src = P.row_map[size_t(g) * P.row_map_ld + r] / P.row_div;
-      a_src[i] = Ab + size_t(src) * P.lda + a_chunk * 8;
+      a_src[t] = Ab + size_t(src) * P.lda + 8 * ((lane & 7) ^ fswz(row));
     }
   }
-  // ---- B sub-block: KR k-rows x 8 n-columns per thread ----
-  const int b_sel = GATED ? (tid >> 7) : 0;
-  const int b_t = GATED ? (tid & 127) : tid;
-  const int b_nb = b_t & 15;           // n block of 8
-  const int b_kb = b_t >> 4;           // k block of KR
-  const int b_n = n0 + b_nb * 8;
-  const bool b_ok = b_n < N;           // N is a multiple of 8
-  const bf16_t* b_src =
-      static_cast<const bf16_t*>(b_sel ? P.B1 : P.B0) + size_t(g) * P.b_gstride + (b_ok ? b_n : 0);
-
-  Stage<GATED> st;
-  auto load = [&](int kt) {
-    const int k0 = kt * BK;
+  // B: load t of wave wv is load u = wv*B_INST + t overall: matrix u / B_IPQ, rows
+  // (u % B_IPQ) * B_RPI .. +B_RPI; this lane's row and physical chunk.
+  const bf16_t* b_src[CF::B_INST];
+  {
+    constexpr int CPR = CF::B_RB / 16;  // chunks per row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-#pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const int kk = k0 + b_kb * KR + r;
-      st.b[r] = b_ok ? *reinterpret_cast<const uint4*>(b_src + size_t(kk) * N) : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < CF::B_INST; ++t) {
+      const int u = wv * CF::B_INST + t;
+      const int q = u / CF::B_IPQ;
+      const int k = (u % CF::B_IPQ) * CF::B_RPI + lane / CPR;
+      const int c = (lane % CPR) ^ hswz<CF::B_RB>(k);
+      int col = n0 + 8 * c;
+      if (col >= N) col = 0;  // columns past N are never stored
+      b_src[t] = static_cast<const bf16_t*>(q ? P.B1 : P.B0) + size_t(g) * P.b_gstride +
+                 size_t(k) * N + col;
     }
-  };
-  auto store = [&](int buf) {
-    char* As = smem + buf * kStageBytes;
-    char* Bs = As + kTileBytes + b_sel * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(As + swz((tid >> 3) + 32 * i, a_chunk)) = st.a[i];
-    // transpose KR x 8 -> 8 columns of KR k-values
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int wsel = c >> 1, hi = c & 1;
-      uint32_t w[KR / 2];
-#pragma unroll
-      for (int r = 0; r < KR; r += 2) {
-        const uint32_t lo_w = reinterpret_cast<const uint32_t*>(&st.b[r])[wsel];
-        const uint32_t hi_w = reinterpret_cast<const uint32_t*>(&st.b[r + 1])[wsel];
-        w[r / 2] = pick2(lo_w, hi_w, hi);
-      }
-      const int n = b_nb * 8 + c;
-      if constexpr (KR == 8) {
-        *reinterpret_cast<uint4*>(Bs + swz(n, b_kb)) = make_uint4(w[0], w[1], w[2], w[3]);
-      } else {
-        *reinterpret_cast<uint2*>(Bs + swz(n, b_kb >> 1) + ((b_kb & 1) << 3)) = make_uint2(w[0], w[1]);
-      }
-    }
-  };
+  }
 
-  f32x4 acc[NB][4][4];
+  f32x4 acc[NB][TM][TN];
 #pragma unroll
   for (int q = 0; q < NB; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fc = lane >> 4;
 
   const int nk = K / BK;
-  load(0);
-  store(0);
-  __syncthreads();
-  const int fr = lane & 15, fc = lane >> 4;
+  const int last = nk - 1;
+  constexpr int S = CF::STAGES;
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    step_issue<CF>(smem + st * CF::STAGE, a_src, b_src, st <= last ? st : last, N, wv);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-    const char* As = smem + cur * kStageBytes;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[4], bfr[NB][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * 64 + i * 16 + fr, ks * 4 + fc));
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfr[q][j] = *reinterpret_cast<const bf16x8*>(As + kTileBytes * (1 + q) +
-                                                       swz(wn * 64 + j * 16 + fr, ks * 4 + fc));
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[q][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[q][j], af[i], acc[q][i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store(cur ^ 1);
-    __syncthreads();
+    // this thread's loads for step kt have landed (S-2 later steps may still be in
+    // flight); after the barrier everyone's have, and every wave is done with step kt-1,
+    // whose slot the next request reuses
+    wait_vmcnt<CF::LOADS * (S - 2)>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int nxt = kt + S - 1 <= last ? kt + S - 1 : last;
+    step_compute_issue<CF>(smem + (kt % S) * CF::STAGE, smem + ((kt + S - 1) % S) * CF::STAGE,
+                           a_src, b_src, nxt, N, wv, wm, wn, lane, acc);
   }
+  wait_vmcnt<0>();  // the clamped tail loads still target LDS
+  __syncthreads();
 
   // ---- epilogue: lane holds C[m][n..n+3] ----
   char* Cb = static_cast<char*>(P.C);
-  const int es = P.out_f32 ? 4 : 2;
-  const bf16_t* bias = static_cast<const bf16_t*>(P.bias);
+  constexpr int es = OF32 ? 4 : 2;
+  // bias of this block's columns, staged once in LDS (free after the main loop)
+  float* sbias = reinterpret_cast<float*>(smem);
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
+    const bf16_t* bias = static_cast<const bf16_t*>(P.bias);
+    for (int c = tid; c < BNQ; c += CF::THREADS)
+      sbias[c] = (bias && n0 + c < N) ? bf16_to_f32(bias[size_t(g) * P.bias_gstride + n0 + c]) : 0.f;
+    __syncthreads();
+  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 64 + i * 16 + fr;
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * CF::WROWS + i * 16 + fr;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + j * 16 + fc * 4;
+    for (int j = 0; j < TN; ++j) {
+      const int nl = wn * CF::WCOLS + j * 16 + fc * 4;
+      const int n = n0 + nl;
       if (n >= N) continue;
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = acc[0][i][j][r];
-      if (GATED) {
+      if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = silu(v[r]) * acc[NB - 1][i][j][r];
-      } else if (P.epi == EPI_BIAS || P.epi == EPI_GELU_BIAS) {
-        if (bias) {
-          const uint2 bb = *reinterpret_cast<const uint2*>(bias + size_t(g) * P.bias_gstride + n);
-          v[0] += bf16_to_f32(bb.x & 0xffff);
-          v[1] += bf16_to_f32(bb.x >> 16);
-          v[2] += bf16_to_f32(bb.y & 0xffff);
-          v[3] += bf16_to_f32(bb.y >> 16);
-        }
-        if (P.epi == EPI_GELU_BIAS) {
+      }
+      if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
+        const float4 bb = *reinterpret_cast<const float4*>(sbias + nl);
+        v[0] += bb.x;
+        v[1] += bb.y;
+        v[2] += bb.z;
+        v[3] += bb.w;
+      }
+      if constexpr (EPI == EPI_GELU_BIAS) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
-        }
+        for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
       }
       char* dst = Cb + (size_t(g) * P.c_gstride + size_t(m) * P.ldc + n) * es;
-      if (P.out_f32) {
+      if constexpr (OF32) {
         *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
         *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -231,31 +313,68 @@ __global__ __launch_bounds__(256, GATED ? 1 : 2) void gemm_bf16_kernel(GemmBatch
   }
 }
 
-moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStream_t s) {
+namespace {
+template <class CF, int EPI, bool OF32>
+moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
   b.total = 0;
   for (int i = 0; i < b.nprob; ++i) {
     GemmProblem& p = b.p[i];
-    p.n_tiles = (p.N + BN - 1) / BN;
+    p.m_tiles = (p.m_tiles_rows + CF::BM - 1) / CF::BM;
+    p.n_tiles = (p.N + CF::BNQ - 1) / CF::BNQ;
     p.tiles = p.groups * p.m_tiles * p.n_tiles;
     b.total += p.tiles;
   }
   if (b.total == 0) return MOE_OK;
-  const size_t shmem = size_t(2) * kTileBytes * (gated ? 3 : 2);
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[gated]) {
-    hipError_t e = gated ? hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel<true>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem))
-                         : hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel<false>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    attr_set[gated] = true;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel<CF, EPI, OF32>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS) != hipSuccess)
+      return MOE_ERR_HIP;
+    attr_set = true;
   }
-  if (gated) {
-    MOE_LAUNCH(name, gemm_bf16_kernel<true>, dim3(b.total), dim3(256), shmem, s, b);
-  } else {
-    MOE_LAUNCH(name, gemm_bf16_kernel<false>, dim3(b.total), dim3(256), shmem, s, b);
-  }
+  MOE_LAUNCH(name, (gemm_bf16_kernel<CF, EPI, OF32>), dim3(b.total), dim3(CF::THREADS), CF::LDS, s, b);
   return MOE_OK;
+}
+
+template <class CF>
+moe_status_t launch_epi(GemmBatch& b, const char* name, hipStream_t s) {
+  const int epi = b.p[0].epi;
+  for (int i = 1; i < b.nprob; ++i)
+    if (b.p[i].epi != epi || b.p[i].out_f32 != b.p[0].out_f32) return MOE_ERR_UNSUPPORTED;
+  if (b.p[0].out_f32) {
+    if (epi != EPI_STORE) return MOE_ERR_UNSUPPORTED;
+    return launch_cfg<CF, EPI_STORE, true>(b, name, s);
+  }
+  switch (epi) {
+    case EPI_STORE: return launch_cfg<CF, EPI_STORE, false>(b, name, s);
+    case EPI_BIAS: return launch_cfg<CF, EPI_BIAS, false>(b, name, s);
+    case EPI_GELU_BIAS: return launch_cfg<CF, EPI_GELU_BIAS, false>(b, name, s);
+    default: return MOE_ERR_UNSUPPORTED;
+  }
+}
+}  // namespace
+
+moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStream_t s) {
+  // Large tiles (256 x 256, 16 waves, two stages) when every problem has enough rows per
+  // group and the grid still holds at least two tiles per CU; else 128 x 128 tiles.
+  using Large = TileCfg<256, 256, true, 4, 4, 2>;
+  bool large = true;
+  long tiles = 0;
+  for (int i = 0; i < b.nprob; ++i) {
+    const GemmProblem& p = b.p[i];
+    if (p.m_tiles_rows < 192) large = false;
+    const int bnq = gated ? Large::BNQ : 2 * Large::BNQ;
+    tiles += long(p.groups) * ((p.m_tiles_rows + 255) / 256) * ((p.N + bnq - 1) / bnq);
+  }
+  if (tiles < 512) large = false;
+  if (gated) {
+    for (int i = 0; i < b.nprob; ++i)
+      if (b.p[i].epi != EPI_SWIGLU || b.p[i].out_f32) return MOE_ERR_UNSUPPORTED;
+    return large ? launch_cfg<TileCfg<256, 256, true, 4, 4, 2>, EPI_SWIGLU, false>(b, name, s)
+                 : launch_cfg<TileCfg<128, 128, true, 2, 2, 3>, EPI_SWIGLU, false>(b, name, s);
+  }
+  return large ? launch_epi<TileCfg<256, 256, false, 4, 4, 2>>(b, name, s)
+               : launch_epi<TileCfg<128, 128, false, 2, 2, 3>>(b, name, s);
 }
 
 }  // namespace moe

@@ -60,7 +60,8 @@ struct GemmProblem {
   int32_t row_div;
   const int32_t* m_count;
   int32_t m_const;
-  int32_t m_tiles;
+  int32_t m_tiles_rows;  // upper bound of rows per group (C, or T when dense)
+  int32_t m_tiles;       // filled by the launcher for its tile height
   const void* B0;
   const void* B1;  // SwiGLU up projection (gated kernel only)
   int64_t b_gstride;
