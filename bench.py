@@ -38,7 +38,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="oracle sample size in tokens (0 = sized from a short probe run so "
+                         "that the timed oracle run takes about --cpu-seconds)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MiB (a "
                          "known-size reference for hardware byte counters)")
@@ -198,9 +201,19 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        n = args.cpu_tokens or (256 if w.E >= 128 else 512)
-        n = min(n, w.T)
-        v, dt, threads = cpu_baseline(w, inp, n)
+        if args.cpu_tokens:
+            n = min(args.cpu_tokens, w.T)
+            v, dt, threads = cpu_baseline(w, inp, n)
+        else:
+            # grow the sample until one run takes at least half of --cpu-seconds (the
+            # oracle's per-token rate rises with batch size, so a single probe misjudges)
+            n = min(w.T, 512)
+            while True:
+                v, dt, threads = cpu_baseline(w, inp, n)
+                if n >= w.T or dt >= 0.5 * args.cpu_seconds:
+                    break
+                grow = max(2.0, min(8.0, args.cpu_seconds / max(dt, 1e-3)))
+                n = min(w.T, int(n * grow) // 256 * 256)
         cpu = {"value": round(v, 2), "unit": "tokens/s", "cores": threads or os.cpu_count(),
                "kind": "oracle", "seconds": round(dt, 2),
                "sample": f"oracle forward (float64 NumPy) on the first {n} tokens of the "

@@ -428,7 +428,8 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t
   st = launch_reduce_scan(T, k, E, C, false, reinterpret_cast<int32_t*>(w.fp), nullptr, nullptr,
                           expert_used, expert_overflow, slot_assign, w, s);
   if (st != MOE_OK) return st;
-  return launch_assign(topk_idx, T, k, E, C, slot, kept, slot_assign, token_drops, w, s);
+  return launch_assign(topk_idx, T, k, E, C, slot, kept, slot_assign, token_drops, expert_used,
+                       w, s);
 }
 
 size_t moe_expert_mlp_workspace_size(const moe_experts_t* ex, int32_t rows) {
@@ -563,7 +564,7 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
                           a->expert_used, a->expert_overflow, a->slot_assign, f.rw, s);
   if (st != MOE_OK) return st;
   st = launch_assign(a->topk_idx, T, k, E, C, a->slot, a->kept, a->slot_assign, a->token_drops,
-                     f.rw, s);
+                     a->expert_used, f.rw, s);
   if (st != MOE_OK) return st;
 
   ExpertPlan plans[2];

@@ -7,9 +7,12 @@ namespace moe {
 
 // ---- routing / dispatch ---------------------------------------------------------
 // Tokens per routing block. The per-block partial counts and probability sums are
-// stored expert-major, [E][nb], nb = ceil(T / kRouteTokens).
-constexpr int kRouteTokens = 16;
+// stored block-major, [nb][E], nb = ceil(T / kRouteTokens).
+constexpr int kRouteTokens = 32;
 inline int route_blocks(int T) { return (T + kRouteTokens - 1) / kRouteTokens; }
+// Routing blocks per scan chunk (the first level of the two-level offset scan).
+constexpr int kScanRows = 16;
+inline int scan_chunks(int T) { return (route_blocks(T) + kScanRows - 1) / kScanRows; }
 // Routing blocks per dispatch (slot assignment) block.
 inline int assign_group(int k) {
   int g = 512 / (kRouteTokens * k);
@@ -18,10 +21,12 @@ inline int assign_group(int k) {
 
 // Workspace carve-up shared by route and dispatch.
 struct RouteWs {
-  int32_t* flags;      // [0] error word, [1] finished-block ticket
-  int32_t* cnt_part;   // [E][nb]
-  int32_t* off_part;   // [E][nb]
-  float* prob_part;    // [E][nb]
+  int32_t* flags;      // [0] error word
+  int32_t* cnt_part;   // [nb][E]
+  float* prob_part;    // [nb][E]
+  int32_t* chunk_cnt;  // [nc][E] counts per chunk of kScanRows routing blocks
+  float* chunk_prob;   // [nc][E]
+  int32_t* chunk_off;  // [nc][E] exclusive offsets of the chunks
   float* fp;           // [E] f_e * P_e
   size_t bytes;
 };
@@ -35,9 +40,10 @@ moe_status_t launch_count(const int32_t* idx, int T, int k, int E, const RouteWs
 moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int32_t* count,
                                 float* prob_sum, float* aux, int32_t* used, int32_t* overflow,
                                 int32_t* slot_assign, const RouteWs& w, hipStream_t s);
+// `used` (from launch_reduce_scan) also drives the -1 fill of unfilled slots.
 moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32_t* slot,
                            uint8_t* kept, int32_t* slot_assign, int32_t* drops,
-                           const RouteWs& w, hipStream_t s);
+                           const int32_t* used, const RouteWs& w, hipStream_t s);
 
 // ---- grouped GEMMs ----------------------------------------------------------------
 enum Epi : int32_t {

@@ -1,23 +1,27 @@
 // Routing and position-priority dispatch for gfx950.
 //
-// route_kernel     one wavefront per token: fp32 softmax over the E logits, top-k by
-//                  logit with exact ties to the lower expert index, gates renormalised
-//                  over the k choices ("Top-k MoE Router with Load Statistics", alpha
-//                  equation; "Sparse MoE Layer in NumPy", top_k_gating), plus per-block
-//                  pre-drop counts and probability sums (trap 6 of the same page).
+// route_kernel     fp32 softmax over the E logits of a token, top-k by logit with exact
+//                  ties to the lower expert index, gates renormalised over the k
+//                  choices ("Top-k MoE Router with Load Statistics", alpha equation;
+//                  "Sparse MoE Layer in NumPy", top_k_gating), plus per-block pre-drop
+//                  counts and probability sums (trap 6 of the same page). A token is
+//                  handled by a group of L lanes (8..64) holding V <= 16 logits each, so
+//                  a wavefront works on 64/L tokens at once and every reduction stays
+//                  inside the group.
 // count_kernel     per-block expert histogram of caller-supplied choices.
-// reduce_scan      one block per expert: exclusive scan of the per-block counts in
-//                  block order, totals, used/overflow, prob_sum, and the aux loss
-//                  (finished by the last block to arrive, in a fixed summation order).
+// chunk_sum        per chunk of kScanRows routing blocks, the per-expert sums.
+// scan_kernel      one block: per expert, the exclusive scan of the chunk sums in chunk
+//                  order, totals, used/overflow, prob_sum, and the aux loss, all summed
+//                  in a fixed order (bitwise reproducible, no atomics or fences).
 // assign_kernel    slots: a stable rank of each assignment among earlier assignments to
 //                  the same expert inside the block (wave ballots, then a per-wave
 //                  prefix), plus the block's scanned offset. This reproduces the serial
 //                  token-then-choice loop of position_priority_dispatch ("Sparse MoE
-//                  Layer in NumPy", trap 3) exactly, with no serial pass.
+//                  Layer in NumPy", trap 3) exactly. The grid also writes -1 into the
+//                  unfilled tail of every expert's slot table.
 //
-// Everything that decides an integer is integer or comparison work, so the indices,
-// slots and counts are bit-exact; the float reductions run in a fixed order so that
-// repeated runs are bitwise identical.
+// Per-block partial arrays are block-major, [nb][E], so every block writes and the scan
+// reads whole rows.
 
 #include "internal.h"
 
@@ -32,126 +36,151 @@ RouteWs carve_route_ws(void* ws, int T, int E) {
   off += 256;
   w.cnt_part = reinterpret_cast<int32_t*>(p + off);
   off = align_up(off + sizeof(int32_t) * size_t(E) * nb, 256);
-  w.off_part = reinterpret_cast<int32_t*>(p + off);
-  off = align_up(off + sizeof(int32_t) * size_t(E) * nb, 256);
   w.prob_part = reinterpret_cast<float*>(p + off);
   off = align_up(off + sizeof(float) * size_t(E) * nb, 256);
+  const int nc = scan_chunks(T);
+  w.chunk_cnt = reinterpret_cast<int32_t*>(p + off);
+  off = align_up(off + sizeof(int32_t) * size_t(E) * nc, 256);
+  w.chunk_prob = reinterpret_cast<float*>(p + off);
+  off = align_up(off + sizeof(float) * size_t(E) * nc, 256);
+  w.chunk_off = reinterpret_cast<int32_t*>(p + off);
+  off = align_up(off + sizeof(int32_t) * size_t(E) * nc, 256);
   w.fp = reinterpret_cast<float*>(p + off);
   off = align_up(off + sizeof(float) * size_t(E), 256);
   w.bytes = off;
   return w;
 }
 
-// EPL: experts held per lane (E <= 64 * EPL). KR: register slots for the k results per
-// lane (k <= 64 * KR).
-template <int EPL, int KR>
+namespace {
+
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, L));
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, L);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) {
+    const uint64_t o = __shfl_xor(v, m, L);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+}  // namespace
+
+// L lanes per token, V logits per lane (E <= L*V), KR result slots per lane (k <= L*KR).
+template <int L, int V, int KR>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
                                                     int E, int k, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
                                                     int32_t* __restrict__ cnt_part,
-                                                    float* __restrict__ prob_part,
-                                                    int32_t* __restrict__ flags) {
-  __shared__ int s_hist[64 * EPL];
-  __shared__ float s_prob[4][64 * EPL];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int nb = gridDim.x;
-  for (int e = threadIdx.x; e < 64 * EPL; e += 256) s_hist[e] = 0;
+                                                    float* __restrict__ prob_part) {
+  constexpr int TPR = 256 / L;  // tokens per round of the block
+  __shared__ int s_hist[L * V];
+  __shared__ float s_prob[TPR][L * V];
+  const int tid = threadIdx.x;
+  const int grp = tid / L;
+  const int li = tid % L;
+  for (int e = tid; e < L * V; e += 256) s_hist[e] = 0;
   __syncthreads();
 
-  float acc[EPL];
+  float acc[V];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
 
   const int t0 = blockIdx.x * kRouteTokens;
-  for (int tt = wv; tt < kRouteTokens; tt += 4) {
-    const int t = t0 + tt;
-    if (t >= T) break;
-    const float* row = logits + size_t(t) * E;
-    float s[EPL];
-    uint64_t key[EPL];
-    float mx = -INFINITY;
+  for (int r = 0; r < kRouteTokens / TPR; ++r) {
+    const int t = t0 + r * TPR + grp;
+    if (t >= T) break;  // uniform across the group
+    const float* row = logits + size_t(t) * E + li * V;
+    float s[V];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      s[i] = (e < E) ? row[e] : -INFINITY;
-      mx = fmaxf(mx, s[i]);
-    }
-    mx = wave_max(mx);
-    float p[EPL];
+    for (int i = 0; i < V; ++i) s[i] = (li * V + i < E) ? row[i] : -INFINITY;
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < V; ++i) mx = fmaxf(mx, s[i]);
+    mx = group_max<L>(mx);
+    float p[V];
     float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      p[i] = (e < E) ? __expf(s[i] - mx) : 0.f;
+    for (int i = 0; i < V; ++i) {
+      p[i] = (li * V + i < E) ? __expf(s[i] - mx) : 0.f;
       sum += p[i];
-      key[i] = (e < E) ? ((uint64_t(orderable(s[i])) << 32) | uint32_t(0xffffffffu - uint32_t(e)))
-                       : 0ull;
     }
-    sum = wave_sum(sum);
+    sum = group_sum<L>(sum);
     const float inv = 1.0f / sum;
+    uint64_t key[V];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
+    for (int i = 0; i < V; ++i) {
       p[i] *= inv;
       acc[i] += p[i];
+      const int e = li * V + i;
+      key[i] = (e < E) ? ((uint64_t(orderable(s[i])) << 32) | uint32_t(0xffffffffu - uint32_t(e))) : 0ull;
     }
 
     int my_e[KR];
     float my_p[KR];
 #pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      my_e[r] = 0;
-      my_p[r] = 0.f;
+    for (int q = 0; q < KR; ++q) {
+      my_e[q] = 0;
+      my_p[q] = 0.f;
     }
     float gsum = 0.f;
     for (int j = 0; j < k; ++j) {
       uint64_t best = key[0];
 #pragma unroll
-      for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
+      for (int i = 1; i < V; ++i) best = key[i] > best ? key[i] : best;
+      best = group_max_u64<L>(best);
       const int e = int(0xffffffffu - uint32_t(best));
-      const int owner = e & 63;
-      const int si = e >> 6;
+      const int owner = e / V;
+      const int si = e - owner * V;
       float pv = 0.f;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        if (i == si) {
+      for (int i = 0; i < V; ++i) {
+        if (li == owner && i == si) {
           pv = p[i];
-          if (lane == owner) key[i] = 0ull;
+          key[i] = 0ull;
         }
       }
-      const float pe = __shfl(pv, owner, kWave);
+      const float pe = __shfl(pv, owner, L);
       gsum += pe;
 #pragma unroll
-      for (int r = 0; r < KR; ++r) {
-        if (lane == (j & 63) && r == (j >> 6)) {
-          my_e[r] = e;
-          my_p[r] = pe;
+      for (int q = 0; q < KR; ++q) {
+        if (li == (j % L) && q == (j / L)) {
+          my_e[q] = e;
+          my_p[q] = pe;
         }
       }
     }
 #pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const int j = lane + 64 * r;
+    for (int q = 0; q < KR; ++q) {
+      const int j = li + L * q;
       if (j < k) {
-        idx_out[size_t(t) * k + j] = my_e[r];
-        gate_out[size_t(t) * k + j] = my_p[r] / gsum;
-        atomicAdd(&s_hist[my_e[r]], 1);
+        idx_out[size_t(t) * k + j] = my_e[q];
+        gate_out[size_t(t) * k + j] = my_p[q] / gsum;
+        atomicAdd(&s_hist[my_e[q]], 1);
       }
     }
   }
 
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) s_prob[wv][lane + 64 * i] = acc[i];
+  for (int i = 0; i < V; ++i) s_prob[grp][li * V + i] = acc[i];
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    const float v = ((s_prob[0][e] + s_prob[1][e]) + s_prob[2][e]) + s_prob[3][e];
-    prob_part[size_t(e) * nb + blockIdx.x] = v;
-    cnt_part[size_t(e) * nb + blockIdx.x] = s_hist[e];
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    flags[0] = 0;
-    flags[1] = 0;
+  const size_t base = size_t(blockIdx.x) * E;
+  for (int e = tid; e < E; e += 256) {
+    float v = 0.f;
+    for (int g2 = 0; g2 < TPR; ++g2) v += s_prob[g2][e];
+    prob_part[base + e] = v;
+    cnt_part[base + e] = s_hist[e];
   }
 }
 
@@ -159,81 +188,93 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 // outside [0, E) are skipped here and reported by assign_kernel.
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx, int T,
                                                     int k, int E,
-                                                    int32_t* __restrict__ cnt_part,
-                                                    int32_t* __restrict__ flags) {
-  extern __shared__ int s_hist[];
-  const int nb = gridDim.x;
-  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+                                                    int32_t* __restrict__ cnt_part) {
+  extern __shared__ int s_cnt[];
+  for (int e = threadIdx.x; e < E; e += 256) s_cnt[e] = 0;
   __syncthreads();
   const int t0 = blockIdx.x * kRouteTokens;
   const int t1 = min(T, t0 + kRouteTokens);
   for (int a = t0 * k + threadIdx.x; a < t1 * k; a += 256) {
     const int e = idx[a];
-    if (e >= 0 && e < E) atomicAdd(&s_hist[e], 1);
+    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) cnt_part[size_t(e) * nb + blockIdx.x] = s_hist[e];
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    flags[0] = 0;
-    flags[1] = 0;
+  for (int e = threadIdx.x; e < E; e += 256) cnt_part[size_t(blockIdx.x) * E + e] = s_cnt[e];
+}
+
+// Chunk sums: block c adds the per-block partials of routing blocks c*kScanRows ..
+// (c+1)*kScanRows - 1 (in block order) for every expert.
+__global__ __launch_bounds__(256) void chunk_sum_kernel(const int32_t* __restrict__ cnt_part,
+                                                        const float* __restrict__ prob_part,
+                                                        int nb, int E, int with_prob,
+                                                        int32_t* __restrict__ chunk_cnt,
+                                                        float* __restrict__ chunk_prob) {
+  const int c = blockIdx.x;
+  const int b0 = c * kScanRows;
+  const int b1 = min(nb, b0 + kScanRows);
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int cs = 0;
+    float ps = 0.f;
+    for (int b = b0; b < b1; ++b) {
+      cs += cnt_part[size_t(b) * E + e];
+      if (with_prob) ps += prob_part[size_t(b) * E + e];
+    }
+    chunk_cnt[size_t(c) * E + e] = cs;
+    if (with_prob) chunk_prob[size_t(c) * E + e] = ps;
   }
 }
 
-// One block per expert. Exclusive scan over the nb per-block counts (in block order),
-// totals and, when requested, dispatch bookkeeping. The last block to finish sums the
-// per-expert aux terms in expert order.
-__global__ __launch_bounds__(256) void reduce_scan_kernel(
-    const int32_t* __restrict__ cnt_part, const float* __restrict__ prob_part,
-    int32_t* __restrict__ off_part, int nb, int T, int k, int E, int C, int with_prob,
-    int32_t* __restrict__ count_out, float* __restrict__ prob_out, float* __restrict__ aux_out,
-    int32_t* __restrict__ used_out, int32_t* __restrict__ overflow_out,
-    int32_t* __restrict__ slot_assign, float* __restrict__ fp, int32_t* __restrict__ flags) {
-  __shared__ int s_c[256];
-  __shared__ float s_p[256];
-  __shared__ int s_last;
-  const int e = blockIdx.x;
+// One block of E*P threads (E*P <= 1024): thread (e, part) owns expert e and the chunk
+// range part*seg .. +seg. It sums its chunks, takes the exclusive prefix of the earlier
+// ranges, and writes each chunk's starting offset. Totals, prob_sum (ranges added in
+// order) and the aux loss (fixed tree over experts) follow; all of it is reproducible
+// bit for bit and needs no atomics or fences.
+__global__ __launch_bounds__(1024) void scan_kernel(
+    const int32_t* __restrict__ chunk_cnt, const float* __restrict__ chunk_prob,
+    int32_t* __restrict__ chunk_off, int nchunks, int P, int T, int k, int E, int C,
+    int with_prob, int32_t* __restrict__ count_out, float* __restrict__ prob_out,
+    float* __restrict__ aux_out, int32_t* __restrict__ used_out,
+    int32_t* __restrict__ overflow_out, int32_t* __restrict__ flags) {
+  __shared__ int s_c[1024];
+  __shared__ float s_p[1024];
   const int tid = threadIdx.x;
-  const int seg = (nb + 255) / 256;
-  const int lo = min(nb, tid * seg);
-  const int hi = min(nb, lo + seg);
-  const int32_t* cp = cnt_part + size_t(e) * nb;
+  const int e = tid % E;
+  const int part = tid / E;
+  const bool active = part < P;
+  const int seg = (nchunks + P - 1) / P;
+  const int lo = min(nchunks, part * seg);
+  const int hi = min(nchunks, lo + seg);
   int csum = 0;
   float psum = 0.f;
-  for (int b = lo; b < hi; ++b) csum += cp[b];
-  if (with_prob) {
-    const float* pp = prob_part + size_t(e) * nb;
-    for (int b = lo; b < hi; ++b) psum += pp[b];
+  if (active) {
+    for (int c = lo; c < hi; ++c) {
+      csum += chunk_cnt[size_t(c) * E + e];
+      if (with_prob) psum += chunk_prob[size_t(c) * E + e];
+    }
   }
   s_c[tid] = csum;
   s_p[tid] = psum;
   __syncthreads();
-  // Hillis-Steele inclusive scan of the per-thread sums (integer: order-free).
-  for (int d = 1; d < 256; d <<= 1) {
-    const int v = tid >= d ? s_c[tid - d] : 0;
-    __syncthreads();
-    s_c[tid] += v;
-    __syncthreads();
-  }
-  const int total = s_c[255];
-  int run = s_c[tid] - csum;
-  if (off_part != nullptr) {
-    int32_t* op = off_part + size_t(e) * nb;
-    for (int b = lo; b < hi; ++b) {
-      op[b] = run;
-      run += cp[b];
+  if (active && chunk_off != nullptr) {
+    int run = 0;
+    for (int q = 0; q < part; ++q) run += s_c[q * E + e];
+    for (int c = lo; c < hi; ++c) {
+      chunk_off[size_t(c) * E + e] = run;
+      run += chunk_cnt[size_t(c) * E + e];
     }
   }
-  // fixed-shape tree for the probability sum
-  for (int d = 128; d >= 1; d >>= 1) {
-    if (tid < d) s_p[tid] += s_p[tid + d];
-    __syncthreads();
-  }
-  if (tid == 0) {
+  float fpv = 0.f;
+  if (part == 0) {
+    int total = 0;
+    float P_e = 0.f;
+    for (int q = 0; q < P; ++q) {
+      total += s_c[q * E + e];
+      P_e += s_p[q * E + e];
+    }
     count_out[e] = total;
     if (with_prob) {
-      const float P = s_p[0];
-      prob_out[e] = P;
-      fp[e] = (float(total) / (float(T) * float(k))) * (P / float(T));
+      prob_out[e] = P_e;
+      fpv = (float(total) / (float(T) * float(k))) * (P_e / float(T));
     }
     if (C >= 0) {
       const int used = min(total, C);
@@ -241,46 +282,36 @@ __global__ __launch_bounds__(256) void reduce_scan_kernel(
       overflow_out[e] = total - used;
     }
   }
-  if (C >= 0) {
-    const int used = min(total, C);
-    for (int c = used + tid; c < C; c += 256) slot_assign[size_t(e) * C + c] = -1;
-  }
+  if (tid == 0) flags[0] = 0;
   if (!with_prob) return;
-  __threadfence();
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&flags[1], 1) == int(gridDim.x) - 1);
+  s_p[tid] = (part == 0) ? fpv : 0.f;
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  float v = 0.f;
-  for (int i = tid; i < E; i += 256) v += __builtin_nontemporal_load(&fp[i]);
-  s_p[tid] = v;
-  __syncthreads();
-  for (int d = 128; d >= 1; d >>= 1) {
+  for (int d = 512; d >= 1; d >>= 1) {
     if (tid < d) s_p[tid] += s_p[tid + d];
     __syncthreads();
   }
-  if (tid == 0) {
-    aux_out[0] = float(E) * s_p[0];
-    flags[1] = 0;
-  }
+  if (tid == 0) aux_out[0] = float(E) * s_p[0];
 }
 
-// Slot assignment. Block b covers tokens [b*G*16, (b+1)*G*16) (G routing blocks) and
+// Slot assignment. Block b covers tokens [b*G*kRouteTokens, ...) (G routing blocks) and
 // walks its assignments in chunks of 256 (a = t*k + j ascending). Within a chunk each
 // wave finds, by ballots on the expert-id bits, the lanes holding the same expert, and
 // ranks a lane by the equal lanes below it; waves are ordered through a per-wave
 // histogram in LDS; chunks through a running per-expert count that starts at the
-// scanned offset of the block.
+// offset of the block (its chunk's scanned offset plus the counts of the earlier routing
+// blocks of that chunk). The grid then writes -1 into slot_assign[e, c] for
+// c >= used[e] (a grid-stride pass over the E*C table).
 __global__ __launch_bounds__(256) void assign_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int C, int G,
-    const int32_t* __restrict__ off_part, int nb, int ebits, int32_t* __restrict__ slot,
-    uint8_t* __restrict__ kept, int32_t* __restrict__ slot_assign, int32_t* __restrict__ drops,
-    int32_t* __restrict__ flags) {
+    const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ cnt_part, int ebits,
+    const int32_t* __restrict__ used,
+    int32_t* __restrict__ slot, uint8_t* __restrict__ kept, int32_t* __restrict__ slot_assign,
+    int32_t* __restrict__ drops, int32_t* __restrict__ flags) {
   extern __shared__ int smem[];
   int* s_run = smem;                // [E]
   int* s_wh = smem + E;             // [4][E]
-  int* s_tk = smem + 5 * E;         // [G*16] kept choices per token
+  int* s_tk = smem + 5 * E;         // [G*kRouteTokens] kept choices per token
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -288,8 +319,11 @@ __global__ __launch_bounds__(256) void assign_kernel(
   const int tok0 = blockIdx.x * tokens;
   const int tok1 = min(T, tok0 + tokens);
   const int rb = blockIdx.x * G;    // first routing block of this block
+  const int cb = rb / kScanRows;
   for (int e = tid; e < E; e += 256) {
-    s_run[e] = off_part[size_t(e) * nb + rb];
+    int run = chunk_off[size_t(cb) * E + e];
+    for (int b = cb * kScanRows; b < rb; ++b) run += cnt_part[size_t(b) * E + e];
+    s_run[e] = run;
     s_wh[e] = 0;
     s_wh[E + e] = 0;
     s_wh[2 * E + e] = 0;
@@ -346,53 +380,74 @@ __global__ __launch_bounds__(256) void assign_kernel(
     __syncthreads();
   }
   for (int t = tid; t < tok1 - tok0; t += 256) drops[tok0 + t] = k - s_tk[t];
+  // unfilled slots
+  const int64_t total = int64_t(E) * C;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + tid; i < total; i += int64_t(gridDim.x) * 256) {
+    const int ee = int(i / C);
+    const int c = int(i - int64_t(ee) * C);
+    if (c >= used[ee]) slot_assign[i] = -1;
+  }
 }
 
-template <int EPL>
-static moe_status_t launch_route_epl(const float* logits, int T, int E, int k, int32_t* idx,
-                                     float* gate, const RouteWs& w, hipStream_t s) {
+template <int L, int V>
+static moe_status_t launch_route_lv(const float* logits, int T, int E, int k, int32_t* idx,
+                                    float* gate, const RouteWs& w, hipStream_t s) {
   const int nb = route_blocks(T);
-  if (k <= 64) {
-    MOE_LAUNCH("route", (route_kernel<EPL, 1>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
-               gate, w.cnt_part, w.prob_part, w.flags);
+  if (k <= L) {
+    MOE_LAUNCH("route", (route_kernel<L, V, 1>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
+               gate, w.cnt_part, w.prob_part);
+  } else if (k <= 4 * L) {
+    MOE_LAUNCH("route", (route_kernel<L, V, 4>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
+               gate, w.cnt_part, w.prob_part);
   } else {
-    MOE_LAUNCH("route", (route_kernel<EPL, 4>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
-               gate, w.cnt_part, w.prob_part, w.flags);
+    MOE_LAUNCH("route", (route_kernel<L, V, 32>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
+               gate, w.cnt_part, w.prob_part);
   }
   return MOE_OK;
 }
 
 moe_status_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* gate,
                           const RouteWs& w, hipStream_t s) {
-  if (E <= 64) return launch_route_epl<1>(logits, T, E, k, idx, gate, w, s);
-  if (E <= 128) return launch_route_epl<2>(logits, T, E, k, idx, gate, w, s);
-  if (E <= 256) return launch_route_epl<4>(logits, T, E, k, idx, gate, w, s);
-  if (E <= 512) return launch_route_epl<8>(logits, T, E, k, idx, gate, w, s);
-  return launch_route_epl<16>(logits, T, E, k, idx, gate, w, s);
+  // L lanes per token with V = E / L <= 16 logits each (L >= 8 so that a round of the
+  // block covers at most kRouteTokens tokens)
+  if (E <= 8) return launch_route_lv<8, 1>(logits, T, E, k, idx, gate, w, s);
+  if (E <= 16) return launch_route_lv<8, 2>(logits, T, E, k, idx, gate, w, s);
+  if (E <= 32) return launch_route_lv<8, 4>(logits, T, E, k, idx, gate, w, s);
+  if (E <= 64) return launch_route_lv<8, 8>(logits, T, E, k, idx, gate, w, s);
+  if (E <= 128) return launch_route_lv<8, 16>(logits, T, E, k, idx, gate, w, s);
+  if (E <= 256) return launch_route_lv<16, 16>(logits, T, E, k, idx, gate, w, s);
+  if (E <= 512) return launch_route_lv<32, 16>(logits, T, E, k, idx, gate, w, s);
+  return launch_route_lv<64, 16>(logits, T, E, k, idx, gate, w, s);
 }
 
 moe_status_t launch_count(const int32_t* idx, int T, int k, int E, const RouteWs& w,
                           hipStream_t s) {
   const int nb = route_blocks(T);
   MOE_LAUNCH("count", count_kernel, dim3(nb), dim3(256), sizeof(int) * E, s, idx, T, k, E,
-             w.cnt_part, w.flags);
+             w.cnt_part);
   return MOE_OK;
 }
 
 moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int32_t* count,
                                 float* prob_sum, float* aux, int32_t* used, int32_t* overflow,
                                 int32_t* slot_assign, const RouteWs& w, hipStream_t s) {
+  (void)slot_assign;
   const int nb = route_blocks(T);
-  MOE_LAUNCH("reduce_scan", reduce_scan_kernel, dim3(E), dim3(256), 0, s, w.cnt_part,
-             w.prob_part, C >= 0 ? w.off_part : nullptr, nb, T, k, E, C, with_prob ? 1 : 0,
-             count, prob_sum, aux, used, overflow, slot_assign, w.fp, w.flags);
+  const int nchunks = scan_chunks(T);
+  MOE_LAUNCH("chunk_sum", chunk_sum_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt_part,
+             w.prob_part, nb, E, with_prob ? 1 : 0, w.chunk_cnt, w.chunk_prob);
+  int P = 1024 / E;
+  if (P < 1) P = 1;
+  if (P > nchunks) P = nchunks;
+  MOE_LAUNCH("scan", scan_kernel, dim3(1), dim3(1024), 0, s, w.chunk_cnt, w.chunk_prob,
+             C >= 0 ? w.chunk_off : nullptr, nchunks, P, T, k, E, C, with_prob ? 1 : 0, count,
+             prob_sum, aux, used, overflow, w.flags);
   return MOE_OK;
 }
 
 moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32_t* slot,
                            uint8_t* kept, int32_t* slot_assign, int32_t* drops,
-                           const RouteWs& w, hipStream_t s) {
-  const int nb = route_blocks(T);
+                           const int32_t* used, const RouteWs& w, hipStream_t s) {
   const int G = assign_group(k);
   const int tokens = G * kRouteTokens;
   const int blocks = (T + tokens - 1) / tokens;
@@ -400,7 +455,7 @@ moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32
   while ((1 << ebits) < E) ++ebits;
   const size_t shmem = sizeof(int) * (5 * size_t(E) + tokens);
   MOE_LAUNCH("assign", assign_kernel, dim3(blocks), dim3(256), shmem, s, idx, T, k, E, C, G,
-             w.off_part, nb, ebits, slot, kept, slot_assign, drops, w.flags);
+             w.chunk_off, w.cnt_part, ebits, used, slot, kept, slot_assign, drops, w.flags);
   return MOE_OK;
 }
 
