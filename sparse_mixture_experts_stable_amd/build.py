@@ -22,6 +22,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["api.hip", "route.hip", "gemm_bf16.hip", "gemm_f32.hip", "combine.hip"]
+# MFMA accumulators in arch VGPRs: avoids AGPR copy chains around the MFMA loops
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_VGPR_FORM: set = set()
 ARCH = "gfx950"
 
 
@@ -36,8 +39,6 @@ def compile_flags():
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA accumulators in arch VGPRs: avoids AGPR copy chains around the MFMA loops
-        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"),
     ]
 
@@ -45,6 +46,8 @@ def compile_flags():
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + compile_flags()
+    if src not in NO_VGPR_FORM:
+        cmd += VGPR_FORM
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

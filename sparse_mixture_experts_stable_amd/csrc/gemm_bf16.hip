@@ -39,88 +39,13 @@
 // tiles. Consecutive tiles belong to the same expert, so the tiles of one expert share
 // their weight panels in one XCD's L2.
 
-#include "internal.h"
+#include "gemm_bf16_tile.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int BK = kBf16BK;  // 64
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ int fswz(int m) { return (m ^ (m >> 3)) & 7; }
-// B rows: the 16-byte chunk index is XORed with an even value that differs for the four
-// rows one 16-lane group reads together and, in addition, between groups 0 and 1 (rows
-// k and k + 8), so that both 16 and 32 lanes per LDS cycle are conflict free.
-template <int RB>
-__device__ __forceinline__ int hswz(int k) {
-  if constexpr (RB == 128) return ((k ^ (k >> 3)) & 3) << 1;
-  return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
-}
-
-__device__ __forceinline__ int logical_block(int bid, int nblk) {
-  const int q = nblk >> 3, r = nblk & 7;
-  const int x = bid & 7, i = bid >> 3;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <int BM_, int BNE_, bool GATED_, int WGM_ = 2, int WGN_ = 2, int STAGES_ = 3>
-struct TileCfg {
-  static constexpr int STAGES = STAGES_;           // LDS ring depth
-  static constexpr int BM = BM_;                 // rows per block
-  static constexpr int BNE = BNE_;               // B columns staged per step (all matrices)
-  static constexpr bool GATED = GATED_;
-  static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid (rows x columns)
-  static constexpr int WAVES = WGM * WGN;
-  static constexpr int THREADS = 64 * WAVES;
-  static constexpr int NB = GATED ? 2 : 1;       // B matrices
-  static constexpr int BNQ = BNE / NB;           // columns per B matrix = output columns
-  static constexpr int WROWS = BM / WGM;         // rows per wave
-  static constexpr int WCOLS = BNQ / WGN;        // output columns per wave
-  static constexpr int TM = WROWS / 16;          // MFMA tiles per wave, rows
-  static constexpr int TN = WCOLS / 16;          // MFMA tiles per wave, columns per matrix
-  static constexpr int A_BYTES = BM * BK * 2;
-  static constexpr int BQ_BYTES = BK * BNQ * 2;  // one B matrix
-  static constexpr int STAGE = A_BYTES + NB * BQ_BYTES;
-  static constexpr int LDS = STAGES * STAGE;
-  static constexpr int A_INST = BM / 8 / WAVES;  // 1 KiB DMA loads of A per wave per step
-  static constexpr int B_RB = BNQ * 2;           // bytes per B row
-  static constexpr int B_RPI = 1024 / B_RB;      // B rows per 1 KiB load
-  static constexpr int B_IPQ = BK / B_RPI;       // loads per B matrix per step
-  static constexpr int B_INST = NB * B_IPQ / WAVES;  // per wave per step
-  static constexpr int LOADS = A_INST + B_INST;  // vector-memory ops per thread per step
-  static_assert(BM % (8 * WAVES) == 0, "A loads split evenly over the waves");
-  static_assert(NB * B_IPQ % WAVES == 0, "B loads split evenly over the waves");
-};
-
-// Requests the tiles of step kt into the LDS slot `dst` (one 1 KiB DMA per instruction).
-template <class CF>
-__device__ __forceinline__ void step_issue(char* __restrict__ dst, const bf16_t* const* a_src,
-                                           const bf16_t* const* b_src, int kt, int N, int wv) {
-  const int k0 = kt * BK;
-#pragma unroll
-  for (int t = 0; t < CF::A_INST; ++t)
-    __builtin_amdgcn_global_load_lds(a_src[t] + k0, (lds_void*)(dst + (wv * CF::A_INST + t) * 1024),
-                                     16, 0, 0);
-#pragma unroll
-  for (int t = 0; t < CF::B_INST; ++t) {
-    const int u = wv * CF::B_INST + t;
-    __builtin_amdgcn_global_load_lds(
-        b_src[t] + size_t(k0) * N,
-        (lds_void*)(dst + CF::A_BYTES + (u / CF::B_IPQ) * CF::BQ_BYTES + (u % CF::B_IPQ) * 1024),
-        16, 0, 0);
-  }
-}
+using namespace tile;
 
 // One K step: request step `nxt` into slot `nxt_slot`, then multiply the tiles in slot
 // `cur`. The two slots are distinct, which the restrict qualifiers state; that lets the
@@ -178,21 +103,11 @@ __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
 template <class CF, int EPI, bool OF32>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch batch) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  constexpr int BM = CF::BM, BNQ = CF::BNQ, NB = CF::NB, TM = CF::TM, TN = CF::TN;
+  constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
 
-  const int lid = logical_block(blockIdx.x, gridDim.x);
-  const int pi = (batch.nprob > 1 && lid >= batch.p[0].tiles) ? 1 : 0;
-  const GemmProblem& P = batch.p[pi];
-  int rem = pi ? lid - batch.p[0].tiles : lid;
-  const int per_group = P.m_tiles * P.n_tiles;
-  const int g = rem / per_group;
-  rem -= g * per_group;
-  const int nt = rem / P.m_tiles;
-  const int mt = rem - nt * P.m_tiles;
-  const int M = P.m_count ? P.m_count[g] : P.m_const;
-  const int m0 = mt * BM;
-  if (m0 >= M) return;
-  const int n0 = nt * BNQ;
+  const TileId tl = decode_tile<CF>(batch, logical_block(blockIdx.x, gridDim.x));
+  if (tl.m0 >= tl.M) return;
+  const GemmProblem& P = batch.p[tl.pi];
   const int N = P.N;
   const int K = P.K;
 
@@ -201,39 +116,9 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
   const int wv = tid >> 6;
   const int wm = wv % CF::WGM, wn = wv / CF::WGM;
 
-  // ---- per-lane DMA sources ----
-  // A: load t of wave wv fills LDS rows (wv*A_INST + t)*8 .. +8; this lane's row and
-  // its physical chunk p = lane % 8, which holds source chunk p ^ f(row).
   const bf16_t* a_src[CF::A_INST];
-  {
-    const bf16_t* Ab = static_cast<const bf16_t*>(P.A) + size_t(g) * P.a_gstride;
-#pragma unroll
-    for (int t = 0; t < CF::A_INST; ++t) {
-      const int row = (wv * CF::A_INST + t) * 8 + (lane >> 3);
-      int r = m0 + row;
-      if (r >= M) r = m0;
-      int src = r;
-      if (P.row_map) src = P.row_map[size_t(g) * P.row_map_ld + r] / P.row_div;
-      a_src[t] = Ab + size_t(src) * P.lda + 8 * ((lane & 7) ^ fswz(row));
-    }
-  }
-  // B: load t of wave wv is load u = wv*B_INST + t overall: matrix u / B_IPQ, rows
-  // (u % B_IPQ) * B_RPI .. +B_RPI; this lane's row and physical chunk.
   const bf16_t* b_src[CF::B_INST];
-  {
-    constexpr int CPR = CF::B_RB / 16;  // chunks per row
-#pragma unroll
-    for (int t = 0; t < CF::B_INST; ++t) {
-      const int u = wv * CF::B_INST + t;
-      const int q = u / CF::B_IPQ;
-      const int k = (u % CF::B_IPQ) * CF::B_RPI + lane / CPR;
-      const int c = (lane % CPR) ^ hswz<CF::B_RB>(k);
-      int col = n0 + 8 * c;
-      if (col >= N) col = 0;  // columns past N are never stored
-      b_src[t] = static_cast<const bf16_t*>(q ? P.B1 : P.B0) + size_t(g) * P.b_gstride +
-                 size_t(k) * N + col;
-    }
-  }
+  tile_sources<CF>(P, tl, wv, lane, a_src, b_src);
 
   f32x4 acc[NB][TM][TN];
 #pragma unroll
@@ -242,8 +127,6 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int fr = lane & 15, fc = lane >> 4;
 
   const int nk = K / BK;
   const int last = nk - 1;
@@ -265,52 +148,13 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
   wait_vmcnt<0>();  // the clamped tail loads still target LDS
   __syncthreads();
 
-  // ---- epilogue: lane holds C[m][n..n+3] ----
-  char* Cb = static_cast<char*>(P.C);
-  constexpr int es = OF32 ? 4 : 2;
   // bias of this block's columns, staged once in LDS (free after the main loop)
   float* sbias = reinterpret_cast<float*>(smem);
   if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
-    const bf16_t* bias = static_cast<const bf16_t*>(P.bias);
-    for (int c = tid; c < BNQ; c += CF::THREADS)
-      sbias[c] = (bias && n0 + c < N) ? bf16_to_f32(bias[size_t(g) * P.bias_gstride + n0 + c]) : 0.f;
+    stage_bias<CF>(P, tl, tid, sbias);
     __syncthreads();
   }
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * CF::WROWS + i * 16 + fr;
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int nl = wn * CF::WCOLS + j * 16 + fc * 4;
-      const int n = n0 + nl;
-      if (n >= N) continue;
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = acc[0][i][j][r];
-      if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = silu(v[r]) * acc[NB - 1][i][j][r];
-      }
-      if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
-        const float4 bb = *reinterpret_cast<const float4*>(sbias + nl);
-        v[0] += bb.x;
-        v[1] += bb.y;
-        v[2] += bb.z;
-        v[3] += bb.w;
-      }
-      if constexpr (EPI == EPI_GELU_BIAS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
-      }
-      char* dst = Cb + (size_t(g) * P.c_gstride + size_t(m) * P.ldc + n) * es;
-      if constexpr (OF32) {
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
-    }
-  }
+  store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, sbias, acc);
 }
 
 namespace {

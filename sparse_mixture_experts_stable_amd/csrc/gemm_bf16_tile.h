@@ -1,0 +1,223 @@
+// Pieces shared by the grouped bf16 GEMM kernels: the tile configuration, the LDS
+// layouts and their swizzles, the DMA requests that fill one LDS stage, the decoding of
+// a block's tile, and the epilogue.
+//
+// LDS stage layout (one K step of BK = 64):
+//   A (expert rows, k contiguous) is stored [m][k], 128 bytes per row, and read as one
+//   16-byte fragment per lane. Each lane fetches source chunk c ^ f(m),
+//   f(m) = (m ^ m/8) % 8, so that the 16 lanes of a fragment read hit distinct bank
+//   groups.
+//   B (weights, n contiguous: [k][n] per expert, as stored) is copied unchanged apart
+//   from a per-row XOR of the 16-byte chunk index (hswz); the k-major fragment each MFMA
+//   needs is assembled with two ds_read_b64_tr_b16 transpose reads. Within a 16-lane
+//   group that instruction hands lane l element l % 4 of the 8-byte pieces addressed by
+//   lanes l/4 + 4v (v = 0..3), so lane s of group g points at row 8g + (s%16)/4 (+4 for
+//   the second read) and column 4 (s % 4) of its 16-column slice.
+// Both operands move HBM -> LDS with global_load_lds_dwordx4: one instruction moves
+// 1 KiB (64 lanes x 16 bytes) to a contiguous LDS range.
+#pragma once
+
+#include "internal.h"
+
+namespace moe {
+namespace tile {
+
+constexpr int BK = kBf16BK;  // 64
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int fswz(int m) { return (m ^ (m >> 3)) & 7; }
+// B rows: the 16-byte chunk index is XORed with an even value that differs for the four
+// rows one 16-lane group reads together and, in addition, between groups 0 and 1 (rows
+// k and k + 8), so that both 16 and 32 lanes per LDS cycle are conflict free.
+template <int RB>
+__device__ __forceinline__ int hswz(int k) {
+  if constexpr (RB == 128) return ((k ^ (k >> 3)) & 3) << 1;
+  return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
+}
+
+// The hardware deals workgroups to the 8 XCDs round-robin; this maps the hardware id to
+// a logical id so that each XCD works through a contiguous range of logical ids.
+__device__ __forceinline__ int logical_block(int bid, int nblk) {
+  const int q = nblk >> 3, r = nblk & 7;
+  const int x = bid & 7, i = bid >> 3;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// s_waitcnt with the vector-memory and LDS counters both at zero.
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
+}
+
+template <int BM_, int BNE_, bool GATED_, int WGM_ = 2, int WGN_ = 2, int STAGES_ = 3>
+struct TileCfg {
+  static constexpr int STAGES = STAGES_;           // LDS ring depth
+  static constexpr int BM = BM_;                 // rows per block
+  static constexpr int BNE = BNE_;               // B columns staged per step (all matrices)
+  static constexpr bool GATED = GATED_;
+  static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid (rows x columns)
+  static constexpr int WAVES = WGM * WGN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int NB = GATED ? 2 : 1;       // B matrices
+  static constexpr int BNQ = BNE / NB;           // columns per B matrix = output columns
+  static constexpr int WROWS = BM / WGM;         // rows per wave
+  static constexpr int WCOLS = BNQ / WGN;        // output columns per wave
+  static constexpr int TM = WROWS / 16;          // MFMA tiles per wave, rows
+  static constexpr int TN = WCOLS / 16;          // MFMA tiles per wave, columns per matrix
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int BQ_BYTES = BK * BNQ * 2;  // one B matrix
+  static constexpr int STAGE = A_BYTES + NB * BQ_BYTES;
+  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int A_INST = BM / 8 / WAVES;  // 1 KiB DMA loads of A per wave per step
+  static constexpr int B_RB = BNQ * 2;           // bytes per B row
+  static constexpr int B_RPI = 1024 / B_RB;      // B rows per 1 KiB load
+  static constexpr int B_IPQ = BK / B_RPI;       // loads per B matrix per step
+  static constexpr int B_INST = NB * B_IPQ / WAVES;  // per wave per step
+  static constexpr int LOADS = A_INST + B_INST;  // vector-memory ops per thread per step
+  static_assert(BM % (8 * WAVES) == 0, "A loads split evenly over the waves");
+  static_assert(NB * B_IPQ % WAVES == 0, "B loads split evenly over the waves");
+};
+
+// Requests the tiles of step kt into the LDS stage `dst` (one 1 KiB DMA per instruction).
+template <class CF>
+__device__ __forceinline__ void step_issue(char* __restrict__ dst, const bf16_t* const* a_src,
+                                           const bf16_t* const* b_src, int kt, int N, int wv) {
+  const int k0 = kt * BK;
+#pragma unroll
+  for (int t = 0; t < CF::A_INST; ++t)
+    __builtin_amdgcn_global_load_lds(a_src[t] + k0, (lds_void*)(dst + (wv * CF::A_INST + t) * 1024),
+                                     16, 0, 0);
+#pragma unroll
+  for (int t = 0; t < CF::B_INST; ++t) {
+    const int u = wv * CF::B_INST + t;
+    __builtin_amdgcn_global_load_lds(
+        b_src[t] + size_t(k0) * N,
+        (lds_void*)(dst + CF::A_BYTES + (u / CF::B_IPQ) * CF::BQ_BYTES + (u % CF::B_IPQ) * 1024),
+        16, 0, 0);
+  }
+}
+
+// A tile of a grouped batch: problem, group (expert), first row and column, row count.
+struct TileId {
+  int pi, g, m0, n0, M;
+};
+
+// Decodes logical tile id `lid`: problems in order, then groups, then column tiles, then
+// row tiles (consecutive ids share a weight panel). M is the row count of the group.
+template <class CF>
+__device__ __forceinline__ TileId decode_tile(const GemmBatch& batch, int lid) {
+  TileId t;
+  t.pi = (batch.nprob > 1 && lid >= batch.p[0].tiles) ? 1 : 0;
+  const GemmProblem& P = batch.p[t.pi];
+  int rem = t.pi ? lid - batch.p[0].tiles : lid;
+  const int per_group = P.m_tiles * P.n_tiles;
+  t.g = rem / per_group;
+  rem -= t.g * per_group;
+  const int nt = rem / P.m_tiles;
+  const int mt = rem - nt * P.m_tiles;
+  t.M = P.m_count ? P.m_count[t.g] : P.m_const;
+  t.m0 = mt * CF::BM;
+  t.n0 = nt * CF::BNQ;
+  return t;
+}
+
+// Per-lane DMA sources of a tile. A: load t of wave wv fills LDS rows
+// (wv*A_INST + t)*8 .. +8; this lane's row and its physical chunk p = lane % 8, which
+// holds source chunk p ^ f(row). Rows past M repeat row m0 (never stored). B: load t of
+// wave wv is load u = wv*B_INST + t overall: matrix u / B_IPQ, rows
+// (u % B_IPQ) * B_RPI .. +B_RPI; columns past N read column 0 (never stored).
+template <class CF>
+__device__ __forceinline__ void tile_sources(const GemmProblem& P, const TileId& t, int wv,
+                                             int lane, const bf16_t** a_src,
+                                             const bf16_t** b_src) {
+  const bf16_t* Ab = static_cast<const bf16_t*>(P.A) + size_t(t.g) * P.a_gstride;
+#pragma unroll
+  for (int i = 0; i < CF::A_INST; ++i) {
+    const int row = (wv * CF::A_INST + i) * 8 + (lane >> 3);
+    int r = t.m0 + row;
+    if (r >= t.M) r = t.m0;
+    int src = r;
+    if (P.row_map) src = P.row_map[size_t(t.g) * P.row_map_ld + r] / P.row_div;
+    a_src[i] = Ab + size_t(src) * P.lda + 8 * ((lane & 7) ^ fswz(row));
+  }
+  constexpr int CPR = CF::B_RB / 16;  // chunks per row
+#pragma unroll
+  for (int i = 0; i < CF::B_INST; ++i) {
+    const int u = wv * CF::B_INST + i;
+    const int q = u / CF::B_IPQ;
+    const int k = (u % CF::B_IPQ) * CF::B_RPI + lane / CPR;
+    const int c = (lane % CPR) ^ hswz<CF::B_RB>(k);
+    int col = t.n0 + 8 * c;
+    if (col >= P.N) col = 0;
+    b_src[i] = static_cast<const bf16_t*>(q ? P.B1 : P.B0) + size_t(t.g) * P.b_gstride +
+               size_t(k) * P.N + col;
+  }
+}
+
+// Epilogue: lane holds C[m][n..n+3] of every MFMA tile (the MFMA ran with B as its first
+// operand, so each tile comes out transposed). `sbias` holds the block's BNQ bias values
+// (EPI_BIAS / EPI_GELU_BIAS only).
+template <class CF, int EPI, bool OF32>
+__device__ __forceinline__ void store_tile(const GemmProblem& P, const TileId& t, int wm, int wn,
+                                           int lane, const float* sbias,
+                                           const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  const int fr = lane & 15, fc = lane >> 4;
+  char* Cb = static_cast<char*>(P.C);
+  constexpr int es = OF32 ? 4 : 2;
+#pragma unroll
+  for (int i = 0; i < CF::TM; ++i) {
+    const int m = t.m0 + wm * CF::WROWS + i * 16 + fr;
+    if (m >= t.M) continue;
+#pragma unroll
+    for (int j = 0; j < CF::TN; ++j) {
+      const int nl = wn * CF::WCOLS + j * 16 + fc * 4;
+      const int n = t.n0 + nl;
+      if (n >= P.N) continue;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[0][i][j][r];
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = silu(v[r]) * acc[CF::NB - 1][i][j][r];
+      }
+      if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
+        const float4 bb = *reinterpret_cast<const float4*>(sbias + nl);
+        v[0] += bb.x;
+        v[1] += bb.y;
+        v[2] += bb.z;
+        v[3] += bb.w;
+      }
+      if constexpr (EPI == EPI_GELU_BIAS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
+      }
+      char* dst = Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * es;
+      if constexpr (OF32) {
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+  }
+}
+
+// Stages the bias of the block's BNQ columns in LDS as fp32 (zeros past N or without a
+// bias). The caller synchronises before the epilogue reads it.
+template <class CF>
+__device__ __forceinline__ void stage_bias(const GemmProblem& P, const TileId& t, int tid,
+                                           float* sbias) {
+  const bf16_t* bias = static_cast<const bf16_t*>(P.bias);
+  for (int c = tid; c < CF::BNQ; c += CF::THREADS)
+    sbias[c] = (bias && t.n0 + c < P.N) ? bf16_to_f32(bias[size_t(t.g) * P.bias_gstride + t.n0 + c]) : 0.f;
+}
+
+}  // namespace tile
+}  // namespace moe
