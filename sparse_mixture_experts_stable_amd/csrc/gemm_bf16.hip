@@ -53,12 +53,12 @@ using namespace tile;
 template <class CF>
 __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
                                                    char* __restrict__ nxt_slot,
-                                                   const bf16_t* const* a_src,
-                                                   const bf16_t* const* b_src, int nxt, int N,
+                                                   const DmaSrc<CF>& S, int nxt, int N,
                                                    int wv, int wm, int wn, int lane,
-                                                   f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+                                                   f32x4 (&acc)[CF::NB][CF::TM][CF::TN],
+                                                   bool issue = true) {
   constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
-  step_issue<CF>(nxt_slot, a_src, b_src, nxt, N, wv);
+  if (issue) issue_stage<CF>(nxt_slot, S, nxt, N, wv);
   const int fr = lane & 15, fc = lane >> 4;
   const int arow = wm * CF::WROWS + fr;
   // B transpose-read coordinates of this lane: k row within the 32-wide k step and the
@@ -113,12 +113,11 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv % CF::WGM, wn = wv / CF::WGM;
 
-  const bf16_t* a_src[CF::A_INST];
-  const bf16_t* b_src[CF::B_INST];
-  tile_sources<CF>(P, tl, wv, lane, a_src, b_src);
+  DmaSrc<CF> S;
+  tile_sources<CF>(P, tl, wv, lane, S);
 
   f32x4 acc[NB][TM][TN];
 #pragma unroll
@@ -130,20 +129,20 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
 
   const int nk = K / BK;
   const int last = nk - 1;
-  constexpr int S = CF::STAGES;
+  constexpr int NS = CF::STAGES;
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st)
-    step_issue<CF>(smem + st * CF::STAGE, a_src, b_src, st <= last ? st : last, N, wv);
+  for (int st = 0; st < NS - 1; ++st)
+    issue_stage<CF>(smem + st * CF::STAGE, S, st <= last ? st : last, N, wv);
   for (int kt = 0; kt < nk; ++kt) {
     // this thread's loads for step kt have landed (S-2 later steps may still be in
     // flight); after the barrier everyone's have, and every wave is done with step kt-1,
     // whose slot the next request reuses
-    wait_vmcnt<CF::LOADS * (S - 2)>();
+    wait_vmcnt<CF::LOADS * (NS - 2)>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const int nxt = kt + S - 1 <= last ? kt + S - 1 : last;
-    step_compute_issue<CF>(smem + (kt % S) * CF::STAGE, smem + ((kt + S - 1) % S) * CF::STAGE,
-                           a_src, b_src, nxt, N, wv, wm, wn, lane, acc);
+    const int nxt = kt + NS - 1 <= last ? kt + NS - 1 : last;
+    step_compute_issue<CF>(smem + (kt % NS) * CF::STAGE, smem + ((kt + NS - 1) % NS) * CF::STAGE,
+                           S, nxt, N, wv, wm, wn, lane, acc);
   }
   wait_vmcnt<0>();  // the clamped tail loads still target LDS
   __syncthreads();
@@ -155,6 +154,99 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
     __syncthreads();
   }
   store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, sbias, acc);
+}
+
+// Persistent form of the two-stage kernel: one block per CU walks a strided list of
+// tiles. XCD x (hardware blocks x, x+8, ...) owns a contiguous range of logical tiles, so
+// the blocks running together on one XCD work on neighbouring tiles, which share weight
+// panels in that XCD's L2. Empty tiles (no rows in the group) are skipped. On the last K
+// step of a tile the DMA request already targets step 0 of the block's next tile, so
+// that tile's first stage streams in while the epilogue of the current one runs; the
+// next tile's gathered row indices are read at the start of the current tile.
+template <class CF, int EPI, bool OF32>
+__global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(GemmBatch batch) {
+  static_assert(CF::STAGES == 2, "two-stage ring");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
+  const int nblk = gridDim.x;
+  const int x = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int nb_x = (nblk >> 3) + ((nblk & 7) > x ? 1 : 0);
+  const int q8 = batch.total >> 3, r8 = batch.total & 7;
+  const int lo = x * q8 + (x < r8 ? x : r8);
+  const int hi = lo + q8 + (x < r8 ? 1 : 0);
+
+  int t = lo + bi;
+  TileId tl;
+  for (; t < hi; t += nb_x) {
+    tl = decode_tile<CF>(batch, t);
+    if (tl.m0 < tl.M) break;
+  }
+  if (t >= hi) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv % CF::WGM, wn = wv / CF::WGM;
+
+  DmaSrc<CF> S;
+  tile_sources<CF>(batch.p[tl.pi], tl, wv, lane, S);
+  f32x4 acc[NB][TM][TN];
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue_stage<CF>(smem, S, 0, batch.p[tl.pi].N, wv);
+  int g = 0;  // steps done by this block: stage g & 1 holds the current one
+  while (true) {
+    const GemmProblem& P = batch.p[tl.pi];
+    // the block's next non-empty tile, and its gathered A rows
+    int t2 = t + nb_x;
+    TileId tl2;
+    for (; t2 < hi; t2 += nb_x) {
+      tl2 = decode_tile<CF>(batch, t2);
+      if (tl2.m0 < tl2.M) break;
+    }
+    const bool more = t2 < hi;
+    int rows2[CF::A_INST];
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < CF::A_INST; ++i) rows2[i] = tile_a_row<CF>(batch.p[tl2.pi], tl2, wv, lane, i);
+    }
+    const int nk = P.K / BK;
+    for (int kt = 0; kt < nk; ++kt, ++g) {
+      // this thread's loads for step kt have landed; after the barrier everyone's have,
+      // and every wave is done with the previous step, whose stage the next request uses
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      int knext = kt + 1, nN = P.N;
+      bool issue = true;
+      if (knext == nk) {
+        if (more) {
+          tile_sources_from_rows<CF>(batch.p[tl2.pi], tl2, wv, lane, rows2, S);
+          knext = 0;
+          nN = batch.p[tl2.pi].N;
+        } else {
+          issue = false;
+        }
+      }
+      step_compute_issue<CF>(smem + (g & 1) * CF::STAGE, smem + ((g + 1) & 1) * CF::STAGE, S,
+                             knext, nN, wv, wm, wn, lane, acc, issue);
+    }
+    store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, nullptr, acc);
+    if (!more) break;
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    t = t2;
+    tl = tl2;
+  }
 }
 
 namespace {
@@ -180,27 +272,71 @@ moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
   return MOE_OK;
 }
 
-template <class CF>
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+  }
+  return n;
+}
+
+template <class CF, int EPI, bool OF32>
+moe_status_t launch_persistent(GemmBatch& b, const char* name, hipStream_t s) {
+  b.total = 0;
+  for (int i = 0; i < b.nprob; ++i) {
+    GemmProblem& p = b.p[i];
+    p.m_tiles = (p.m_tiles_rows + CF::BM - 1) / CF::BM;
+    p.n_tiles = (p.N + CF::BNQ - 1) / CF::BNQ;
+    p.tiles = p.groups * p.m_tiles * p.n_tiles;
+    b.total += p.tiles;
+  }
+  if (b.total == 0) return MOE_OK;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_persistent_kernel<CF, EPI, OF32>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS) != hipSuccess)
+      return MOE_ERR_HIP;
+    attr_set = true;
+  }
+  const int grid = b.total < cu_count() ? int(b.total) : cu_count();
+  MOE_LAUNCH(name, (gemm_bf16_persistent_kernel<CF, EPI, OF32>), dim3(grid), dim3(CF::THREADS),
+             CF::LDS, s, b);
+  return MOE_OK;
+}
+
+template <class CF, int EPI, bool OF32, bool PERSISTENT>
+moe_status_t launch_one(GemmBatch& b, const char* name, hipStream_t s) {
+  if constexpr (PERSISTENT)
+    return launch_persistent<CF, EPI, OF32>(b, name, s);
+  else
+    return launch_cfg<CF, EPI, OF32>(b, name, s);
+}
+
+template <class CF, bool PERSISTENT>
 moe_status_t launch_epi(GemmBatch& b, const char* name, hipStream_t s) {
   const int epi = b.p[0].epi;
   for (int i = 1; i < b.nprob; ++i)
     if (b.p[i].epi != epi || b.p[i].out_f32 != b.p[0].out_f32) return MOE_ERR_UNSUPPORTED;
   if (b.p[0].out_f32) {
     if (epi != EPI_STORE) return MOE_ERR_UNSUPPORTED;
-    return launch_cfg<CF, EPI_STORE, true>(b, name, s);
+    return launch_one<CF, EPI_STORE, true, PERSISTENT>(b, name, s);
   }
   switch (epi) {
-    case EPI_STORE: return launch_cfg<CF, EPI_STORE, false>(b, name, s);
-    case EPI_BIAS: return launch_cfg<CF, EPI_BIAS, false>(b, name, s);
-    case EPI_GELU_BIAS: return launch_cfg<CF, EPI_GELU_BIAS, false>(b, name, s);
+    case EPI_STORE: return launch_one<CF, EPI_STORE, false, PERSISTENT>(b, name, s);
+    case EPI_BIAS: return launch_one<CF, EPI_BIAS, false, PERSISTENT>(b, name, s);
+    case EPI_GELU_BIAS: return launch_one<CF, EPI_GELU_BIAS, false, PERSISTENT>(b, name, s);
     default: return MOE_ERR_UNSUPPORTED;
   }
 }
 }  // namespace
 
 moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStream_t s) {
-  // Large tiles (256 x 256, 16 waves, two stages) when every problem has enough rows per
-  // group and the grid still holds at least two tiles per CU; else 128 x 128 tiles.
+  // Large tiles (256 x 256, 16 waves, two stages, persistent blocks) when every problem
+  // has enough rows per group and the grid still holds at least two tiles per CU; else
+  // 128 x 128 tiles.
   using Large = TileCfg<256, 256, true, 4, 4, 2>;
   bool large = true;
   long tiles = 0;
@@ -214,11 +350,11 @@ moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStr
   if (gated) {
     for (int i = 0; i < b.nprob; ++i)
       if (b.p[i].epi != EPI_SWIGLU || b.p[i].out_f32) return MOE_ERR_UNSUPPORTED;
-    return large ? launch_cfg<TileCfg<256, 256, true, 4, 4, 2>, EPI_SWIGLU, false>(b, name, s)
+    return large ? launch_persistent<TileCfg<256, 256, true, 4, 4, 2>, EPI_SWIGLU, false>(b, name, s)
                  : launch_cfg<TileCfg<128, 128, true, 2, 2, 3>, EPI_SWIGLU, false>(b, name, s);
   }
-  return large ? launch_epi<TileCfg<256, 256, false, 4, 4, 2>>(b, name, s)
-               : launch_epi<TileCfg<128, 128, false, 2, 2, 3>>(b, name, s);
+  return large ? launch_epi<TileCfg<256, 256, false, 4, 4, 2>, true>(b, name, s)
+               : launch_epi<TileCfg<128, 128, false, 2, 2, 3>, false>(b, name, s);
 }
 
 }  // namespace moe

@@ -86,21 +86,35 @@ struct TileCfg {
   static_assert(NB * B_IPQ % WAVES == 0, "B loads split evenly over the waves");
 };
 
-// Requests the tiles of step kt into the LDS stage `dst` (one 1 KiB DMA per instruction).
+// DMA sources of a tile: uniform group bases (scalar registers) and this lane's byte
+// offsets from them.
 template <class CF>
-__device__ __forceinline__ void step_issue(char* __restrict__ dst, const bf16_t* const* a_src,
-                                           const bf16_t* const* b_src, int kt, int N, int wv) {
-  const int k0 = kt * BK;
+struct DmaSrc {
+  const char* a;              // A of the group (uniform)
+  const char* b[CF::NB];      // B matrices of the group (uniform)
+  uint32_t ao[CF::A_INST];    // per lane: gathered row and swizzled chunk
+  uint32_t bo[CF::B_INST];    // per lane: k row and swizzled chunk
+};
+
+// Requests the tiles of step kt into the LDS stage `dst` (one 1 KiB DMA per instruction).
+// `wv` is the wave index (uniform).
+template <class CF>
+__device__ __forceinline__ void issue_stage(char* __restrict__ dst, const DmaSrc<CF>& S, int kt,
+                                            int N, int wv) {
+  const size_t ka = size_t(kt) * BK * 2;
+  const size_t kb = size_t(kt) * BK * size_t(N) * 2;
 #pragma unroll
-  for (int t = 0; t < CF::A_INST; ++t)
-    __builtin_amdgcn_global_load_lds(a_src[t] + k0, (lds_void*)(dst + (wv * CF::A_INST + t) * 1024),
-                                     16, 0, 0);
+  for (int t = 0; t < CF::A_INST; ++t) {
+    const char* g = S.a + ka + S.ao[t];
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(dst + (wv * CF::A_INST + t) * 1024), 16, 0, 0);
+  }
 #pragma unroll
   for (int t = 0; t < CF::B_INST; ++t) {
     const int u = wv * CF::B_INST + t;
+    const char* bq = (CF::NB > 1 && u / CF::B_IPQ) ? S.b[CF::NB - 1] : S.b[0];
+    const char* g = bq + kb + S.bo[t];
     __builtin_amdgcn_global_load_lds(
-        b_src[t] + size_t(k0) * N,
-        (lds_void*)(dst + CF::A_BYTES + (u / CF::B_IPQ) * CF::BQ_BYTES + (u % CF::B_IPQ) * 1024),
+        g, (lds_void*)(dst + CF::A_BYTES + (u / CF::B_IPQ) * CF::BQ_BYTES + (u % CF::B_IPQ) * 1024),
         16, 0, 0);
   }
 }
@@ -123,48 +137,66 @@ __device__ __forceinline__ TileId decode_tile(const GemmBatch& batch, int lid) {
   rem -= t.g * per_group;
   const int nt = rem / P.m_tiles;
   const int mt = rem - nt * P.m_tiles;
-  t.M = P.m_count ? P.m_count[t.g] : P.m_const;
+  // the same value in every lane: keep it (and all tile bookkeeping) in scalar registers
+  t.M = P.m_count ? __builtin_amdgcn_readfirstlane(P.m_count[t.g]) : P.m_const;
   t.m0 = mt * CF::BM;
   t.n0 = nt * CF::BNQ;
   return t;
 }
 
-// Per-lane DMA sources of a tile. A: load t of wave wv fills LDS rows
-// (wv*A_INST + t)*8 .. +8; this lane's row and its physical chunk p = lane % 8, which
-// holds source chunk p ^ f(row). Rows past M repeat row m0 (never stored). B: load t of
-// wave wv is load u = wv*B_INST + t overall: matrix u / B_IPQ, rows
-// (u % B_IPQ) * B_RPI .. +B_RPI; columns past N read column 0 (never stored).
+// The A source row of DMA load i of this lane for tile t: load i of wave wv fills LDS
+// rows (wv*A_INST + i)*8 .. +8, this lane row (lane / 8); rows past M repeat row m0
+// (never stored); with a row map the row is the gathered token (or slot) row.
 template <class CF>
-__device__ __forceinline__ void tile_sources(const GemmProblem& P, const TileId& t, int wv,
-                                             int lane, const bf16_t** a_src,
-                                             const bf16_t** b_src) {
-  const bf16_t* Ab = static_cast<const bf16_t*>(P.A) + size_t(t.g) * P.a_gstride;
+__device__ __forceinline__ int tile_a_row(const GemmProblem& P, const TileId& t, int wv, int lane,
+                                          int i) {
+  const int row = (wv * CF::A_INST + i) * 8 + (lane >> 3);
+  int r = t.m0 + row;
+  if (r >= t.M) r = t.m0;
+  return P.row_map ? P.row_map[size_t(t.g) * P.row_map_ld + r] / P.row_div : r;
+}
+
+// DMA sources of tile t from the A rows of tile_a_row. A: this lane's physical chunk
+// p = lane % 8 holds source chunk p ^ f(row). B: load i of wave wv is load
+// u = wv*B_INST + i overall: matrix u / B_IPQ, rows (u % B_IPQ) * B_RPI .. +B_RPI;
+// columns past N read column 0 (never stored).
+template <class CF>
+__device__ __forceinline__ void tile_sources_from_rows(const GemmProblem& P, const TileId& t,
+                                                       int wv, int lane, const int* rows,
+                                                       DmaSrc<CF>& S) {
+  S.a = static_cast<const char*>(P.A) + size_t(t.g) * P.a_gstride * 2;
+  S.b[0] = static_cast<const char*>(P.B0) + size_t(t.g) * P.b_gstride * 2;
+  if constexpr (CF::NB > 1) S.b[CF::NB - 1] = static_cast<const char*>(P.B1) + size_t(t.g) * P.b_gstride * 2;
 #pragma unroll
   for (int i = 0; i < CF::A_INST; ++i) {
     const int row = (wv * CF::A_INST + i) * 8 + (lane >> 3);
-    int r = t.m0 + row;
-    if (r >= t.M) r = t.m0;
-    int src = r;
-    if (P.row_map) src = P.row_map[size_t(t.g) * P.row_map_ld + r] / P.row_div;
-    a_src[i] = Ab + size_t(src) * P.lda + 8 * ((lane & 7) ^ fswz(row));
+    S.ao[i] = uint32_t((size_t(rows[i]) * P.lda + 8 * ((lane & 7) ^ fswz(row))) * 2);
   }
   constexpr int CPR = CF::B_RB / 16;  // chunks per row
 #pragma unroll
   for (int i = 0; i < CF::B_INST; ++i) {
     const int u = wv * CF::B_INST + i;
-    const int q = u / CF::B_IPQ;
     const int k = (u % CF::B_IPQ) * CF::B_RPI + lane / CPR;
     const int c = (lane % CPR) ^ hswz<CF::B_RB>(k);
     int col = t.n0 + 8 * c;
     if (col >= P.N) col = 0;
-    b_src[i] = static_cast<const bf16_t*>(q ? P.B1 : P.B0) + size_t(t.g) * P.b_gstride +
-               size_t(k) * P.N + col;
+    S.bo[i] = uint32_t((size_t(k) * P.N + col) * 2);
   }
 }
 
+template <class CF>
+__device__ __forceinline__ void tile_sources(const GemmProblem& P, const TileId& t, int wv,
+                                             int lane, DmaSrc<CF>& S) {
+  int rows[CF::A_INST];
+#pragma unroll
+  for (int i = 0; i < CF::A_INST; ++i) rows[i] = tile_a_row<CF>(P, t, wv, lane, i);
+  tile_sources_from_rows<CF>(P, t, wv, lane, rows, S);
+}
+
 // Epilogue: lane holds C[m][n..n+3] of every MFMA tile (the MFMA ran with B as its first
-// operand, so each tile comes out transposed). `sbias` holds the block's BNQ bias values
-// (EPI_BIAS / EPI_GELU_BIAS only).
+// operand, so each tile comes out transposed). For EPI_BIAS / EPI_GELU_BIAS the bias
+// comes from `sbias` (the block's BNQ values staged in LDS) or, when `sbias` is null,
+// straight from the problem's bias vector.
 template <class CF, int EPI, bool OF32>
 __device__ __forceinline__ void store_tile(const GemmProblem& P, const TileId& t, int wm, int wn,
                                            int lane, const float* sbias,
@@ -189,11 +221,21 @@ __device__ __forceinline__ void store_tile(const GemmProblem& P, const TileId& t
         for (int r = 0; r < 4; ++r) v[r] = silu(v[r]) * acc[CF::NB - 1][i][j][r];
       }
       if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
-        const float4 bb = *reinterpret_cast<const float4*>(sbias + nl);
-        v[0] += bb.x;
-        v[1] += bb.y;
-        v[2] += bb.z;
-        v[3] += bb.w;
+        if (sbias) {
+          const float4 bb = *reinterpret_cast<const float4*>(sbias + nl);
+          v[0] += bb.x;
+          v[1] += bb.y;
+          v[2] += bb.z;
+          v[3] += bb.w;
+        } else if (P.bias) {
+          // n .. n+3 < N: N is a multiple of 64
+          const uint2 bw = *reinterpret_cast<const uint2*>(
+              static_cast<const bf16_t*>(P.bias) + size_t(t.g) * P.bias_gstride + n);
+          v[0] += bf16_to_f32(bf16_t(bw.x & 0xffff));
+          v[1] += bf16_to_f32(bf16_t(bw.x >> 16));
+          v[2] += bf16_to_f32(bf16_t(bw.y & 0xffff));
+          v[3] += bf16_to_f32(bf16_t(bw.y >> 16));
+        }
       }
       if constexpr (EPI == EPI_GELU_BIAS) {
 #pragma unroll
