@@ -23,6 +23,14 @@ struct Vec;
 template <>
 struct Vec<float> {
   static constexpr int N = 4;
+  typedef float4 Raw;
+  __device__ static Raw load_raw(const void* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static void fma_raw(float g, const Raw& r, float* acc) {
+    acc[0] = fmaf(g, r.x, acc[0]);
+    acc[1] = fmaf(g, r.y, acc[1]);
+    acc[2] = fmaf(g, r.z, acc[2]);
+    acc[3] = fmaf(g, r.w, acc[3]);
+  }
   __device__ static void load(const void* p, float* v) {
     const float4 q = *reinterpret_cast<const float4*>(p);
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
@@ -34,6 +42,16 @@ struct Vec<float> {
 template <>
 struct Vec<bf16_t> {
   static constexpr int N = 8;
+  typedef uint4 Raw;
+  __device__ static Raw load_raw(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void fma_raw(float g, const Raw& r, float* acc) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(g, __uint_as_float(w[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(g, __uint_as_float(w[i] & 0xffff0000u), acc[2 * i + 1]);
+    }
+  }
   __device__ static void load(const void* p, float* v) {
     const uint4 q = *reinterpret_cast<const uint4*>(p);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -49,7 +67,12 @@ struct Vec<bf16_t> {
   }
 };
 
-template <typename T>
+// Expert rows are fetched in batches of KB choices: first the batch's (expert, slot,
+// gate) triples, then all its row loads at once (kept packed until used), then the
+// fused multiply-adds in choice order, so a token costs ceil(k / KB) dependent round
+// trips instead of k. A dropped choice is skipped (not added as zero), so a fully
+// dropped token keeps y == residual bit for bit, signed zeros included.
+template <typename T, int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ residual,
                                                       const T* __restrict__ shared_out,
                                                       const T* __restrict__ expert_out,
@@ -60,13 +83,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
                                                       T* __restrict__ y) {
   constexpr int V = Vec<T>::N;
   const int per_row = D / V;
-  const int rows_per_block = 256 / per_row;  // >= 1 (per_row <= 256 or a multiple)
   int t, col;
   if (per_row >= 256) {
     const int chunks = per_row / 256;
     t = blockIdx.x / chunks;
     col = ((blockIdx.x % chunks) * 256 + threadIdx.x) * V;
   } else {
+    const int rows_per_block = 256 / per_row;
     t = blockIdx.x * rows_per_block + threadIdx.x / per_row;
     col = (threadIdx.x % per_row) * V;
     if (threadIdx.x >= rows_per_block * per_row) return;
@@ -85,15 +108,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] += v[i];
   }
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[size_t(t) * k + j];
-    const int s = slot[size_t(t) * k + j];
-    if (s < 0 || s >= C || e < 0 || e >= E) continue;
-    const float g = gate[size_t(t) * k + j];
-    float v[V];
-    Vec<T>::load(expert_out + (size_t(e) * C + s) * D + col, v);
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    int off[KB];
+    float g[KB];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    for (int b = 0; b < KB; ++b) {
+      off[b] = -1;
+      g[b] = 0.f;
+      const int j = j0 + b;
+      if (j < k) {
+        const int e = idx[size_t(t) * k + j];
+        const int sl = slot[size_t(t) * k + j];
+        if (sl >= 0 && sl < C && e >= 0 && e < E) {
+          off[b] = e * C + sl;
+          g[b] = gate[size_t(t) * k + j];
+        }
+      }
+    }
+    typename Vec<T>::Raw v[KB];
+#pragma unroll
+    for (int b = 0; b < KB; ++b)
+      if (off[b] >= 0) v[b] = Vec<T>::load_raw(expert_out + size_t(off[b]) * D + col);
+#pragma unroll
+    for (int b = 0; b < KB; ++b)
+      if (off[b] >= 0) Vec<T>::fma_raw(g[b], v[b], acc);
   }
   Vec<T>::store(y + size_t(t) * D + col, acc);
 }
@@ -112,12 +150,12 @@ moe_status_t launch_combine(int dt, const void* residual, int64_t ldr, const voi
     blocks = (T + rpb - 1) / rpb;
   }
   if (dt == MOE_BF16) {
-    MOE_LAUNCH("combine", combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s,
+    MOE_LAUNCH("combine", (combine_kernel<bf16_t, 4>), dim3(blocks), dim3(256), 0, s,
                static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(shared_out),
                static_cast<const bf16_t*>(expert_out), idx, slot, gate, T, k, E, C, D,
                ldr, static_cast<bf16_t*>(y));
   } else {
-    MOE_LAUNCH("combine", combine_kernel<float>, dim3(blocks), dim3(256), 0, s,
+    MOE_LAUNCH("combine", (combine_kernel<float, 4>), dim3(blocks), dim3(256), 0, s,
                static_cast<const float*>(residual), static_cast<const float*>(shared_out),
                static_cast<const float*>(expert_out), idx, slot, gate, T, k, E, C, D,
                ldr, static_cast<float*>(y));
