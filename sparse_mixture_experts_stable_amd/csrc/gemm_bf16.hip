@@ -147,13 +147,18 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
   wait_vmcnt<0>();  // the clamped tail loads still target LDS
   __syncthreads();
 
-  // bias of this block's columns, staged once in LDS (free after the main loop)
-  float* sbias = reinterpret_cast<float*>(smem);
+  constexpr bool STAGED = !OF32 && CF::WAVES == 16 && CF::BM == 256;
+  // bias of this block's columns, staged once in LDS (free after the main loop; above
+  // the 64 KiB the staged epilogue uses)
+  float* sbias = reinterpret_cast<float*>(smem + (STAGED ? 65536 : 0));
   if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
     stage_bias<CF>(P, tl, tid, sbias);
     __syncthreads();
   }
-  store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, sbias, acc);
+  if constexpr (STAGED)
+    store_tile_staged<CF, EPI>(P, tl, wm, wn, wv, lane, sbias, smem, acc);
+  else
+    store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, sbias, acc);
 }
 
 // Persistent form of the two-stage kernel: one block per CU walks a strided list of
@@ -334,9 +339,11 @@ moe_status_t launch_epi(GemmBatch& b, const char* name, hipStream_t s) {
 }  // namespace
 
 moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStream_t s) {
-  // Large tiles (256 x 256, 16 waves, two stages, persistent blocks) when every problem
-  // has enough rows per group and the grid still holds at least two tiles per CU; else
-  // 128 x 128 tiles.
+  // Large tiles (256 x 256, 16 waves, two stages) when every problem has enough rows per
+  // group and the grid still holds at least two tiles per CU; else 128 x 128 tiles. The
+  // gated (SwiGLU) GEMM, with long K loops and small output tiles, runs persistent blocks;
+  // the others (K as short as d_hidden, 128 KiB output tiles) run one block per tile with
+  // the LDS-staged epilogue, whose stores overlap the next block's start.
   using Large = TileCfg<256, 256, true, 4, 4, 2>;
   bool large = true;
   long tiles = 0;
@@ -353,7 +360,7 @@ moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStr
     return large ? launch_persistent<TileCfg<256, 256, true, 4, 4, 2>, EPI_SWIGLU, false>(b, name, s)
                  : launch_cfg<TileCfg<128, 128, true, 2, 2, 3>, EPI_SWIGLU, false>(b, name, s);
   }
-  return large ? launch_epi<TileCfg<256, 256, false, 4, 4, 2>, true>(b, name, s)
+  return large ? launch_epi<TileCfg<256, 256, false, 4, 4, 2>, false>(b, name, s)
                : launch_epi<TileCfg<128, 128, false, 2, 2, 3>, false>(b, name, s);
 }
 

@@ -251,6 +251,106 @@ __device__ __forceinline__ void store_tile(const GemmProblem& P, const TileId& t
   }
 }
 
+// The epilogue math for 4 consecutive outputs n..n+3 of row m: SwiGLU product, bias
+// (staged `sbias` or, when null, read from the problem's bias vector), GELU.
+template <class CF, int EPI>
+__device__ __forceinline__ void epi_math(const GemmProblem& P, const TileId& t, int nl, int n,
+                                         const float* sbias, const float (&a)[4],
+                                         const float (&b)[4], float (&v)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = a[r];
+  if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = silu(a[r]) * b[r];
+  }
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
+    if (sbias) {
+      const float4 bb = *reinterpret_cast<const float4*>(sbias + nl);
+      v[0] += bb.x;
+      v[1] += bb.y;
+      v[2] += bb.z;
+      v[3] += bb.w;
+    } else if (P.bias) {
+      // n .. n+3 < N: N is a multiple of 64
+      const uint2 bw = *reinterpret_cast<const uint2*>(
+          static_cast<const bf16_t*>(P.bias) + size_t(t.g) * P.bias_gstride + n);
+      v[0] += bf16_to_f32(bf16_t(bw.x & 0xffff));
+      v[1] += bf16_to_f32(bf16_t(bw.x >> 16));
+      v[2] += bf16_to_f32(bf16_t(bw.y & 0xffff));
+      v[3] += bf16_to_f32(bf16_t(bw.y >> 16));
+    }
+  }
+  if constexpr (EPI == EPI_GELU_BIAS) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
+  }
+}
+
+// bf16 epilogue through LDS: the tile is written to `stage` (64 KiB) in rounds of
+// R = 64 KiB / (2 BNQ) rows, each lane's 8-byte pieces placed with the 16-byte chunk
+// index XORed by (row % 16), then read back as 16 bytes per lane along whole rows and
+// stored, so every store instruction writes complete row segments. All threads of the
+// block take part (it synchronises); `stage` must be free on entry and is free again
+// on return.
+template <class CF, int EPI>
+__device__ __forceinline__ void store_tile_staged(const GemmProblem& P, const TileId& t, int wm,
+                                                  int wn, int wv, int lane, const float* sbias,
+                                                  char* stage,
+                                                  const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  constexpr int RB = CF::BNQ * 2;         // bytes per output row
+  constexpr int CPR = RB / 16;            // 16-byte chunks per row
+  constexpr int R = 65536 / RB;           // rows per round
+  constexpr int ROUNDS = CF::BM / R;
+  constexpr int LPR = 64 / CPR;           // rows per wave instruction when reading back
+  static_assert(CPR >= 16 && R % CF::WROWS == 0 && CF::BM % R == 0 && CF::WAVES == 16,
+                "staged epilogue shape");
+  const int fr = lane & 15, fc = lane >> 4;
+  char* Cb = static_cast<char*>(P.C);
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    __syncthreads();  // stage free (previous round stored, or the K loop done with it)
+    if (wm * CF::WROWS >= rd * R && wm * CF::WROWS < (rd + 1) * R) {
+#pragma unroll
+      for (int i = 0; i < CF::TM; ++i) {
+        const int ml = wm * CF::WROWS + i * 16 + fr - rd * R;
+        const int m = t.m0 + rd * R + ml;
+#pragma unroll
+        for (int j = 0; j < CF::TN; ++j) {
+          const int nl = wn * CF::WCOLS + j * 16 + fc * 4;
+          const int n = t.n0 + nl;
+          float a[4], b[4], v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            a[r] = acc[0][i][j][r];
+            b[r] = acc[CF::NB - 1][i][j][r];
+          }
+          if (m < t.M && n < P.N) {
+            epi_math<CF, EPI>(P, t, nl, n, sbias, a, b, v);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = 0.f;
+          }
+          const int bc = nl * 2;  // byte column
+          *reinterpret_cast<uint2*>(stage + ml * RB + 16 * ((bc >> 4) ^ (ml & 15)) + (bc & 15)) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < R / (16 * LPR); ++q) {
+      const int ml = (wv * (R / 16)) + q * LPR + lane / CPR;  // 16 waves, R/16 rows each
+      const int c = lane % CPR;
+      const int m = t.m0 + rd * R + ml;
+      const int n = t.n0 + 8 * c;
+      if (m < t.M && n < P.N)
+        *reinterpret_cast<uint4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2) =
+            *reinterpret_cast<const uint4*>(stage + ml * RB + 16 * (c ^ (ml & 15)));
+    }
+  }
+  __syncthreads();  // every wave has read the stage back
+}
+
 // Stages the bias of the block's BNQ columns in LDS as fp32 (zeros past N or without a
 // bias). The caller synchronises before the epilogue reads it.
 template <class CF>
