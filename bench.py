@@ -190,7 +190,8 @@ def main():
     flops = gemm1_flops(w, kept)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
-    src_hash = source_hash("gemm_bf16.hip" if w.dtype == "bf16" else "gemm_f32.hip")
+    src_hash = source_hash(*(("gemm_bf16.hip", "gemm_bf16_tile.h") if w.dtype == "bf16"
+                             else ("gemm_f32.hip",)))
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic_record(dom, w.name, src_hash),
