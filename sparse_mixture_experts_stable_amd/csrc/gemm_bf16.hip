@@ -105,7 +105,9 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
 
-  const TileId tl = decode_tile<CF>(batch, logical_block(blockIdx.x, gridDim.x));
+  const int lt = xcd_tile(batch.total, batch.chunk, blockIdx.x & 7, blockIdx.x >> 3);
+  if (lt < 0) return;
+  const TileId tl = decode_tile<CF>(batch, lt);
   if (tl.m0 >= tl.M) return;
   const GemmProblem& P = batch.p[tl.pi];
   const int N = P.N;
@@ -176,17 +178,15 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
   const int nblk = gridDim.x;
   const int x = blockIdx.x & 7, bi = blockIdx.x >> 3;
   const int nb_x = (nblk >> 3) + ((nblk & 7) > x ? 1 : 0);
-  const int q8 = batch.total >> 3, r8 = batch.total & 7;
-  const int lo = x * q8 + (x < r8 ? x : r8);
-  const int hi = lo + q8 + (x < r8 ? 1 : 0);
-
-  int t = lo + bi;
+  // this block takes entries bi, bi + nb_x, ... of XCD x's tile list
+  int j = bi;
   TileId tl;
-  for (; t < hi; t += nb_x) {
-    tl = decode_tile<CF>(batch, t);
+  for (;; j += nb_x) {
+    const int lt = xcd_tile(batch.total, batch.chunk, x, j);
+    if (lt < 0) return;
+    tl = decode_tile<CF>(batch, lt);
     if (tl.m0 < tl.M) break;
   }
-  if (t >= hi) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -208,13 +208,18 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
   while (true) {
     const GemmProblem& P = batch.p[tl.pi];
     // the block's next non-empty tile, and its gathered A rows
-    int t2 = t + nb_x;
+    int j2 = j + nb_x;
     TileId tl2;
-    for (; t2 < hi; t2 += nb_x) {
-      tl2 = decode_tile<CF>(batch, t2);
-      if (tl2.m0 < tl2.M) break;
+    bool more = false;
+    for (;; j2 += nb_x) {
+      const int lt = xcd_tile(batch.total, batch.chunk, x, j2);
+      if (lt < 0) break;
+      tl2 = decode_tile<CF>(batch, lt);
+      if (tl2.m0 < tl2.M) {
+        more = true;
+        break;
+      }
     }
-    const bool more = t2 < hi;
     int rows2[CF::A_INST];
     if (more) {
 #pragma unroll
@@ -249,14 +254,15 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    t = t2;
+    j = j2;
     tl = tl2;
   }
 }
 
 namespace {
-template <class CF, int EPI, bool OF32>
-moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
+// Tile counts of every problem, the chunk dealt to one XCD and the longest XCD list.
+template <class CF>
+void plan_tiles(GemmBatch& b) {
   b.total = 0;
   for (int i = 0; i < b.nprob; ++i) {
     GemmProblem& p = b.p[i];
@@ -265,6 +271,23 @@ moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
     p.tiles = p.groups * p.m_tiles * p.n_tiles;
     b.total += p.tiles;
   }
+  // one group's tiles, but at least 256 chunks overall (32 per XCD) for balance
+  const int group = b.p[0].m_tiles * b.p[0].n_tiles;
+  const int cap = b.total / 256;
+  int ch = group < cap ? group : cap;
+  b.chunk = ch < 1 ? 1 : ch;
+  b.xcd_max = 0;
+  const int nchunks = (b.total + b.chunk - 1) / b.chunk;
+  for (int x = 0; x < 8; ++x) {
+    int n = 0;
+    for (int c = x; c < nchunks; c += 8) n += (c == nchunks - 1) ? b.total - c * b.chunk : b.chunk;
+    if (n > b.xcd_max) b.xcd_max = n;
+  }
+}
+
+template <class CF, int EPI, bool OF32>
+moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
+  plan_tiles<CF>(b);
   if (b.total == 0) return MOE_OK;
   static bool attr_set = false;
   if (!attr_set) {
@@ -273,7 +296,8 @@ moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
       return MOE_ERR_HIP;
     attr_set = true;
   }
-  MOE_LAUNCH(name, (gemm_bf16_kernel<CF, EPI, OF32>), dim3(b.total), dim3(CF::THREADS), CF::LDS, s, b);
+  MOE_LAUNCH(name, (gemm_bf16_kernel<CF, EPI, OF32>), dim3(8 * b.xcd_max), dim3(CF::THREADS), CF::LDS,
+             s, b);
   return MOE_OK;
 }
 
@@ -290,14 +314,7 @@ int cu_count() {
 
 template <class CF, int EPI, bool OF32>
 moe_status_t launch_persistent(GemmBatch& b, const char* name, hipStream_t s) {
-  b.total = 0;
-  for (int i = 0; i < b.nprob; ++i) {
-    GemmProblem& p = b.p[i];
-    p.m_tiles = (p.m_tiles_rows + CF::BM - 1) / CF::BM;
-    p.n_tiles = (p.N + CF::BNQ - 1) / CF::BNQ;
-    p.tiles = p.groups * p.m_tiles * p.n_tiles;
-    b.total += p.tiles;
-  }
+  plan_tiles<CF>(b);
   if (b.total == 0) return MOE_OK;
   static bool attr_set = false;
   if (!attr_set) {

@@ -38,12 +38,15 @@ __device__ __forceinline__ int hswz(int k) {
   return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
 }
 
-// The hardware deals workgroups to the 8 XCDs round-robin; this maps the hardware id to
-// a logical id so that each XCD works through a contiguous range of logical ids.
-__device__ __forceinline__ int logical_block(int bid, int nblk) {
-  const int q = nblk >> 3, r = nblk & 7;
-  const int x = bid & 7, i = bid >> 3;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+// Tiles are dealt to the 8 XCDs in chunks of `chunk` consecutive logical tiles (one
+// group's tiles, which share weight panels): chunk c goes to XCD c % 8. The hardware
+// dispatches workgroup h to XCD h % 8, so the j-th tile of XCD x is taken by a block
+// with h % 8 == x. This keeps the tiles of one expert in one XCD's L2 and spreads
+// busy and empty groups evenly over the XCDs. Returns -1 past the end of XCD x's list.
+__device__ __forceinline__ int xcd_tile(int total, int chunk, int x, int j) {
+  const int c = x + 8 * (j / chunk);
+  const int t = c * chunk + (j % chunk);
+  return t < total ? t : -1;
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).

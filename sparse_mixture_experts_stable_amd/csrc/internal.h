@@ -89,6 +89,8 @@ struct GemmBatch {
   GemmProblem p[2];
   int32_t nprob;
   int32_t total;
+  int32_t chunk;     // tiles per chunk dealt to one XCD (one group's tiles of problem 0)
+  int32_t xcd_max;   // most tiles any XCD receives
 };
 
 constexpr int kBf16BM = 128, kBf16BN = 128, kBf16BK = 64;
