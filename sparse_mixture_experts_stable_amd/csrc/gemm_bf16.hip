@@ -13,8 +13,7 @@
 // next tile.
 //   A (expert rows, k contiguous) is stored [m][k], 128 bytes per row (BK = 64), and
 //   read as one 16-byte fragment per lane. Each lane fetches the source chunk
-//   c ^ f(m), f(m) = (m ^ m/8) % 8, so that the 16 lanes of a fragment read hit distinct
-//   bank groups.
+//   c ^ (m % 8), so that the lanes of a fragment read hit distinct bank groups.
 //   B (weights, n contiguous: [k][n] per expert, as stored) is copied unchanged apart
 //   from a per-row XOR of the 16-byte chunk index (hswz); the k-major fragment
 //   each MFMA needs is assembled with two ds_read_b64_tr_b16 transpose reads. Within a
