@@ -60,6 +60,9 @@ __all__ = [
     "forward",
     "dense_forward",
     "backward_linear",
+    "backward",
+    "gelu_grad",
+    "silu_grad",
     "router_grad",
     "aux_grad",
 ]
@@ -492,3 +495,105 @@ def backward_linear(dy, x, W, logits, idx, gate, kept, slot, count, *,
     if aux_grad_scale:
         dlogits = dlogits + aux_grad_scale * aux_grad(logits, count, k)
     return {"dgate": dgate, "dW": dW, "dx": dx, "dlogits": dlogits}
+
+
+def gelu_grad(z):
+    """d GELU / dz = Phi(z) + z phi(z) for the exact (erf) GELU, with Phi the standard
+    normal CDF and phi its density (the derivative of z Phi(z))."""
+    z = _f64(z)
+    phi = np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+    Phi = 0.5 * (1.0 + np.vectorize(math.erf)(z / math.sqrt(2.0)))
+    return Phi + z * phi
+
+
+def silu_grad(z):
+    """d silu / dz = sigma(z) (1 + z (1 - sigma(z))), the derivative of z sigma(z)."""
+    z = _f64(z)
+    sig = np.where(z >= 0, 1.0 / (1.0 + np.exp(-np.abs(z))), np.exp(-np.abs(z)) / (1.0 + np.exp(-np.abs(z))))
+    return sig * (1.0 + z * (1.0 - sig))
+
+
+def _mlp_backward(kind, w, e, xr, dO):
+    """Backward of one expert applied to the rows xr with output gradient dO (already
+    gated): returns (grads of its parameters, gradient of its input rows). The chain rule
+    through o = act(xr W1 + b1) W2 + b2 (GELU), o = (silu(xr Wg) * (xr Wu)) Wd (SwiGLU),
+    o = xr W (single linear); parameters indexed [e] in the layouts of expert_apply."""
+    if kind == "linear":
+        W = _f64(w["w_in"][e])
+        return {"w_in": xr.T @ dO}, dO @ W.T
+    if kind == "gelu":
+        W1, W2 = _f64(w["w_in"][e]), _f64(w["w_out"][e])
+        z = xr @ W1 + _f64(w["b_in"][e])
+        h = gelu(z)
+        dh = dO @ W2.T
+        dz = dh * gelu_grad(z)
+        g = {"w_in": xr.T @ dz, "b_in": dz.sum(axis=0), "w_out": h.T @ dO, "b_out": dO.sum(axis=0)}
+        return g, dz @ W1.T
+    if kind == "swiglu":
+        Wg, Wu, Wd = _f64(w["w_in"][e]), _f64(w["w_up"][e]), _f64(w["w_out"][e])
+        a = xr @ Wg
+        u = xr @ Wu
+        sa = silu(a)
+        h = sa * u
+        dh = dO @ Wd.T
+        du = dh * sa
+        da = dh * u * silu_grad(a)
+        g = {"w_in": xr.T @ da, "w_up": xr.T @ du, "w_out": h.T @ dO}
+        return g, da @ Wg.T + du @ Wu.T
+    raise ValueError(f"unknown expert kind {kind!r}")
+
+
+def backward(dy, x, kind, weights, logits, idx, gate, kept, count, *, residual=True,
+             aux_grad_scale=0.0, shared=None, w_router=None):
+    """Backward of the whole layer for every expert kind, in float64, with the discrete
+    choices (top-k set, kept mask) held constant (P1 section 2 moe_backward and trap 7,
+    extended through the expert MLPs by the chain rule).
+
+    For a kept assignment a = (t, j) to expert e the expert output o_a is scaled by
+    gate_a, so its output gradient is gate_a dy_t and
+      dgate_a = <dy_t, o_a>,
+    the expert's parameter gradients sum over its kept rows, and its input gradient is
+    added to dx_t. The shared SwiGLU expert (ungated, every token) contributes its own
+    parameter gradients and adds its input gradient to dx. With ``w_router`` (logits =
+    x W_r) the router weights get dW_r = x^T dlogits and dx gets dlogits W_r^T; without
+    it the logits are an independent input and dx has no router term.
+
+    Returns dgate, dlogits, dx, a dict ``dexperts`` of [E, ...] gradients named like the
+    weights (w_in, w_up, w_out, b_in, b_out as the kind has them), ``dshared`` (or None)
+    and ``dw_router`` (or None).
+    """
+    dy = _f64(dy)
+    x = _f64(x)
+    T, k = idx.shape
+    E = np.asarray(weights["w_in"]).shape[0]
+    dgate = np.zeros((T, k))
+    dx = dy.copy() if residual else np.zeros_like(x)
+    names = {"linear": ["w_in"], "gelu": ["w_in", "b_in", "w_out", "b_out"],
+             "swiglu": ["w_in", "w_up", "w_out"]}[kind]
+    dexp = {n: np.zeros(np.asarray(weights[n]).shape) for n in names}
+    for e in range(E):
+        tt, jj = np.nonzero((idx == e) & kept)
+        if tt.size == 0:
+            continue
+        o = expert_apply(kind, weights, e, x[tt])
+        dgate[tt, jj] = np.sum(dy[tt] * o, axis=1)
+        dO = gate[tt, jj][:, None] * dy[tt]
+        g, dxr = _mlp_backward(kind, weights, e, x[tt], dO)
+        for n in names:
+            dexp[n][e] = g[n]
+        np.add.at(dx, tt, dxr)
+    dshared = None
+    if shared is not None:
+        g, dxr = _mlp_backward("swiglu", {n: np.asarray(shared[n])[None] for n in ("w_in", "w_up", "w_out")},
+                               0, x, dy)
+        dshared = g
+        dx = dx + dxr
+    dlogits = router_grad(logits, idx, gate, dgate)
+    if aux_grad_scale:
+        dlogits = dlogits + aux_grad_scale * aux_grad(logits, count, k)
+    dw_router = None
+    if w_router is not None:
+        dw_router = x.T @ dlogits
+        dx = dx + dlogits @ _f64(w_router).T
+    return {"dgate": dgate, "dlogits": dlogits, "dx": dx, "dexperts": dexp,
+            "dshared": dshared, "dw_router": dw_router}

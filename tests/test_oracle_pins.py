@@ -396,6 +396,94 @@ def test_aux_grad_fd():
     assert np.max(np.abs(fd - g)) < 1e-8
 
 
+def test_activation_gradients():
+    """gelu' and silu' against central differences of gelu / silu, and their values at
+    0: both derivatives are 1/2 there (Phi(0) = sigma(0) = 1/2)."""
+    z = np.linspace(-6, 6, 241)
+    h = 1e-6
+    np.testing.assert_allclose(om.gelu_grad(z), (om.gelu(z + h) - om.gelu(z - h)) / (2 * h), atol=1e-8)
+    np.testing.assert_allclose(om.silu_grad(z), (om.silu(z + h) - om.silu(z - h)) / (2 * h), atol=1e-8)
+    assert om.gelu_grad(np.array([0.0]))[0] == 0.5 and om.silu_grad(np.array([0.0]))[0] == 0.5
+
+
+def _mlp_problem(kind, seed, T=7, D=4, E=3, k=2, F=5, with_shared=False, with_router=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, D))
+    w = {"w_in": rng.standard_normal((E, D, D if kind == "linear" else F)) * 0.7}
+    if kind == "gelu":
+        w.update(b_in=rng.standard_normal((E, F)) * 0.5, w_out=rng.standard_normal((E, F, D)) * 0.7,
+                 b_out=rng.standard_normal((E, D)) * 0.5)
+    if kind == "swiglu":
+        w.update(w_up=rng.standard_normal((E, D, F)) * 0.7, w_out=rng.standard_normal((E, F, D)) * 0.7)
+    sh = None
+    if with_shared:
+        sh = {"w_in": rng.standard_normal((D, 3)) * 0.7, "w_up": rng.standard_normal((D, 3)) * 0.7,
+              "w_out": rng.standard_normal((3, D)) * 0.7}
+    wr = rng.standard_normal((D, E)) if with_router else None
+    s = None if with_router else np.stack([rng.permutation(E) * 0.37 + rng.random() for _ in range(T)])
+    dy = rng.standard_normal((T, D))
+    return x, w, sh, wr, s, dy, k
+
+
+@pytest.mark.parametrize("kind,shared,router,aux,residual", [
+    ("gelu", False, False, 0.0, True), ("swiglu", False, False, 1.0, True),
+    ("swiglu", True, False, 0.0, False), ("gelu", False, True, 1.0, True),
+    ("swiglu", True, True, 0.5, True), ("linear", False, True, 0.0, True)])
+def test_mlp_backward_finite_differences(kind, shared, router, aux, residual):
+    """The whole-layer backward through GELU / SwiGLU experts, the shared expert and the
+    router weights equals central differences of <dy, y> + aux_scale * aux with the top-k
+    set and the kept mask constant (Sparse MoE Layer in NumPy, section 3 method)."""
+    x, w, sh, wr, s, dy, k = _mlp_problem(kind, seed=11 + len(kind), with_shared=shared, with_router=router)
+    C = 3
+    f = om.forward(x, k, kind, w, logits=s, w_router=wr, C=C, residual=residual, shared=sh)
+    g = om.backward(dy, x, kind, w, f["logits"], f["idx"], f["gate"], f["kept"], f["count"],
+                    residual=residual, aux_grad_scale=aux, shared=sh, w_router=wr)
+    assert (~f["kept"]).any()   # some assignments dropped
+    h = 1e-6
+
+    def loss(x_, w_, sh_, wr_, s_):
+        ff = om.forward(x_, k, kind, w_, logits=s_, w_router=wr_, C=C, residual=residual, shared=sh_)
+        assert np.array_equal(ff["idx"], f["idx"]) and np.array_equal(ff["kept"], f["kept"])
+        return float(np.sum(dy * ff["y"]) + aux * ff["aux"])
+
+    def fd(get, put):
+        base = get()
+        out = np.zeros_like(base)
+        for i in np.ndindex(base.shape):
+            a = base.copy(); a[i] += h; lp = put(a)
+            a = base.copy(); a[i] -= h; lm = put(a)
+            out[i] = (lp - lm) / (2 * h)
+        return out
+
+    np.testing.assert_allclose(fd(lambda: x, lambda a: loss(a, w, sh, wr, s)), g["dx"], atol=2e-6)
+    for n, arr in w.items():
+        def put(a, n=n):
+            w2 = dict(w); w2[n] = a
+            return loss(x, w2, sh, wr, s)
+        np.testing.assert_allclose(fd(lambda arr=arr: arr, put), g["dexperts"][n], atol=2e-6)
+    if sh is not None:
+        for n, arr in sh.items():
+            def put(a, n=n):
+                s2 = dict(sh); s2[n] = a
+                return loss(x, w, s2, wr, s)
+            np.testing.assert_allclose(fd(lambda arr=arr: arr, put), g["dshared"][n][0] if g["dshared"][n].ndim == 3 else g["dshared"][n], atol=2e-6)
+    if wr is not None:
+        np.testing.assert_allclose(fd(lambda: wr, lambda a: loss(x, w, sh, a, s)), g["dw_router"], atol=2e-6)
+    else:
+        np.testing.assert_allclose(fd(lambda: s, lambda a: loss(x, w, sh, wr, a)), g["dlogits"], atol=2e-6)
+
+
+def test_general_backward_matches_linear_backward():
+    """For single-linear experts the general backward reduces to backward_linear."""
+    x, W, s, dy, k, C = _fd_problem(C=2)
+    f = om.forward(x, k, "linear", {"w_in": W}, logits=s, C=C)
+    a = om.backward_linear(dy, x, W, s, f["idx"], f["gate"], f["kept"], f["slot"], f["count"], aux_grad_scale=0.3)
+    b = om.backward(dy, x, "linear", {"w_in": W}, s, f["idx"], f["gate"], f["kept"], f["count"], aux_grad_scale=0.3)
+    for n_a, n_b in (("dx", "dx"), ("dgate", "dgate"), ("dlogits", "dlogits")):
+        np.testing.assert_allclose(a[n_a], b[n_b], atol=1e-12)
+    np.testing.assert_allclose(a["dW"], b["dexperts"]["w_in"], atol=1e-12)
+
+
 # ---------------------------------------------------------------------------------
 # Invariants and edge cases
 # ---------------------------------------------------------------------------------
