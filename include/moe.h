@@ -22,8 +22,9 @@
  *                                                        router page, y equation)
  *   Switch aux loss E sum_e f_e P_e before any drop, f_e = count_e / (T k),
  *   P_e = mean_t p[t, e]                               ("Sparse MoE Layer in NumPy", trap 6)
- *   backward: dgate, dW, dx and the router-logit gradient through the quotient
- *   rule and the softmax Jacobian, drops held constant ("Sparse MoE Layer in NumPy",
+ *   backward: dgate, dx, the router-logit gradient through the quotient rule and
+ *   the softmax Jacobian, expert (GELU, SwiGLU, linear), shared-expert and router weight
+ *   gradients, discrete choices held constant         ("Sparse MoE Layer in NumPy",
  *                                                        trap 7 and section 2)
  *
  * Conventions shared by every entry point
@@ -61,7 +62,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,  /* bad size, NULL required pointer, k outside [1, E]     */
-  MOE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (shape limits, MLP backward) */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (shape limits, bf16 backward) */
   MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the matching *_workspace_size    */
   MOE_ERR_HIP = 4           /* a HIP launch or call failed                            */
 } moe_status_t;
@@ -218,20 +219,37 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
                          void* stream);
 
 /*
- * Backward for single-linear experts ("Sparse MoE Layer in NumPy", section 2
- * moe_backward and trap 7), discrete choices held constant:
- *   dgate[a]  = kept_a <dy_t, expert_out[e_a, slot_a]>
- *   dW[e]     = sum over kept a -> e of gate_a x_t^T dy_t  ([E, D, D]; 0 if unused)
- *   dx[t]     = r dy_t + sum over kept a in t of gate_a dy_t W_e^T
+ * Backward of the whole layer ("Sparse MoE Layer in NumPy", section 2 moe_backward and
+ * trap 7, for single-linear experts; extended by the chain rule through the GELU and
+ * SwiGLU expert MLPs of "Module 7" / llm-atlas "Mixture of Experts", Expert), with the
+ * discrete choices (top-k set, kept mask) held constant. For a kept assignment
+ * a = (t, j) -> e with expert output o_a (ungated, from the forward) the expert's output
+ * gradient is dO_a = gate_a dy_t, and
+ *   dgate[a]  = kept_a <dy_t, o_a>
  *   dlogits   = p * (dp - <p, dp>), dp[t, idx_tj] = (dgate_tj - sum_r g_tr dgate_tr) / S_t,
  *               S_t = sum_r p[t, idx_tr]; plus aux_grad_scale * (E/T) p (f - <p, f>),
  *               f_e = count_e / (T k)
- * Other expert kinds return MOE_ERR_UNSUPPORTED.
+ *   expert parameter gradients = sums over the expert's kept rows of the MLP's chain
+ *               rule with input x_t and output gradient dO_a (LINEAR: dW = x^T dO;
+ *               GELU_MLP: Z = x W_in + b_in, dZ = (dO W_out^T) gelu'(Z), dW_in = x^T dZ,
+ *               db_in = sum dZ, dW_out = gelu(Z)^T dO, db_out = sum dO; SWIGLU:
+ *               A = x W_in, U = x W_up, dH = dO W_out^T, dA = dH U silu'(A),
+ *               dU = dH silu(A), dW_in = x^T dA, dW_up = x^T dU, dW_out = (silu(A) U)^T dO);
+ *               experts without kept rows get zeros
+ *   dx[t]     = r dy_t + sum over kept a in t of the expert's input gradient
+ *               (LINEAR: dO W^T; GELU_MLP: dZ W_in^T; SWIGLU: dA W_in^T + dU W_up^T)
+ *               + the shared expert's input gradient (ungated: its dO is dy)
+ *               + dlogits W_r^T when w_router is given (logits = x W_r); without
+ *               w_router the logits are an independent input and dx has no router term
+ *   dw_router = x^T dlogits
+ * The pre-activations are recomputed from x (nothing but expert_out is kept from the
+ * forward). fp32 experts only (bf16 returns MOE_ERR_UNSUPPORTED). All reductions run in
+ * a fixed order: results are bitwise reproducible.
  */
 typedef struct {
   const void* dy;           /* device [T, ld]  */
   const void* x;            /* device [T, ld]  */
-  int64_t ld;
+  int64_t ld;               /* must equal d_model */
   int32_t T;
   const float* logits;      /* device [T, E]   */
   moe_experts_t experts;
@@ -248,9 +266,22 @@ typedef struct {
   const void* expert_out;   /* [E, C, D] from the forward */
   /* outputs (device) */
   void* dx;                 /* [T, D]    */
-  void* dW;                 /* [E, D, D] */
+  void* dW;                 /* [E, D, F] gradient of experts.w_in ([E, D, D] for LINEAR) */
   float* dgate;             /* [T, k]    */
   float* dlogits;           /* [T, E]    */
+  /* MLP experts: further outputs, required when the kind has the weight */
+  void* dW_up;              /* [E, D, F] SWIGLU                                        */
+  void* dW_out;             /* [E, F, D] GELU_MLP, SWIGLU                              */
+  void* db_in;              /* [E, F]    GELU_MLP with b_in                            */
+  void* db_out;             /* [E, D]    GELU_MLP with b_out                           */
+  /* shared SwiGLU expert as in the forward, or shared.w_in == NULL */
+  moe_experts_t shared;
+  void* dshared_w_in;       /* [D, Fs] */
+  void* dshared_w_up;       /* [D, Fs] */
+  void* dshared_w_out;      /* [Fs, D] */
+  /* router weights, or NULL (see dx above); E must be a multiple of 4 */
+  const void* w_router;     /* [D, E] */
+  void* dw_router;          /* [D, E] */
 } moe_backward_args_t;
 
 size_t moe_backward_workspace_size(const moe_backward_args_t* a);

@@ -60,7 +60,10 @@ class BackwardArgs(ctypes.Structure):
                 ("experts", Experts), ("k", i32), ("capacity", i32), ("use_residual", i32),
                 ("aux_grad_scale", f32), ("topk_idx", vp), ("topk_gate", vp),
                 ("expert_count", vp), ("slot", vp), ("slot_assign", vp), ("expert_used", vp),
-                ("expert_out", vp), ("dx", vp), ("dW", vp), ("dgate", vp), ("dlogits", vp)]
+                ("expert_out", vp), ("dx", vp), ("dW", vp), ("dgate", vp), ("dlogits", vp),
+                ("dW_up", vp), ("dW_out", vp), ("db_in", vp), ("db_out", vp),
+                ("shared", Experts), ("dshared_w_in", vp), ("dshared_w_up", vp),
+                ("dshared_w_out", vp), ("w_router", vp), ("dw_router", vp)]
 
 
 _lib = None

@@ -80,7 +80,6 @@ moe_status_t check_experts(const moe_experts_t* ex) {
   if (ex->kind == MOE_EXPERT_GELU_MLP && !ex->w_out) return MOE_ERR_INVALID_ARG;
   const int q = ex->dtype == MOE_BF16 ? 64 : 16;
   if (ex->d_model % q || ex->d_hidden % q) return MOE_ERR_UNSUPPORTED;
-  if (ex->dtype == MOE_F32 && ex->kind == MOE_EXPERT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -164,6 +163,7 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
     a.g_const = T;
     a.m_tiles = (rows + kF32BM - 1) / kF32BM;
     a.B = static_cast<const float*>(ex->w_in);
+    a.B1 = static_cast<const float*>(ex->kind == MOE_EXPERT_SWIGLU ? ex->w_up : nullptr);
     a.N = pl.two_stage ? F : D;
     a.ldb = a.N;
     a.b_gstride = int64_t(D) * a.N;
@@ -171,7 +171,9 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
     a.bias_gstride = F;
     a.K = D;
     a.groups = E;
-    a.epi = ex->kind == MOE_EXPERT_GELU_MLP ? EPI_GELU_BIAS : EPI_STORE;
+    a.epi = ex->kind == MOE_EXPERT_GELU_MLP ? EPI_GELU_BIAS
+          : ex->kind == MOE_EXPERT_SWIGLU  ? EPI_SWIGLU
+                                           : EPI_STORE;
     a.C = static_cast<float*>(pl.two_stage ? hidden : out);
     a.ldc = a.N;
     a.c_gstride = int64_t(rows) * a.N;
@@ -188,7 +190,7 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
       b.B = static_cast<const float*>(ex->w_out);
       b.ldb = D;
       b.b_gstride = int64_t(F) * D;
-      b.bias = static_cast<const float*>(ex->b_out);
+      b.bias = static_cast<const float*>(ex->kind == MOE_EXPERT_GELU_MLP ? ex->b_out : nullptr);
       b.bias_gstride = D;
       b.K = F;
       b.N = D;
@@ -231,7 +233,9 @@ moe_status_t run_experts(const ExpertPlan* plans, const moe_experts_t* const* ex
   }
   for (int i = 0; i < n; ++i) {
     ExpertPlan p = plans[i];
-    moe_status_t st = launch_gemm_f32(p.f1, A_ROWS, B_KN, "expert_gemm1_f32", s);
+    moe_status_t st = launch_gemm_f32(p.f1, A_ROWS, B_KN,
+                                      p.f1.epi == EPI_SWIGLU ? "expert_gemm1_swiglu_f32"
+                                                             : "expert_gemm1_f32", s);
     if (st != MOE_OK) return st;
     if (p.two_stage) {
       st = launch_gemm_f32(p.f2, A_ROWS, B_KN, "expert_gemm2_f32", s);
@@ -592,86 +596,405 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
 }
 
 // ---- backward -----------------------------------------------------------------------
-size_t moe_backward_workspace_size(const moe_backward_args_t* a) {
-  if (!a || a->T < 1 || a->experts.num_experts < 1) return 0;
-  return align_up(size_t(a->experts.num_experts) * a->capacity * a->experts.d_model * 4, 256) + 256;
+namespace {
+// One expert set seen by the backward: routed (rows of expert e are its kept
+// assignments, slot_assign order, output gradient gate * dy) or dense (the shared expert:
+// all T rows, output gradient dy).
+struct BwdSet {
+  const moe_experts_t* ex;
+  int rows;                  // C (routed) or T (dense)
+  const int32_t* row_map;    // slot_assign or NULL
+  int row_div;               // k or 1
+  const int32_t* count;      // expert_used or NULL (then every group has `cnt_const` rows)
+  int cnt_const;
+  const float* gate;         // topk_gate or NULL
+  float *dw_in, *dw_up, *dw_out, *db_in, *db_out;
+  float *h, *g, *u;          // [E, rows, F] scratch: H, dH -> dZ / dA, dU
+  float* dxr;                // [E, rows, D] input gradient of each row
+};
+
+struct BwdWs {
+  float* dxe;
+  float *h, *g, *u;
+  float *sh_h, *sh_g, *sh_u, *sh_dx;
+  float* part;
+  size_t bytes;
+};
+
+BwdWs carve_bwd(const moe_backward_args_t* a, void* ws) {
+  BwdWs w{};
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t floats) -> float* {
+    float* p = base ? reinterpret_cast<float*>(base + off) : nullptr;
+    off = align_up(off + floats * 4, 256);
+    return p;
+  };
+  const moe_experts_t& ex = a->experts;
+  const size_t E = ex.num_experts, C = a->capacity, D = ex.d_model, F = ex.d_hidden;
+  const size_t T = a->T;
+  w.dxe = take(E * C * D);
+  if (ex.kind != MOE_EXPERT_LINEAR) {
+    w.h = take(E * C * F);
+    w.g = take(E * C * F);
+    if (ex.kind == MOE_EXPERT_SWIGLU) w.u = take(E * C * F);
+  }
+  if (a->shared.w_in) {
+    const size_t Fs = a->shared.d_hidden;
+    w.sh_h = take(T * Fs);
+    w.sh_g = take(T * Fs);
+    w.sh_u = take(T * Fs);
+    w.sh_dx = take(T * D);
+  }
+  if (ex.kind == MOE_EXPERT_GELU_MLP) {
+    const size_t pf = colsum_part_floats(int(E), int(C), int(F));
+    const size_t pd = colsum_part_floats(int(E), int(C), int(D));
+    w.part = take(pf > pd ? pf : pd);
+  }
+  w.bytes = off + 256;
+  return w;
 }
 
-moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+// Backward through the MLPs of one expert set: parameter gradients and set.dxr.
+moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int64_t ld,
+                          float* part, hipStream_t s) {
+  const moe_experts_t* ex = S.ex;
+  const int E = ex->num_experts, D = ex->d_model, F = ex->d_hidden, R = S.rows;
+  const bool swiglu = ex->kind == MOE_EXPERT_SWIGLU;
+  const int mt_rows = (R + kF32BM - 1) / kF32BM;
+  moe_status_t st;
+
+  // dH = dO W_out^T, ungated here (the gate is applied in the recompute epilogue)
+  GemmF32Problem p{};
+  p.A = dy;
+  p.lda = ld;
+  p.row_map = S.row_map;
+  p.row_map_ld = R;
+  p.row_div = S.row_div;
+  p.g_count = S.count;
+  p.g_const = S.cnt_const;
+  p.m_tiles = mt_rows;
+  p.B = static_cast<const float*>(ex->w_out);
+  p.ldb = D;
+  p.b_gstride = int64_t(F) * D;
+  p.K = D;
+  p.N = F;
+  p.groups = E;
+  p.epi = EPI_STORE;
+  p.C = S.g;
+  p.ldc = F;
+  p.c_gstride = int64_t(R) * F;
+  st = launch_gemm_f32(p, A_ROWS, B_NK, "bwd_dh_gemm", s);
+  if (st != MOE_OK) return st;
+
+  // recompute the pre-activation; epilogue writes H and dZ (GELU) or H, dA, dU (SwiGLU)
+  p = GemmF32Problem{};
+  p.A = x;
+  p.lda = ld;
+  p.row_map = S.row_map;
+  p.row_map_ld = R;
+  p.row_div = S.row_div;
+  p.g_count = S.count;
+  p.g_const = S.cnt_const;
+  p.m_tiles = mt_rows;
+  p.B = static_cast<const float*>(ex->w_in);
+  p.B1 = swiglu ? static_cast<const float*>(ex->w_up) : nullptr;
+  p.ldb = F;
+  p.b_gstride = int64_t(D) * F;
+  p.gate = S.gate;
+  p.bias = swiglu ? nullptr : static_cast<const float*>(ex->b_in);
+  p.bias_gstride = F;
+  p.K = D;
+  p.N = F;
+  p.groups = E;
+  p.epi = swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD;
+  p.C = S.h;
+  p.G = S.g;
+  p.C2 = S.u;
+  p.ldc = F;
+  p.c_gstride = int64_t(R) * F;
+  st = launch_gemm_f32(p, A_ROWS, B_KN, swiglu ? "bwd_swiglu_recompute" : "bwd_gelu_recompute", s);
+  if (st != MOE_OK) return st;
+
+  // dW_out = H^T dO (K = the group's rows; dO rows gathered and gated)
+  p = GemmF32Problem{};
+  p.A = S.h;
+  p.lda = F;
+  p.a_gstride = int64_t(R) * F;
+  p.row_map_ld = R;
+  p.row_div = S.row_div;
+  p.g_count = S.count;
+  p.g_const = S.cnt_const;
+  p.M = F;
+  p.m_tiles = (F + kF32BM - 1) / kF32BM;
+  p.B = dy;
+  p.ldb = ld;
+  p.b_row_map = S.row_map;
+  p.gate = S.gate;
+  p.N = D;
+  p.groups = E;
+  p.epi = EPI_STORE;
+  p.C = S.dw_out;
+  p.ldc = D;
+  p.c_gstride = int64_t(F) * D;
+  st = launch_gemm_f32(p, A_KROWS, B_KROWS, "bwd_dw_out_gemm", s);
+  if (st != MOE_OK) return st;
+
+  // dW_in = X^T dZ (dA); dW_up = X^T dU
+  for (int w = 0; w < (swiglu ? 2 : 1); ++w) {
+    p = GemmF32Problem{};
+    p.A = x;
+    p.lda = ld;
+    p.row_map = S.row_map;
+    p.row_map_ld = R;
+    p.row_div = S.row_div;
+    p.g_count = S.count;
+    p.g_const = S.cnt_const;
+    p.M = D;
+    p.m_tiles = (D + kF32BM - 1) / kF32BM;
+    p.B = w == 0 ? S.g : S.u;
+    p.ldb = F;
+    p.b_gstride = int64_t(R) * F;
+    p.N = F;
+    p.groups = E;
+    p.epi = EPI_STORE;
+    p.C = w == 0 ? S.dw_in : S.dw_up;
+    p.ldc = F;
+    p.c_gstride = int64_t(D) * F;
+    st = launch_gemm_f32(p, A_KROWS, B_KROWS, w == 0 ? "bwd_dw_in_gemm" : "bwd_dw_up_gemm", s);
+    if (st != MOE_OK) return st;
+  }
+
+  if (!swiglu) {
+    if (S.db_out) {
+      st = launch_colsum(dy, ld, 0, S.row_map, R, S.row_div, S.gate, S.count, S.cnt_const, R, E,
+                         D, part, S.db_out, D, s);
+      if (st != MOE_OK) return st;
+    }
+    if (S.db_in) {
+      st = launch_colsum(S.g, F, int64_t(R) * F, nullptr, R, 1, nullptr, S.count, S.cnt_const, R,
+                         E, F, part, S.db_in, F, s);
+      if (st != MOE_OK) return st;
+    }
+  }
+
+  // input gradient of each row: dZ W_in^T (+ dU W_up^T)
+  for (int w = 0; w < (swiglu ? 2 : 1); ++w) {
+    p = GemmF32Problem{};
+    p.A = w == 0 ? S.g : S.u;
+    p.lda = F;
+    p.a_gstride = int64_t(R) * F;
+    p.row_div = 1;
+    p.g_count = S.count;
+    p.g_const = S.cnt_const;
+    p.m_tiles = mt_rows;
+    p.B = static_cast<const float*>(w == 0 ? ex->w_in : ex->w_up);
+    p.ldb = F;
+    p.b_gstride = int64_t(D) * F;
+    p.K = F;
+    p.N = D;
+    p.groups = E;
+    p.epi = w == 0 ? EPI_STORE : EPI_ACCUM;
+    p.C = S.dxr;
+    p.ldc = D;
+    p.c_gstride = int64_t(R) * D;
+    st = launch_gemm_f32(p, A_ROWS, B_NK, "bwd_dx_gemm", s);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status_t check_backward(const moe_backward_args_t* a) {
   if (!a) return MOE_ERR_INVALID_ARG;
   moe_status_t st = check_experts(&a->experts);
   if (st != MOE_OK) return st;
-  if (a->experts.kind != MOE_EXPERT_LINEAR || a->experts.dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
-  const int T = a->T, E = a->experts.num_experts, k = a->k, C = a->capacity;
-  const int D = a->experts.d_model;
+  const moe_experts_t& ex = a->experts;
+  if (ex.dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  const int T = a->T, E = ex.num_experts, k = a->k, C = a->capacity;
+  const int D = ex.d_model;
   if (!route_shape_ok(T, E, k) || C < 0) return MOE_ERR_INVALID_ARG;
-  if (k > 256) return MOE_ERR_UNSUPPORTED;
+  if (k > 256 || int64_t(T) * k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (!a->dy || !a->x || a->ld < D || !a->logits || !a->topk_idx || !a->topk_gate ||
       !a->expert_count || !a->slot || !a->expert_used || !a->dx || !a->dW || !a->dgate ||
       !a->dlogits || (C > 0 && (!a->slot_assign || !a->expert_out)))
     return MOE_ERR_INVALID_ARG;
+  if (ex.kind != MOE_EXPERT_LINEAR && !a->dW_out) return MOE_ERR_INVALID_ARG;
+  if (ex.kind == MOE_EXPERT_SWIGLU && !a->dW_up) return MOE_ERR_INVALID_ARG;
+  if (ex.kind == MOE_EXPERT_GELU_MLP && ((ex.b_in && !a->db_in) || (ex.b_out && !a->db_out)))
+    return MOE_ERR_INVALID_ARG;
   if (a->ld != D) return MOE_ERR_UNSUPPORTED;
   const int per_row = D / 4;
   if ((per_row > 256 && per_row % 256) || (per_row < 256 && 256 % per_row)) return MOE_ERR_UNSUPPORTED;
+  if (a->shared.w_in) {
+    st = check_experts(&a->shared);
+    if (st != MOE_OK) return st;
+    if (a->shared.kind != MOE_EXPERT_SWIGLU || a->shared.num_experts != 1 ||
+        a->shared.dtype != MOE_F32 || a->shared.d_model != D)
+      return MOE_ERR_UNSUPPORTED;
+    if (!a->dshared_w_in || !a->dshared_w_up || !a->dshared_w_out) return MOE_ERR_INVALID_ARG;
+  }
+  if (a->w_router) {
+    if (!a->dw_router) return MOE_ERR_INVALID_ARG;
+    if (E % 4) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+}  // namespace
+
+size_t moe_backward_workspace_size(const moe_backward_args_t* a) {
+  if (!a || a->T < 1 || a->experts.num_experts < 1 || a->capacity < 0) return 0;
+  return carve_bwd(a, nullptr).bytes;
+}
+
+moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_backward(a);
+  if (st != MOE_OK) return st;
   if (!ws || ws_bytes < moe_backward_workspace_size(a)) return MOE_ERR_WORKSPACE;
   hipStream_t s = S(stream);
+  const moe_experts_t& ex = a->experts;
+  const int T = a->T, E = ex.num_experts, k = a->k, C = a->capacity;
+  const int D = ex.d_model;
   const float* dy = static_cast<const float*>(a->dy);
   const float* x = static_cast<const float*>(a->x);
-  float* dxe = static_cast<float*>(ws);
+  BwdWs w = carve_bwd(a, ws);
 
   st = launch_dgate_router_bwd(dy, static_cast<const float*>(a->expert_out), a->logits,
                                a->topk_idx, a->topk_gate, a->slot, a->expert_count, T, k, E, C,
                                D, a->aux_grad_scale, a->dgate, a->dlogits, s);
   if (st != MOE_OK) return st;
 
-  // dX_e = dY_e W_e^T on the slot rows, then the gate-weighted scatter-sum (+ dy)
-  GemmF32Problem px{};
-  px.A = dy;
-  px.lda = a->ld;
-  px.row_map = a->slot_assign;
-  px.row_map_ld = C;
-  px.row_div = k;
-  px.g_count = a->expert_used;
-  px.m_tiles = (C + kF32BM - 1) / kF32BM;
-  px.B = static_cast<const float*>(a->experts.w_in);
-  px.ldb = D;
-  px.b_gstride = int64_t(D) * D;
-  px.K = D;
-  px.N = D;
-  px.groups = E;
-  px.epi = EPI_STORE;
-  px.C = dxe;
-  px.ldc = D;
-  px.c_gstride = int64_t(C) * D;
-  if (C > 0) {
-    st = launch_gemm_f32(px, A_ROWS, B_NK, "bwd_dx_gemm", s);
+  // with C == 0 no row is kept: every weight gradient is zero (K = 0 products)
+  const int32_t* used = C > 0 ? a->expert_used : nullptr;
+  if (ex.kind == MOE_EXPERT_LINEAR) {
+    // dX_e = dY_e W_e^T on the slot rows (ungated; the combine below applies the gate)
+    GemmF32Problem px{};
+    px.A = dy;
+    px.lda = a->ld;
+    px.row_map = a->slot_assign;
+    px.row_map_ld = C;
+    px.row_div = k;
+    px.g_count = a->expert_used;
+    px.m_tiles = (C + kF32BM - 1) / kF32BM;
+    px.B = static_cast<const float*>(ex.w_in);
+    px.ldb = D;
+    px.b_gstride = int64_t(D) * D;
+    px.K = D;
+    px.N = D;
+    px.groups = E;
+    px.epi = EPI_STORE;
+    px.C = w.dxe;
+    px.ldc = D;
+    px.c_gstride = int64_t(C) * D;
+    if (C > 0) {
+      st = launch_gemm_f32(px, A_ROWS, B_NK, "bwd_dx_gemm", s);
+      if (st != MOE_OK) return st;
+    }
+    // dW_e = X_e^T (gate * dY_e), K = used_e gathered rows
+    GemmF32Problem pw{};
+    pw.A = x;
+    pw.lda = a->ld;
+    pw.row_map = a->slot_assign;
+    pw.row_map_ld = C;
+    pw.row_div = k;
+    pw.g_count = used;
+    pw.g_const = 0;
+    pw.M = D;
+    pw.m_tiles = (D + kF32BM - 1) / kF32BM;
+    pw.B = dy;
+    pw.ldb = a->ld;
+    pw.b_row_map = a->slot_assign;
+    pw.gate = a->topk_gate;
+    pw.N = D;
+    pw.groups = E;
+    pw.epi = EPI_STORE;
+    pw.C = static_cast<float*>(a->dW);
+    pw.ldc = D;
+    pw.c_gstride = int64_t(D) * D;
+    st = launch_gemm_f32(pw, A_KROWS, B_KROWS, "bwd_dw_gemm", s);
+    if (st != MOE_OK) return st;
+  } else {
+    BwdSet r{};
+    r.ex = &ex;
+    r.rows = C;
+    r.row_map = a->slot_assign;
+    r.row_div = k;
+    r.count = used;
+    r.cnt_const = 0;
+    r.gate = a->topk_gate;
+    r.dw_in = static_cast<float*>(a->dW);
+    r.dw_up = static_cast<float*>(a->dW_up);
+    r.dw_out = static_cast<float*>(a->dW_out);
+    r.db_in = ex.b_in ? static_cast<float*>(a->db_in) : nullptr;
+    r.db_out = ex.b_out ? static_cast<float*>(a->db_out) : nullptr;
+    r.h = w.h;
+    r.g = w.g;
+    r.u = w.u;
+    r.dxr = w.dxe;
+    st = mlp_backward(r, x, dy, a->ld, w.part, s);
     if (st != MOE_OK) return st;
   }
-  st = launch_combine(MOE_F32, a->use_residual ? a->dy : nullptr, a->ld, nullptr, dxe, a->topk_idx,
-                      a->slot, a->topk_gate, T, k, E, C, D, a->dx, s);
+
+  if (a->shared.w_in) {
+    BwdSet sh{};
+    sh.ex = &a->shared;
+    sh.rows = T;
+    sh.row_div = 1;
+    sh.cnt_const = T;
+    sh.dw_in = static_cast<float*>(a->dshared_w_in);
+    sh.dw_up = static_cast<float*>(a->dshared_w_up);
+    sh.dw_out = static_cast<float*>(a->dshared_w_out);
+    sh.h = w.sh_h;
+    sh.g = w.sh_g;
+    sh.u = w.sh_u;
+    sh.dxr = w.sh_dx;
+    st = mlp_backward(sh, x, dy, a->ld, nullptr, s);
+    if (st != MOE_OK) return st;
+  }
+
+  // dx = r dy + shared input gradient + sum over kept choices of the routed rows'
+  // input gradients (gated here for single-linear experts, already gated for MLPs)
+  st = launch_combine(MOE_F32, a->use_residual ? a->dy : nullptr, a->ld, w.sh_dx, w.dxe,
+                      a->topk_idx, a->slot, ex.kind == MOE_EXPERT_LINEAR ? a->topk_gate : nullptr,
+                      T, k, E, C, D, a->dx, s);
   if (st != MOE_OK) return st;
 
-  // dW_e = X_e^T (gate * dY_e), K = used_e gathered rows; unused experts get 0
-  GemmF32Problem pw{};
-  pw.A = x;
-  pw.lda = a->ld;
-  pw.row_map = a->slot_assign;
-  pw.row_map_ld = C;
-  pw.row_div = k;
-  pw.g_count = C > 0 ? a->expert_used : nullptr;
-  pw.g_const = 0;
-  pw.M = D;
-  pw.m_tiles = (D + kF32BM - 1) / kF32BM;
-  pw.B = dy;
-  pw.ldb = a->ld;
-  pw.gate = a->topk_gate;
-  pw.N = D;
-  pw.groups = E;
-  pw.epi = EPI_STORE;
-  pw.C = static_cast<float*>(a->dW);
-  pw.ldc = D;
-  pw.c_gstride = int64_t(D) * D;
-  return launch_gemm_f32(pw, A_KROWS, B_KROWS_GATE, "bwd_dw_gemm", s);
+  if (a->w_router) {
+    // dW_r = x^T dlogits
+    GemmF32Problem pr{};
+    pr.A = x;
+    pr.lda = a->ld;
+    pr.row_div = 1;
+    pr.g_const = T;
+    pr.M = D;
+    pr.m_tiles = (D + kF32BM - 1) / kF32BM;
+    pr.B = a->dlogits;
+    pr.ldb = E;
+    pr.N = E;
+    pr.groups = 1;
+    pr.epi = EPI_STORE;
+    pr.C = static_cast<float*>(a->dw_router);
+    pr.ldc = E;
+    st = launch_gemm_f32(pr, A_KROWS, B_KROWS, "bwd_dw_router_gemm", s);
+    if (st != MOE_OK) return st;
+    // dx += dlogits W_r^T
+    GemmF32Problem pd{};
+    pd.A = a->dlogits;
+    pd.lda = E;
+    pd.row_div = 1;
+    pd.g_const = T;
+    pd.m_tiles = (T + kF32BM - 1) / kF32BM;
+    pd.B = static_cast<const float*>(a->w_router);
+    pd.ldb = E;
+    pd.K = E;
+    pd.N = D;
+    pd.groups = 1;
+    pd.epi = EPI_ACCUM;
+    pd.C = static_cast<float*>(a->dx);
+    pd.ldc = D;
+    st = launch_gemm_f32(pd, A_ROWS, B_NK, "bwd_dx_router_gemm", s);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
 }
 
 // ---- errors and profiling -------------------------------------------------------------

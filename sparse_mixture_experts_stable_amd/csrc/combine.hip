@@ -70,7 +70,8 @@ struct Vec<bf16_t> {
 // Expert rows are fetched in batches of KB choices: first the batch's (expert, slot,
 // gate) triples, then all its row loads at once (kept packed until used), then the
 // fused multiply-adds in choice order, so a token costs ceil(k / KB) dependent round
-// trips instead of k. A dropped choice is skipped (not added as zero), so a fully
+// trips instead of k. gate == NULL weights every choice by 1 (exact: fma(1, v, acc) is
+// acc + v), for expert rows that already carry their gate. A dropped choice is skipped (not added as zero), so a fully
 // dropped token keeps y == residual bit for bit, signed zeros included.
 template <typename T, int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ residual,
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
         const int sl = slot[size_t(t) * k + j];
         if (sl >= 0 && sl < C && e >= 0 && e < E) {
           off[b] = e * C + sl;
-          g[b] = gate[size_t(t) * k + j];
+          g[b] = gate ? gate[size_t(t) * k + j] : 1.0f;
         }
       }
     }
@@ -292,6 +293,81 @@ moe_status_t launch_dgate_router_bwd(const float* dy, const float* expert_out,
     MOE_DG(16);
   }
 #undef MOE_DG
+  return MOE_OK;
+}
+
+// ---- bias gradients: grouped column sums -------------------------------------------
+// Stage 1: block (x, c, g) sums rows [c*kColRows, (c+1)*kColRows) of group g for 1024
+// columns (4 per thread), in row order, into part[g][c][n]. Stage 2 adds the chunks in
+// chunk order. The result depends only on the shapes, never on scheduling.
+namespace {
+constexpr int kColRows = 64;
+inline int col_chunks(int max_rows) { return (max_rows + kColRows - 1) / kColRows; }
+}  // namespace
+
+size_t colsum_part_floats(int groups, int max_rows, int N) {
+  return size_t(groups) * (col_chunks(max_rows) > 0 ? col_chunks(max_rows) : 1) * N;
+}
+
+__global__ __launch_bounds__(256) void colsum_part_kernel(
+    const float* __restrict__ src, int64_t ld, int64_t gstride, const int32_t* __restrict__ map,
+    int32_t map_ld, int32_t div, const float* __restrict__ gate,
+    const int32_t* __restrict__ g_count, int32_t g_const, int N, float* __restrict__ part) {
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int c = blockIdx.y, g = blockIdx.z, nch = gridDim.y;
+  if (n >= N) return;
+  const int Mg = g_count ? g_count[g] : g_const;
+  const int r0 = c * kColRows;
+  const int r1 = min(r0 + kColRows, Mg);
+  const float* base = src + size_t(g) * gstride + n;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int r = r0; r < r1; ++r) {
+    int row = r;
+    float sc = 1.f;
+    if (map) {
+      const int a = map[size_t(g) * map_ld + r];
+      row = a / div;
+      if (gate) sc = gate[a];
+    }
+    const float4 v = *reinterpret_cast<const float4*>(base + size_t(row) * ld);
+    acc.x += sc * v.x;
+    acc.y += sc * v.y;
+    acc.z += sc * v.z;
+    acc.w += sc * v.w;
+  }
+  *reinterpret_cast<float4*>(part + (size_t(g) * nch + c) * N + n) = acc;
+}
+
+__global__ __launch_bounds__(256) void colsum_finish_kernel(const float* __restrict__ part,
+                                                            int nch, int N,
+                                                            float* __restrict__ out,
+                                                            int64_t out_gstride) {
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int g = blockIdx.y;
+  if (n >= N) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = 0; c < nch; ++c) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (size_t(g) * nch + c) * N + n);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *reinterpret_cast<float4*>(out + size_t(g) * out_gstride + n) = acc;
+}
+
+moe_status_t launch_colsum(const float* src, int64_t ld, int64_t gstride, const int32_t* map,
+                           int32_t map_ld, int32_t div, const float* gate,
+                           const int32_t* g_count, int32_t g_const, int max_rows, int groups,
+                           int N, float* part, float* out, int64_t out_gstride, hipStream_t s) {
+  if (groups < 1 || N < 1) return MOE_OK;
+  if (N % 4 || max_rows < 0) return MOE_ERR_UNSUPPORTED;
+  const int nch = col_chunks(max_rows) > 0 ? col_chunks(max_rows) : 1;
+  const int xb = (N + 1023) / 1024;
+  MOE_LAUNCH("colsum_part", colsum_part_kernel, dim3(xb, nch, groups), dim3(256), 0, s, src, ld,
+             gstride, map, map_ld, div, gate, g_count, g_const, N, part);
+  MOE_LAUNCH("colsum_finish", colsum_finish_kernel, dim3(xb, groups), dim3(256), 0, s, part, nch,
+             N, out, out_gstride);
   return MOE_OK;
 }
 

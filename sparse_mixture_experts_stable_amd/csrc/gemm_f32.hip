@@ -1,16 +1,21 @@
 // Grouped fp32 GEMM on gfx950 fp32 MFMA (v_mfma_f32_16x16x4_f32). gfx950 has no
 // reduced-precision xf32 path, so fp32 experts run on true fp32 matrix cores.
 //
-// Used for the fp32 expert MLPs ("Sparse MoE Layer in NumPy", section 2 forward
-// einsum for single-linear experts; llm-atlas "Mixture of Experts", Expert) and for the
-// two GEMMs of the single-linear backward (same page, section 2 moe_backward):
-//   dX_e = (dY rows of e) W_e^T               A_ROWS x B_NK  (rows gathered by slot)
-//   dW_e = X_e^T (gate * dY_e)                A_KROWS x B_KROWS_GATE (K gathered)
+// Forward: the fp32 expert MLPs ("Sparse MoE Layer in NumPy", section 2 forward einsum
+// for single-linear experts; llm-atlas "Mixture of Experts", Expert; "Module 7",
+// swiglu_expert), the gated kernel computing silu(X Wg) * (X Wu) in one pass.
+// Backward (the chain rule through those experts; single-linear form in "Sparse MoE
+// Layer in NumPy", section 2 moe_backward), with dO = gate * dY on the kept rows:
+//   dH   = dO W2^T                           A_ROWS x B_NK
+//   Z    = X W1 + b1, then H, dZ             A_ROWS x B_KN, EPI_GELU_BWD / EPI_SWIGLU_BWD
+//   dW2  = H^T dO,  dW1 = X^T dZ             A_KROWS x B_KROWS (K = the expert's rows)
+//   dX_e = dZ W1^T                           A_ROWS x B_NK (+ EPI_ACCUM for SwiGLU's 2nd)
 //
 // Tile 64 x 64 x 16 per 256-thread block; four waves in 2 x 2, each 32 x 32 (2 x 2
 // MFMA tiles). LDS holds A as [k][m] and B as [k][n] (m / n contiguous, rows padded to
 // 68 floats), so every fragment read is one conflict-free 4-byte read per lane; operands
-// that arrive k-contiguous from HBM are transposed on the LDS store.
+// that arrive k-contiguous from HBM are transposed on the LDS store. Loads are guarded
+// per float4 against M, N and K, so those sizes need only be multiples of 4.
 
 #include "internal.h"
 
@@ -25,12 +30,24 @@ __device__ __forceinline__ int logical_block_f32(int bid, int nblk) {
   const int x = bid & 7, i = bid >> 3;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
+
+__device__ __forceinline__ float4 ld4(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+
+// d/dz of z * Phi(z): Phi(z) + z phi(z), with the standard normal cdf / pdf.
+__device__ __forceinline__ float gelu_erf_grad(float z) {
+  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752440f));
+  const float pdf = 0.39894228040143267794f * __expf(-0.5f * z * z);
+  return cdf + z * pdf;
+}
 }  // namespace
 
-template <int AM, int BMODE>
+template <int AM, int BMODE, bool GATED>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
+  constexpr int NB = GATED ? 2 : 1;
   __shared__ float As[2][BK][LDP];
-  __shared__ float Bs[2][BK][LDP];
+  __shared__ float Bs[NB][2][BK][LDP];
   const int lid = logical_block_f32(blockIdx.x, gridDim.x);
   const int per_group = P.m_tiles * P.n_tiles;
   const int g = lid / per_group;
@@ -59,47 +76,55 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   const int tr_row = tid >> 2, tr_kq = tid & 3;
   const int dr_k = tid >> 4, dr_q = tid & 15;
 
+  const float* a_base = P.A + size_t(g) * P.a_gstride;
   const float* a_row_ptr = nullptr;  // A_ROWS
   if (AM == A_ROWS) {
     int r = m0 + tr_row;
     if (r >= M) r = m0;
-    int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + r] / P.row_div : r;
-    a_row_ptr = P.A + size_t(g) * P.a_gstride + size_t(src) * P.lda + tr_kq * 4;
+    const int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + r] / P.row_div : r;
+    a_row_ptr = a_base + size_t(src) * P.lda + tr_kq * 4;
   }
   const float* b_base = P.B + size_t(g) * P.b_gstride;
+  const float* b1_base = GATED ? P.B1 + size_t(g) * P.b_gstride : nullptr;
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  float4 ra, rb;
+  float4 ra, rb[NB];
   auto load = [&](int kt) {
     const int k0 = kt * BK;
     if (AM == A_ROWS) {
-      ra = *reinterpret_cast<const float4*>(a_row_ptr + k0);
+      ra = (k0 + tr_kq * 4 < Kg) ? ld4(a_row_ptr + k0) : zero;
     } else {
       const int kk = k0 + dr_k;
+      ra = zero;
       if (kk < Kg && m0 + dr_q * 4 < M) {
-        const int a = P.row_map[size_t(g) * P.row_map_ld + kk];
-        ra = *reinterpret_cast<const float4*>(P.A + size_t(a / P.row_div) * P.lda + m0 + dr_q * 4);
-      } else {
-        ra = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + kk] / P.row_div : kk;
+        ra = ld4(a_base + size_t(src) * P.lda + m0 + dr_q * 4);
       }
     }
     if (BMODE == B_KN) {
       const int kk = k0 + dr_k;
       const int n = n0 + dr_q * 4;
-      rb = (n < N) ? *reinterpret_cast<const float4*>(b_base + size_t(kk) * P.ldb + n)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool ok = kk < Kg && n < N;
+      rb[0] = ok ? ld4(b_base + size_t(kk) * P.ldb + n) : zero;
+      if constexpr (GATED) rb[1] = ok ? ld4(b1_base + size_t(kk) * P.ldb + n) : zero;
     } else if (BMODE == B_NK) {
       const int n = n0 + tr_row;
-      rb = (n < N) ? *reinterpret_cast<const float4*>(b_base + size_t(n) * P.ldb + k0 + tr_kq * 4)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int kq = k0 + tr_kq * 4;
+      rb[0] = (n < N && kq < Kg) ? ld4(b_base + size_t(n) * P.ldb + kq) : zero;
     } else {
       const int kk = k0 + dr_k;
-      if (kk < Kg && n0 + dr_q * 4 < N) {
-        const int a = P.row_map[size_t(g) * P.row_map_ld + kk];
-        const float gs = P.gate[a];
-        float4 v = *reinterpret_cast<const float4*>(P.B + size_t(a / P.row_div) * P.ldb + n0 + dr_q * 4);
-        rb = make_float4(v.x * gs, v.y * gs, v.z * gs, v.w * gs);
-      } else {
-        rb = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int n = n0 + dr_q * 4;
+      rb[0] = zero;
+      if (kk < Kg && n < N) {
+        int src = kk;
+        float sc = 1.f;
+        if (P.b_row_map) {
+          const int a = P.b_row_map[size_t(g) * P.row_map_ld + kk];
+          src = a / P.row_div;
+          if (P.gate) sc = P.gate[a];
+        }
+        const float4 v = ld4(b_base + size_t(src) * P.ldb + n);
+        rb[0] = make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc);
       }
     }
   };
@@ -113,20 +138,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
       *reinterpret_cast<float4*>(&As[buf][dr_k][dr_q * 4]) = ra;
     }
     if (BMODE == B_NK) {
-      Bs[buf][tr_kq * 4 + 0][tr_row] = rb.x;
-      Bs[buf][tr_kq * 4 + 1][tr_row] = rb.y;
-      Bs[buf][tr_kq * 4 + 2][tr_row] = rb.z;
-      Bs[buf][tr_kq * 4 + 3][tr_row] = rb.w;
+      Bs[0][buf][tr_kq * 4 + 0][tr_row] = rb[0].x;
+      Bs[0][buf][tr_kq * 4 + 1][tr_row] = rb[0].y;
+      Bs[0][buf][tr_kq * 4 + 2][tr_row] = rb[0].z;
+      Bs[0][buf][tr_kq * 4 + 3][tr_row] = rb[0].w;
     } else {
-      *reinterpret_cast<float4*>(&Bs[buf][dr_k][dr_q * 4]) = rb;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) *reinterpret_cast<float4*>(&Bs[b][buf][dr_k][dr_q * 4]) = rb[b];
     }
   };
 
-  f32x4 acc[2][2];
+  f32x4 acc[NB][2][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (Kg + BK - 1) / BK;
   const int fr = lane & 15, fc = lane >> 4;
@@ -139,16 +167,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
       if (kt + 1 < nk) load(kt + 1);
 #pragma unroll
       for (int ks = 0; ks < BK / 4; ++ks) {
-        float af[2], bf[2];
+        float af[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) af[i] = As[cur][ks * 4 + fc][wm * 32 + i * 16 + fr];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = Bs[cur][ks * 4 + fc][wn * 32 + j * 16 + fr];
+        for (int b = 0; b < NB; ++b) {
+          float bf[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+          for (int j = 0; j < 2; ++j) bf[j] = Bs[b][cur][ks * 4 + fc][wn * 32 + j * 16 + fr];
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j], af[i], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[b][i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j], af[i], acc[b][i][j], 0, 0, 0);
+        }
       }
       if (kt + 1 < nk) store(cur ^ 1);
       __syncthreads();
@@ -156,30 +188,71 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   }
 
   // ---- epilogue: lane holds C[m][n..n+3] ----
+  const int epi = P.epi;
+  const bool bwd = epi == EPI_GELU_BWD || epi == EPI_SWIGLU_BWD;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = m0 + wm * 32 + i * 16 + fr;
     if (m >= M) continue;
+    float rg = 1.f;
+    if (bwd && AM == A_ROWS && P.gate && P.row_map)
+      rg = P.gate[P.row_map[size_t(g) * P.row_map_ld + m]];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn * 32 + j * 16 + fc * 4;
       if (n >= N) continue;
-      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      if (P.epi == EPI_BIAS || P.epi == EPI_GELU_BIAS) {
-        if (P.bias) {
-          const float4 bb = *reinterpret_cast<const float4*>(P.bias + size_t(g) * P.bias_gstride + n);
-          v[0] += bb.x;
-          v[1] += bb.y;
-          v[2] += bb.z;
-          v[3] += bb.w;
-        }
-        if (P.epi == EPI_GELU_BIAS) {
+      const size_t off = size_t(g) * P.c_gstride + size_t(m) * P.ldc + n;
+      float v[4] = {acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]};
+      if ((epi == EPI_BIAS || epi == EPI_GELU_BIAS || epi == EPI_GELU_BWD) && P.bias) {
+        const float4 bb = ld4(P.bias + size_t(g) * P.bias_gstride + n);
+        v[0] += bb.x;
+        v[1] += bb.y;
+        v[2] += bb.z;
+        v[3] += bb.w;
+      }
+      if (epi == EPI_GELU_BIAS) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
+        for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
+      } else if (epi == EPI_ACCUM) {
+        const float4 c = ld4(P.C + off);
+        v[0] += c.x;
+        v[1] += c.y;
+        v[2] += c.z;
+        v[3] += c.w;
+      } else if (epi == EPI_GELU_BWD) {
+        const float4 gi = ld4(P.G + off);
+        const float dh[4] = {gi.x * rg, gi.y * rg, gi.z * rg, gi.w * rg};
+        float dz[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dz[r] = dh[r] * gelu_erf_grad(v[r]);
+          v[r] = gelu_erf(v[r]);
+        }
+        *reinterpret_cast<float4*>(P.G + off) = make_float4(dz[0], dz[1], dz[2], dz[3]);
+      }
+      if constexpr (GATED) {
+        const float u[4] = {acc[1][i][j][0], acc[1][i][j][1], acc[1][i][j][2], acc[1][i][j][3]};
+        if (epi == EPI_SWIGLU) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = silu(v[r]) * u[r];
+        } else if (epi == EPI_SWIGLU_BWD) {
+          const float4 gi = ld4(P.G + off);
+          const float dh[4] = {gi.x * rg, gi.y * rg, gi.z * rg, gi.w * rg};
+          float da[4], du[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = v[r];
+            const float sg = 1.0f / (1.0f + __expf(-a));
+            const float sa = a * sg;
+            du[r] = dh[r] * sa;
+            da[r] = dh[r] * u[r] * (sg * (1.0f + a * (1.0f - sg)));
+            v[r] = sa * u[r];
+          }
+          *reinterpret_cast<float4*>(P.G + off) = make_float4(da[0], da[1], da[2], da[3]);
+          *reinterpret_cast<float4*>(P.C2 + off) = make_float4(du[0], du[1], du[2], du[3]);
         }
       }
-      float* dst = P.C + size_t(g) * P.c_gstride + size_t(m) * P.ldc + n;
-      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(P.C + off) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -189,13 +262,22 @@ moe_status_t launch_gemm_f32(GemmF32Problem& p, int amode, int bmode, const char
   p.n_tiles = (p.N + BN - 1) / BN;
   p.tiles = p.groups * p.m_tiles * p.n_tiles;
   if (p.tiles == 0) return MOE_OK;
+  const bool gated = p.epi == EPI_SWIGLU || p.epi == EPI_SWIGLU_BWD;
+  if (gated && (!p.B1 || amode != A_ROWS || bmode != B_KN)) return MOE_ERR_UNSUPPORTED;
+  if ((p.epi == EPI_GELU_BWD || p.epi == EPI_SWIGLU_BWD) && (!p.G || amode != A_ROWS))
+    return MOE_ERR_UNSUPPORTED;
+  if (p.epi == EPI_SWIGLU_BWD && !p.C2) return MOE_ERR_UNSUPPORTED;
   const dim3 grid(p.tiles), block(256);
   if (amode == A_ROWS && bmode == B_KN) {
-    MOE_LAUNCH(name, (gemm_f32_kernel<A_ROWS, B_KN>), grid, block, 0, s, p);
+    if (gated) {
+      MOE_LAUNCH(name, (gemm_f32_kernel<A_ROWS, B_KN, true>), grid, block, 0, s, p);
+    } else {
+      MOE_LAUNCH(name, (gemm_f32_kernel<A_ROWS, B_KN, false>), grid, block, 0, s, p);
+    }
   } else if (amode == A_ROWS && bmode == B_NK) {
-    MOE_LAUNCH(name, (gemm_f32_kernel<A_ROWS, B_NK>), grid, block, 0, s, p);
-  } else if (amode == A_KROWS && bmode == B_KROWS_GATE) {
-    MOE_LAUNCH(name, (gemm_f32_kernel<A_KROWS, B_KROWS_GATE>), grid, block, 0, s, p);
+    MOE_LAUNCH(name, (gemm_f32_kernel<A_ROWS, B_NK, false>), grid, block, 0, s, p);
+  } else if (amode == A_KROWS && bmode == B_KROWS) {
+    MOE_LAUNCH(name, (gemm_f32_kernel<A_KROWS, B_KROWS, false>), grid, block, 0, s, p);
   } else {
     return MOE_ERR_UNSUPPORTED;
   }

@@ -97,28 +97,49 @@ constexpr int kBf16BM = 128, kBf16BN = 128, kBf16BK = 64;
 moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStream_t s);
 
 // fp32 grouped GEMM (fp32 MFMA). Modes select the operand layouts.
+// Every operand row is addressed as X + g*x_gstride + src*ldx, where src is the row's
+// index or, with a row map, map[g*row_map_ld + i] / row_div (callers pass gstride 0
+// with a map: the map then indexes one shared tensor).
+//   A_ROWS : row r < M_g of C[g] is the product of A row r (mapped by row_map); K = P.K.
+//   A_KROWS: the K index walks rows of A (an A^T operand), mapped by row_map;
+//            M = P.M columns of A; K_g = g_count ? g_count[g] : g_const.
+//   B_KN   : B[g] = B + g*b_gstride, [K][N] (N contiguous); B1 likewise (gated kernels).
+//   B_NK   : B[g] = B + g*b_gstride, [N][K] (K contiguous): C = A B^T.
+//   B_KROWS: the K index walks rows of B, mapped by b_row_map; a mapped row a is scaled
+//            by gate[a] when gate != NULL.
 enum AMode : int32_t { A_ROWS = 0, A_KROWS = 1 };
-enum BMode : int32_t { B_KN = 0, B_NK = 1, B_KROWS_GATE = 2 };
+enum BMode : int32_t { B_KN = 0, B_NK = 1, B_KROWS = 2 };
+// Epilogues of the fp32 kernel beyond those of the bf16 one. With an A_ROWS row map,
+// rgate(m) = gate[row_map[g*row_map_ld + m]], else 1.
+//   EPI_ACCUM      : C += acc
+//   EPI_GELU_BWD   : z = acc + bias; dh = G * rgate(m); C = gelu(z); G = dh * gelu'(z)
+//   EPI_SWIGLU_BWD : a = acc (B), u = acc1 (B1); dh = G * rgate(m); C = silu(a) u;
+//                    G = dh u silu'(a); C2 = dh silu(a)
+constexpr int32_t EPI_ACCUM = 5, EPI_GELU_BWD = 6, EPI_SWIGLU_BWD = 7;
 struct GemmF32Problem {
   const float* A;
   int64_t lda;
   int64_t a_gstride;
-  const int32_t* row_map;   // A_ROWS: maps M rows; A_KROWS: maps K rows
+  const int32_t* row_map;   // A_ROWS: maps M rows; A_KROWS: maps K rows; NULL: identity
   int32_t row_map_ld;
   int32_t row_div;
-  const int32_t* g_count;   // A_ROWS: M per group; A_KROWS: K per group
+  const int32_t* g_count;   // A_ROWS: M per group; A_KROWS: K per group (NULL: g_const)
   int32_t g_const;
   int32_t M;                // A_KROWS: fixed M
   int32_t m_tiles;
   const float* B;
+  const float* B1;          // gated kernels: second weight (the SwiGLU up projection)
   int64_t ldb;
   int64_t b_gstride;
-  const float* gate;        // B_KROWS_GATE: scale of each gathered row (by assignment)
+  const int32_t* b_row_map; // B_KROWS: maps K rows (shares row_map_ld / row_div); NULL: identity
+  const float* gate;        // B_KROWS: row scales by assignment; *_BWD: rgate source
   const float* bias;
   int64_t bias_gstride;
   float* C;
   int64_t ldc;
   int64_t c_gstride;
+  float* G;                 // *_BWD: incoming dH, overwritten (layout of C)
+  float* C2;                // EPI_SWIGLU_BWD: dU (layout of C)
   int32_t K;                // A_ROWS: inner size
   int32_t N;
   int32_t n_tiles;
@@ -129,6 +150,14 @@ struct GemmF32Problem {
 constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 moe_status_t launch_gemm_f32(GemmF32Problem& p, int amode, int bmode, const char* name,
                              hipStream_t s);
+// Column sums per group: out[g*out_gstride + n] = sum over rows r < M_g (in row order,
+// fixed chunking) of scale(r) * row(r)[n], rows addressed like B_KROWS (map / identity,
+// gate). Deterministic. part: >= colsum_part_floats(groups, max_rows, N) floats.
+size_t colsum_part_floats(int groups, int max_rows, int N);
+moe_status_t launch_colsum(const float* src, int64_t ld, int64_t gstride, const int32_t* map,
+                           int32_t map_ld, int32_t div, const float* gate,
+                           const int32_t* g_count, int32_t g_const, int max_rows, int groups,
+                           int N, float* part, float* out, int64_t out_gstride, hipStream_t s);
 
 // Plain SIMT router GEMM for shapes the MFMA kernels do not tile (any E).
 moe_status_t launch_router_simt(const void* x, int dtype, int64_t ldx, const void* w, int T,

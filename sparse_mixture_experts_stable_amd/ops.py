@@ -243,21 +243,53 @@ class ForwardCall:
             L.check("moe_forward", st)
 
 
-def backward(dy, x, experts, fwd, *, k, use_residual=True, aux_grad_scale=0.0):
-    """moe_backward for single-linear fp32 experts. ``fwd`` is the dict returned by
-    forward(). Returns dx, dW, dgate, dlogits."""
+def backward(dy, x, experts, fwd, *, k, use_residual=True, aux_grad_scale=0.0, shared=None,
+             w_router=None):
+    """moe_backward for fp32 experts of any kind. ``fwd`` is the dict returned by
+    forward(). ``shared``: the shared SwiGLU expert of the forward; ``w_router``: the
+    router weights, for dw_router and the router term of dx.
+
+    Returns dx, dgate, dlogits, ``dexperts`` (gradients named like the expert weights),
+    ``dW`` (= dexperts["w_in"]), ``dshared`` (or None) and ``dw_router`` (or None)."""
     dy = _c(dy)
     x = _c(x)
     T, D = x.shape
     dev = x.device
     es, keep = _experts_struct(experts)
-    E = es.num_experts
+    E, F = es.num_experts, es.d_hidden
     C = int(fwd["capacity"])
+    kind = experts["kind"]
+
+    def new(*shape):
+        return torch.empty(*shape, dtype=x.dtype, device=dev)
+
+    dexp = {"w_in": new(E, D, F)}
+    if kind == "swiglu":
+        dexp["w_up"] = new(E, D, F)
+    if kind != "linear":
+        dexp["w_out"] = new(E, F, D)
+    if kind == "gelu":
+        if experts.get("b_in") is not None:
+            dexp["b_in"] = new(E, F)
+        if experts.get("b_out") is not None:
+            dexp["b_out"] = new(E, D)
+    shs, shkeep = (_experts_struct(shared) if shared is not None else (L.Experts(), {}))
+    dsh = None
+    if shared is not None:
+        Fs = shs.d_hidden
+        dsh = {"w_in": new(D, Fs), "w_up": new(D, Fs), "w_out": new(Fs, D)}
+    dwr = None
+    if w_router is not None:
+        w_router = _c(w_router)
+        dwr = torch.empty(D, E, dtype=torch.float32, device=dev)
     out = {
-        "dx": torch.empty(T, D, dtype=x.dtype, device=dev),
-        "dW": torch.empty(E, D, D, dtype=x.dtype, device=dev),
+        "dx": new(T, D),
         "dgate": torch.empty(T, k, dtype=torch.float32, device=dev),
         "dlogits": torch.empty(T, E, dtype=torch.float32, device=dev),
+        "dexperts": dexp,
+        "dW": dexp["w_in"],
+        "dshared": dsh,
+        "dw_router": dwr,
     }
     a = L.BackwardArgs(
         dy=_p(dy), x=_p(x), ld=x.stride(0), T=T, logits=_p(fwd["logits"]), experts=es, k=k,
@@ -265,11 +297,18 @@ def backward(dy, x, experts, fwd, *, k, use_residual=True, aux_grad_scale=0.0):
         topk_idx=_p(fwd["topk_idx"]), topk_gate=_p(fwd["topk_gate"]),
         expert_count=_p(fwd["expert_count"]), slot=_p(fwd["slot"]),
         slot_assign=_p(fwd["slot_assign"]), expert_used=_p(fwd["expert_used"]),
-        expert_out=_p(fwd["expert_out"]), dx=_p(out["dx"]), dW=_p(out["dW"]),
-        dgate=_p(out["dgate"]), dlogits=_p(out["dlogits"]))
+        expert_out=_p(fwd["expert_out"]), dx=_p(out["dx"]), dW=_p(dexp["w_in"]),
+        dgate=_p(out["dgate"]), dlogits=_p(out["dlogits"]),
+        dW_up=_p(dexp.get("w_up")), dW_out=_p(dexp.get("w_out")), db_in=_p(dexp.get("b_in")),
+        db_out=_p(dexp.get("b_out")), shared=shs,
+        dshared_w_in=_p(dsh["w_in"]) if dsh else None,
+        dshared_w_up=_p(dsh["w_up"]) if dsh else None,
+        dshared_w_out=_p(dsh["w_out"]) if dsh else None,
+        w_router=_p(w_router), dw_router=_p(dwr))
     ws = _ws(L.lib().moe_backward_workspace_size(ctypes.byref(a)), dev)
     st = L.lib().moe_backward(ctypes.byref(a), _p(ws), ws.numel(), _stream())
     L.check("moe_backward", st)
+    del keep, shkeep
     return out
 
 

@@ -90,6 +90,35 @@ def test_dispatch_and_forward_reject_bad_arguments():
                     d_hidden=128, w_in=p, w_up=p, w_out=p)
     b = L.BackwardArgs(dy=p, x=p, ld=128, T=8, logits=p, experts=bex, k=2, capacity=4)
     assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    # fp32 MLP backward: every gradient the kind has must be given
+    fex = L.Experts(kind=L.MOE_EXPERT_SWIGLU, dtype=L.MOE_F32, num_experts=4, d_model=128,
+                    d_hidden=64, w_in=p, w_up=p, w_out=p)
+    full = dict(dy=p, x=p, ld=128, T=8, logits=p, experts=fex, k=2, capacity=4, topk_idx=p,
+                topk_gate=p, expert_count=p, slot=p, slot_assign=p, expert_used=p,
+                expert_out=p, dx=p, dW=p, dgate=p, dlogits=p, dW_up=p, dW_out=p)
+    for drop in ("dW_up", "dW_out", "dW"):
+        kw = dict(full)
+        kw[drop] = None
+        b = L.BackwardArgs(**kw)
+        assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_INVALID_ARG, drop
+    b = L.BackwardArgs(**full)
+    assert lib.moe_backward(ctypes.byref(b), p, 1, None) == L.MOE_ERR_WORKSPACE
+    # router weights need their gradient, and E a multiple of 4
+    b = L.BackwardArgs(**dict(full, w_router=p))
+    assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    fex3 = L.Experts(kind=L.MOE_EXPERT_SWIGLU, dtype=L.MOE_F32, num_experts=3, d_model=128,
+                     d_hidden=64, w_in=p, w_up=p, w_out=p)
+    b = L.BackwardArgs(**dict(full, experts=fex3, w_router=p, dw_router=p))
+    assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    # GELU biases need their gradients; the shared expert needs all three
+    gex = L.Experts(kind=L.MOE_EXPERT_GELU_MLP, dtype=L.MOE_F32, num_experts=4, d_model=128,
+                    d_hidden=64, w_in=p, w_out=p, b_in=p, b_out=p)
+    b = L.BackwardArgs(**dict(full, experts=gex, db_in=p))
+    assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    sh = L.Experts(kind=L.MOE_EXPERT_SWIGLU, dtype=L.MOE_F32, num_experts=1, d_model=128,
+                   d_hidden=64, w_in=p, w_up=p, w_out=p)
+    b = L.BackwardArgs(**dict(full, shared=sh, dshared_w_in=p, dshared_w_up=p))
+    assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
 
 
 def test_workspace_sizes_positive():

@@ -59,6 +59,18 @@ def test_forward_small_zipf_pmf_variant():
     H.check_outputs(w, inp, h, r, d)
 
 
+@pytest.mark.parametrize("kind", ["swiglu", "gelu"])
+def test_forward_small_f32_mlp(kind):
+    """fp32 SwiGLU (gated fp32 kernel) and GELU experts with a shared fp32 expert."""
+    base = SMALL[3] if kind == "swiglu" else SMALL[2].scaled(shared_F=128)
+    w = base.scaled(dtype="f32")
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp)
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.check_outputs(w, inp, h, r, d)
+
+
 def _sample_tokens(T, d, n=24, seed=0):
     rng = np.random.default_rng(seed)
     toks = set(range(8)) | set(range(T - 8, T)) | set(rng.integers(0, T, n).tolist())
@@ -113,6 +125,70 @@ def test_backward_full_size():
 
 def test_backward_no_residual_tiny_capacity():
     _backward_case(SMALL[5].scaled(residual=False, cf=0.25), 0.5)
+
+
+# ---------------------------------------------------------------------------------
+# general backward: GELU / SwiGLU experts, shared expert, router weights (fp32)
+# ---------------------------------------------------------------------------------
+
+def _backward_general(w, aux_scale, router):
+    ops = _ops()
+    inp = make_inputs(w)
+    out, g = H.run_forward(w, inp)
+    grads = ops.backward(g["dy"], g["x"], H.experts_dict(w, g), out, k=w.k,
+                         use_residual=w.residual, aux_grad_scale=aux_scale,
+                         shared=H.shared_dict(w, g),
+                         w_router=g["w_router"] if router else None)
+    torch.cuda.synchronize()
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    want = om.backward(to_numpy_f32(inp["dy"]), to_numpy_f32(inp["x"]), w.kind,
+                       H.oracle_weights(inp), h["logits"].astype(np.float64), r["idx"], r["gate"],
+                       d["kept"], r["count"], residual=w.residual, aux_grad_scale=aux_scale,
+                       shared=H.oracle_shared(inp),
+                       w_router=to_numpy_f32(inp["w_router"]) if router else None)
+    for key in ("dgate", "dlogits", "dx"):
+        H.assert_close(grads[key].cpu().numpy(), want[key], 1e-4, key)
+    assert set(grads["dexperts"]) == set(want["dexperts"])
+    for key, v in grads["dexperts"].items():
+        H.assert_close(v.cpu().numpy(), want["dexperts"][key], 1e-4, "d" + key)
+    if w.shared_F:
+        for key, v in grads["dshared"].items():
+            H.assert_close(v.cpu().numpy(), want["dshared"][key], 1e-4, "dshared_" + key)
+    if router:
+        H.assert_close(grads["dw_router"].cpu().numpy(), want["dw_router"], 1e-4, "dw_router")
+    # experts with no kept row get exactly zero gradients
+    unused = np.flatnonzero(d["used"] == 0)
+    for v in grads["dexperts"].values():
+        assert not v[torch.as_tensor(unused, device=v.device)].any()
+
+
+BWD = {
+    "gelu_bias": WORKLOADS[1].scaled(backward=True),
+    "gelu_wide": WORKLOADS[2].scaled(T=1024, D=256, F=512, dtype="f32", backward=True),
+    "swiglu_shared": WORKLOADS[3].scaled(T=1024, D=256, E=32, F=128, shared_F=128, dtype="f32",
+                                         backward=True),
+    "linear": SMALL[5],
+}
+
+
+@pytest.mark.parametrize("case,aux_scale,router", [
+    ("gelu_bias", 0.0, False), ("gelu_bias", 1.0, True), ("gelu_wide", 0.0, True),
+    ("swiglu_shared", 0.0, False), ("swiglu_shared", 0.5, True), ("linear", 0.0, True),
+])
+def test_backward_general(case, aux_scale, router):
+    _backward_general(BWD[case], aux_scale, router)
+
+
+def test_backward_general_no_residual_tiny_capacity():
+    w = BWD["swiglu_shared"].scaled(residual=False, cf=0.1, E=16)
+    _backward_general(w, 0.25, True)
+
+
+def test_backward_general_zero_capacity():
+    """C = 0: every routed gradient is zero; dx = r dy + shared + router terms."""
+    w = BWD["gelu_bias"].scaled(cf=0.0)
+    _backward_general(w, 0.0, True)
 
 
 # ---------------------------------------------------------------------------------
