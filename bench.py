@@ -1,17 +1,21 @@
-"""Throughput of the MoE layer forward on one MI355X.
+"""Throughput of the MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+                    [--backward | --forward-only] [--dtype f32] [--router-grad]
 
 A step is one moe_forward call over the whole hot path (router GEMM, routing, dispatch,
 grouped expert GEMMs with the shared expert, combine, aux loss) on one batch of seeded
-synthetic input already resident in HBM. The default workload is T=16384 tokens,
-d_model 2048, 256 SwiGLU experts (intermediate 512) at top-8 plus one shared SwiGLU
-expert, bf16 data with fp32 routing, capacity factor 1.0.
+synthetic input already resident in HBM; with the backward (the default for the
+forward+backward workload 5, or --backward for any fp32 workload) the step is
+moe_forward followed by moe_backward. The default workload is T=16384 tokens, d_model
+2048, 256 SwiGLU experts (intermediate 512) at top-8 plus one shared SwiGLU expert,
+bf16 data with fp32 routing, capacity factor 1.0, forward.
 
 Prints one JSON line: throughput (tokens/s), a roofline entry for the dominant kernel
-(the gated grouped GEMM: routed experts plus the shared expert), whose duration comes
-from HIP events recorded around that kernel on its own stream over a second timed pass,
-and the CPU oracle timed on a bounded token sample of the same workload.
+(the GEMM launch with the largest time per step), whose duration comes from HIP events
+recorded around that kernel on its own stream over a second timed pass, per-GEMM MFMA
+and per-kernel HBM fractions, and the CPU oracle timed on a bounded token sample of the
+same workload.
 """
 
 from __future__ import annotations
@@ -42,22 +46,88 @@ def parse():
                     help="oracle sample size in tokens (0 = sized from a short probe run so "
                          "that the timed oracle run takes about --cpu-seconds)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward (fp32 experts)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time the forward only, also for the forward+backward workload")
+    ap.add_argument("--dtype", choices=["f32", "bf16"], default=None,
+                    help="override the workload's data type")
+    ap.add_argument("--router-grad", action="store_true",
+                    help="with the backward: also the router weight gradient and dx's "
+                         "router term (logits = x W_r)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MiB (a "
                          "known-size reference for hardware byte counters)")
     return ap.parse_args()
 
 
-def gemm1_flops(w, kept):
-    """Algorithmic FLOPs of the first (gated) expert GEMM launch: 2*D*F per output per
-    matrix, two matrices (gate and up) for SwiGLU, one for GELU/linear, over the kept
-    rows; plus the shared expert over all T rows."""
-    mats = 2 if w.kind == "swiglu" else 1
+def gemm_table(w, kept, backward, router_grad):
+    """Algorithmic FLOPs of one launch of each GEMM kernel a step launches, by kernel
+    name: 2 * rows * inner * outer per product, over the kept rows only (the shared expert
+    and the router over all T rows). Forward: the first expert GEMM has two weight
+    matrices (gate, up) for SwiGLU. Backward, per expert set: dH = dO W_out^T, the
+    pre-activation recompute, dW_out = H^T dO, dW_in (and dW_up) = X^T dZ, and the input
+    gradient dZ W_in^T (SwiGLU: two launches, one per weight)."""
+    T, D, E, Fs = w.T, w.D, w.E, w.shared_F
     F = w.F if w.kind != "linear" else w.D
-    fl = 2.0 * kept * w.D * F * mats
-    if w.shared_F:
-        fl += 2.0 * w.T * w.D * w.shared_F * 2
-    return fl
+    mats = 2 if w.kind == "swiglu" else 1
+    g1 = 2.0 * kept * D * F * mats
+    g2 = 2.0 * kept * F * D
+    f = {}
+    if w.dtype == "bf16":
+        f["expert_gemm1_swiglu" if w.kind == "swiglu" else "expert_gemm1"] = (
+            g1 + (4.0 * T * D * Fs if Fs else 0.0))
+        f["expert_gemm2"] = (g2 if w.kind != "linear" else 0.0) + (2.0 * T * Fs * D if Fs else 0.0)
+        f["router_gemm"] = 2.0 * T * D * E
+    else:
+        f["expert_gemm1_swiglu_f32" if w.kind == "swiglu" else "expert_gemm1_f32"] = g1
+        if w.kind != "linear":
+            f["expert_gemm2_f32"] = g2
+        if Fs:
+            f["shared_gemm1_swiglu_f32"] = 4.0 * T * D * Fs
+            f["shared_gemm2_f32"] = 2.0 * T * Fs * D
+        f["router_gemm_f32"] = 2.0 * T * D * E
+    if backward:
+        if w.kind == "linear":
+            f["bwd_dx_gemm"] = 2.0 * kept * D * D
+            f["bwd_dw_gemm"] = 2.0 * kept * D * D
+        else:
+            for pre, rows, FF, m in (("bwd_", kept, F, mats), ("bwd_shared_", T, Fs, 2)):
+                if pre == "bwd_shared_" and not Fs:
+                    continue
+                one = 2.0 * rows * D * FF
+                f[pre + "dh_gemm"] = one
+                f[pre + ("swiglu_recompute" if m == 2 else "gelu_recompute")] = one * m
+                f[pre + "dw_out_gemm"] = one
+                f[pre + "dw_in_gemm"] = one
+                if m == 2:
+                    f[pre + "dw_up_gemm"] = one
+                f[pre + "dx_gemm"] = one
+        if Fs and w.kind == "linear":
+            for nm in ("dh_gemm", "swiglu_recompute", "dw_out_gemm", "dw_in_gemm",
+                       "dw_up_gemm", "dx_gemm"):
+                f["bwd_shared_" + nm] = 2.0 * T * D * Fs * (2 if nm == "swiglu_recompute" else 1)
+        if router_grad:
+            f["bwd_dw_router_gemm"] = 2.0 * T * D * E
+            f["bwd_dx_router_gemm"] = 2.0 * T * D * E
+    return f
+
+
+def hbm_table(w, kept, backward):
+    """Algorithmic HBM bytes of one launch of the memory-bound kernels: each operand
+    read once and each result written once (kept rows only)."""
+    T, D, E, k = w.T, w.D, w.E, w.k
+    es = 2 if w.dtype == "bf16" else 4
+    b = {}
+    # y = r x + Sh + sum_kept g o: kept expert rows, x, Sh, idx/slot/gate; y written
+    b["combine"] = es * D * (kept + (T if w.residual else 0) + (T if w.shared_F else 0) + T) \
+        + T * k * 12
+    # logits read; idx, gate and the per-block expert partials written
+    b["route"] = T * E * 4 + T * k * 8
+    if backward:
+        # dy, kept expert rows, logits, idx/gate/slot read; dgate, dlogits written
+        b["dgate_router_bwd"] = 4 * D * (T + kept) + T * E * 4 * 2 + T * k * 16
+    return b
 
 
 def source_hash(*names):
@@ -84,9 +154,10 @@ def traffic_record(kernel, workload_name, src_hash):
     return r.get("bytes_per_launch")
 
 
-def cpu_baseline(w, inp, n_tokens):
+def cpu_baseline(w, inp, n_tokens, backward=False, router_grad=False):
     """The oracle (float64 NumPy) on the first n_tokens tokens of the workload, as a batch
-    of its own (its capacity recomputed for that batch size)."""
+    of its own (its capacity recomputed for that batch size): the forward, and with
+    ``backward`` the backward after it."""
     import numpy as np
     import oracle.moe_oracle as om
     from workloads import to_numpy_f32
@@ -102,9 +173,14 @@ def cpu_baseline(w, inp, n_tokens):
         kw["logits"] = to_numpy_f32(inp["logits"][:n_tokens])
     else:
         kw["w_router"] = to_numpy_f32(inp["w_router"])
+    dy = to_numpy_f32(inp["dy"][:n_tokens]) if backward else None
     t0 = time.perf_counter()
-    om.forward(x, w.k, w.kind, wts, cf=w.cf, residual=w.residual, shared=shared,
-               bf16=(w.dtype == "bf16"), **kw)
+    f = om.forward(x, w.k, w.kind, wts, cf=w.cf, residual=w.residual, shared=shared,
+                   bf16=(w.dtype == "bf16"), **kw)
+    if backward:
+        om.backward(dy, x, w.kind, wts, f["logits"], f["idx"], f["gate"], f["kept"], f["count"],
+                    residual=w.residual, shared=shared,
+                    w_router=kw.get("w_router") if router_grad else None)
     dt = time.perf_counter() - t0
     threads = None
     try:
@@ -128,6 +204,16 @@ def main():
     from workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    backward = (w.backward or args.backward) and not args.forward_only
+    if args.dtype and args.dtype != w.dtype:
+        w = w.scaled(dtype=args.dtype, name=w.name.replace("_bf16", "").replace("_f32", "")
+                     + "_" + args.dtype)
+    if backward and not w.backward:
+        w = w.scaled(backward=True, name=w.name + "_fwd_bwd")
+    if backward and w.dtype != "f32":
+        print("the backward runs on fp32 experts: add --dtype f32", file=sys.stderr)
+        sys.exit(2)
+    router_grad = backward and args.router_grad and w.logits_mode == "router"
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
     inp = make_inputs(w)
@@ -144,7 +230,16 @@ def main():
     C = ops.capacity(w.T, w.k, w.E, w.cf)
     kw = {"logits": g["logits"]} if "logits" in g else {"w_router": g["w_router"]}
     out = ops.forward(g["x"], ex, k=w.k, capacity=C, shared=shared, use_residual=w.residual, **kw)
-    call = out["_call"]
+    calls = [out["_call"]]
+    if backward:
+        grads = ops.backward(g["dy"], g["x"], ex, out, k=w.k, use_residual=w.residual,
+                             shared=shared, w_router=g["w_router"] if router_grad else None)
+        calls.append(grads["_call"])
+
+    def step():
+        for c in calls:
+            c()
+
     torch.cuda.synchronize()
     kept = int(out["kept"].sum().item())
     stream = torch.cuda.current_stream()
@@ -159,14 +254,14 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        call()
+        step()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(args.steps):
-        call()
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
@@ -177,25 +272,40 @@ def main():
     torch.cuda.synchronize()
     p0 = time.perf_counter()
     for _ in range(args.steps):
-        call()
+        step()
     torch.cuda.synchronize()
     prof_ms = (time.perf_counter() - p0) * 1e3 / args.steps
     ops.profile_enable(False)
     kern = ops.profile_read()
 
-    dom = "expert_gemm1_swiglu" if w.kind == "swiglu" else (
-        "expert_gemm1" if w.dtype == "bf16" else "expert_gemm1_f32")
-    cnt, tot = kern.get(dom, (0, 0.0))
-    dom_ms = tot / max(cnt, 1)
-    flops = gemm1_flops(w, kept)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    achieved = flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
+    flops = gemm_table(w, kept, backward, router_grad)
+    gemms = {}
+    for name, fl in flops.items():
+        if name not in kern or fl <= 0:
+            continue
+        cnt, tot = kern[name]
+        avg = tot / cnt
+        ach = fl / (avg * 1e-3) / 1e12
+        gemms[name] = {"ms_per_step": round(tot / args.steps, 4), "avg_launch_ms": round(avg, 4),
+                       "tflops": round(ach, 2), "frac": round(ach / peak, 4)}
+    dom = max(gemms, key=lambda n: gemms[n]["ms_per_step"])
+    dom_ms = kern[dom][1] / kern[dom][0]
+    achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
     src_hash = source_hash(*(("gemm_bf16.hip", "gemm_bf16_tile.h") if w.dtype == "bf16"
                              else ("gemm_f32.hip",)))
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic_record(dom, w.name, src_hash),
-                "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(dom_ms, 4)}
+                "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(dom_ms, 4)}
+    hbm = {}
+    for name, by in hbm_table(w, kept, backward).items():
+        if name not in kern:
+            continue
+        cnt, tot = kern[name]
+        gbs = by / (tot / cnt * 1e-3) / 1e9
+        hbm[name] = {"avg_launch_ms": round(tot / cnt, 4), "bytes_per_launch": by,
+                     "GBs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
     kernels = {k: {"launches_per_step": round(c / args.steps, 2), "avg_ms": round(t / c, 4)}
                for k, (c, t) in kern.items()}
@@ -204,24 +314,27 @@ def main():
     if not args.no_cpu_baseline:
         if args.cpu_tokens:
             n = min(args.cpu_tokens, w.T)
-            v, dt, threads = cpu_baseline(w, inp, n)
+            v, dt, threads = cpu_baseline(w, inp, n, backward, router_grad)
         else:
             # grow the sample until one run takes at least half of --cpu-seconds (the
             # oracle's per-token rate rises with batch size, so a single probe misjudges)
             n = min(w.T, 512)
             while True:
-                v, dt, threads = cpu_baseline(w, inp, n)
+                v, dt, threads = cpu_baseline(w, inp, n, backward, router_grad)
                 if n >= w.T or dt >= 0.5 * args.cpu_seconds:
                     break
                 grow = max(2.0, min(8.0, args.cpu_seconds / max(dt, 1e-3)))
                 n = min(w.T, int(n * grow) // 256 * 256)
+        what = "forward + backward" if backward else "forward"
         cpu = {"value": round(v, 2), "unit": "tokens/s", "cores": threads or os.cpu_count(),
                "kind": "oracle", "seconds": round(dt, 2),
-               "sample": f"oracle forward (float64 NumPy) on the first {n} tokens of the "
+               "sample": f"oracle {what} (float64 NumPy) on the first {n} tokens of the "
                          f"workload as a batch of their own"}
 
     rec = {
-        "metric": "MoE layer fwd tokens/s (E=256,k=8,D=2048) + MFMA % / HBM GB/s of peak",
+        "metric": ("MoE layer fwd tokens/s (E=256,k=8,D=2048) + MFMA % / HBM GB/s of peak"
+                   if not backward else
+                   f"MoE layer fwd+bwd tokens/s (E={w.E},k={w.k},D={w.D}) + MFMA % / HBM GB/s of peak"),
         "value": round(w.T / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -236,8 +349,11 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d_model": w.D, "experts": w.E, "top_k": w.k,
                    "expert": w.kind, "d_hidden": w.F, "shared_hidden": w.shared_F,
                    "capacity": C, "capacity_factor": w.cf, "kept_assignments": kept,
-                   "parallelism": "single GPU"},
+                   "step": "forward + backward" if backward else "forward",
+                   "router_grad": router_grad, "parallelism": "single GPU"},
         "roofline": roofline,
+        "gemms": gemms,
+        "hbm": hbm,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "profiled_ms_per_step": round(prof_ms, 4),

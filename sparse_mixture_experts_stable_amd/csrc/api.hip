@@ -233,12 +233,14 @@ moe_status_t run_experts(const ExpertPlan* plans, const moe_experts_t* const* ex
   }
   for (int i = 0; i < n; ++i) {
     ExpertPlan p = plans[i];
-    moe_status_t st = launch_gemm_f32(p.f1, A_ROWS, B_KN,
-                                      p.f1.epi == EPI_SWIGLU ? "expert_gemm1_swiglu_f32"
-                                                             : "expert_gemm1_f32", s);
+    // a dense set (the shared expert) runs under names of its own
+    const bool dense = p.f1.row_map == nullptr;
+    const char* n1 = p.f1.epi == EPI_SWIGLU ? (dense ? "shared_gemm1_swiglu_f32" : "expert_gemm1_swiglu_f32")
+                                            : (dense ? "shared_gemm1_f32" : "expert_gemm1_f32");
+    moe_status_t st = launch_gemm_f32(p.f1, A_ROWS, B_KN, n1, s);
     if (st != MOE_OK) return st;
     if (p.two_stage) {
-      st = launch_gemm_f32(p.f2, A_ROWS, B_KN, "expert_gemm2_f32", s);
+      st = launch_gemm_f32(p.f2, A_ROWS, B_KN, dense ? "shared_gemm2_f32" : "expert_gemm2_f32", s);
       if (st != MOE_OK) return st;
     }
   }
@@ -600,7 +602,20 @@ namespace {
 // One expert set seen by the backward: routed (rows of expert e are its kept
 // assignments, slot_assign order, output gradient gate * dy) or dense (the shared expert:
 // all T rows, output gradient dy).
+// Kernel names of one set's launches (static storage: the profiler keeps the pointers).
+struct BwdNames {
+  const char *dh, *recompute_gelu, *recompute_swiglu, *dw_out, *dw_in, *dw_up, *dx;
+};
+constexpr BwdNames kRoutedNames{"bwd_dh_gemm", "bwd_gelu_recompute", "bwd_swiglu_recompute",
+                                "bwd_dw_out_gemm", "bwd_dw_in_gemm", "bwd_dw_up_gemm",
+                                "bwd_dx_gemm"};
+constexpr BwdNames kSharedNames{"bwd_shared_dh_gemm", "bwd_shared_gelu_recompute",
+                                "bwd_shared_swiglu_recompute", "bwd_shared_dw_out_gemm",
+                                "bwd_shared_dw_in_gemm", "bwd_shared_dw_up_gemm",
+                                "bwd_shared_dx_gemm"};
+
 struct BwdSet {
+  const BwdNames* names;
   const moe_experts_t* ex;
   int rows;                  // C (routed) or T (dense)
   const int32_t* row_map;    // slot_assign or NULL
@@ -684,7 +699,8 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
   p.C = S.g;
   p.ldc = F;
   p.c_gstride = int64_t(R) * F;
-  st = launch_gemm_f32(p, A_ROWS, B_NK, "bwd_dh_gemm", s);
+  const BwdNames& nm = *S.names;
+  st = launch_gemm_f32(p, A_ROWS, B_NK, nm.dh, s);
   if (st != MOE_OK) return st;
 
   // recompute the pre-activation; epilogue writes H and dZ (GELU) or H, dA, dU (SwiGLU)
@@ -713,7 +729,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
   p.C2 = S.u;
   p.ldc = F;
   p.c_gstride = int64_t(R) * F;
-  st = launch_gemm_f32(p, A_ROWS, B_KN, swiglu ? "bwd_swiglu_recompute" : "bwd_gelu_recompute", s);
+  st = launch_gemm_f32(p, A_ROWS, B_KN, swiglu ? nm.recompute_swiglu : nm.recompute_gelu, s);
   if (st != MOE_OK) return st;
 
   // dW_out = H^T dO (K = the group's rows; dO rows gathered and gated)
@@ -737,7 +753,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
   p.C = S.dw_out;
   p.ldc = D;
   p.c_gstride = int64_t(F) * D;
-  st = launch_gemm_f32(p, A_KROWS, B_KROWS, "bwd_dw_out_gemm", s);
+  st = launch_gemm_f32(p, A_KROWS, B_KROWS, nm.dw_out, s);
   if (st != MOE_OK) return st;
 
   // dW_in = X^T dZ (dA); dW_up = X^T dU
@@ -761,7 +777,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
     p.C = w == 0 ? S.dw_in : S.dw_up;
     p.ldc = F;
     p.c_gstride = int64_t(D) * F;
-    st = launch_gemm_f32(p, A_KROWS, B_KROWS, w == 0 ? "bwd_dw_in_gemm" : "bwd_dw_up_gemm", s);
+    st = launch_gemm_f32(p, A_KROWS, B_KROWS, w == 0 ? nm.dw_in : nm.dw_up, s);
     if (st != MOE_OK) return st;
   }
 
@@ -798,7 +814,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
     p.C = S.dxr;
     p.ldc = D;
     p.c_gstride = int64_t(R) * D;
-    st = launch_gemm_f32(p, A_ROWS, B_NK, "bwd_dx_gemm", s);
+    st = launch_gemm_f32(p, A_ROWS, B_NK, nm.dx, s);
     if (st != MOE_OK) return st;
   }
   return MOE_OK;
@@ -914,6 +930,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
     if (st != MOE_OK) return st;
   } else {
     BwdSet r{};
+    r.names = &kRoutedNames;
     r.ex = &ex;
     r.rows = C;
     r.row_map = a->slot_assign;
@@ -936,6 +953,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
 
   if (a->shared.w_in) {
     BwdSet sh{};
+    sh.names = &kSharedNames;
     sh.ex = &a->shared;
     sh.rows = T;
     sh.row_div = 1;

@@ -219,19 +219,21 @@ def forward(x, experts, *, k, capacity, w_router=None, logits=None, shared=None,
     L.check("moe_forward", st)
     o["ws"] = ws
     # everything a repeat call needs, kept alive together
-    o["_call"] = ForwardCall(a, ws, (x, w_router, keep, shkeep))
+    o["_call"] = PreparedCall("moe_forward", a, ws, (x, w_router, keep, shkeep))
     return o
 
 
-class ForwardCall:
-    """A prepared moe_forward: the argument struct and workspace of an earlier call, so
-    that the same layer can be re-run on the same buffers without re-marshalling."""
+class PreparedCall:
+    """A prepared library call (moe_forward or moe_backward): the argument struct and
+    workspace of an earlier call, so that the same layer can be re-run on the same
+    buffers without re-marshalling."""
 
-    def __init__(self, args, ws, keepalive):
+    def __init__(self, fn_name, args, ws, keepalive):
         self.args = args
         self.ws = ws
         self._keep = keepalive
-        self._fn = L.lib().moe_forward
+        self._name = fn_name
+        self._fn = getattr(L.lib(), fn_name)
         self._ref = ctypes.byref(self.args)
         self._ws_p = _p(ws)
         self._ws_n = ws.numel()
@@ -240,7 +242,7 @@ class ForwardCall:
         s = ctypes.c_void_p(stream) if stream is not None else _stream()
         st = self._fn(self._ref, self._ws_p, self._ws_n, s)
         if st != L.MOE_OK:
-            L.check("moe_forward", st)
+            L.check(self._name, st)
 
 
 def backward(dy, x, experts, fwd, *, k, use_residual=True, aux_grad_scale=0.0, shared=None,
@@ -308,7 +310,8 @@ def backward(dy, x, experts, fwd, *, k, use_residual=True, aux_grad_scale=0.0, s
     ws = _ws(L.lib().moe_backward_workspace_size(ctypes.byref(a)), dev)
     st = L.lib().moe_backward(ctypes.byref(a), _p(ws), ws.numel(), _stream())
     L.check("moe_backward", st)
-    del keep, shkeep
+    out["_call"] = PreparedCall("moe_backward", a, ws,
+                                (dy, x, w_router, keep, shkeep, fwd, out.copy()))
     return out
 
 
