@@ -268,7 +268,7 @@ moe_status_t router_gemm(const void* x, int dt, int64_t ldx, const void* w, int 
     p.ldc = E;
     return launch_gemm_bf16(b, false, "router_gemm", s);
   }
-  if (dt == MOE_F32 && D % kF32BK == 0 && E % 4 == 0 && ldx % 4 == 0) {
+  if (dt == MOE_F32 && D % 4 == 0 && E % 4 == 0 && ldx % 4 == 0) {
     GemmF32Problem p{};
     p.A = static_cast<const float*>(x);
     p.lda = ldx;

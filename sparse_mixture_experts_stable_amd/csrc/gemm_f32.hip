@@ -11,11 +11,18 @@
 //   dW2  = H^T dO,  dW1 = X^T dZ             A_KROWS x B_KROWS (K = the expert's rows)
 //   dX_e = dZ W1^T                           A_ROWS x B_NK (+ EPI_ACCUM for SwiGLU's 2nd)
 //
-// Tile 64 x 64 x 16 per 256-thread block; four waves in 2 x 2, each 32 x 32 (2 x 2
-// MFMA tiles). LDS holds A as [k][m] and B as [k][n] (m / n contiguous, rows padded to
-// 68 floats), so every fragment read is one conflict-free 4-byte read per lane; operands
-// that arrive k-contiguous from HBM are transposed on the LDS store. Loads are guarded
-// per float4 against M, N and K, so those sizes need only be multiples of 4.
+// Tile 64 x 64 x 32 per 256-thread block; four waves in 2 x 2, each 32 x 32 (2 x 2
+// MFMA tiles). An operand keeps its HBM orientation in LDS, so every global load is a
+// float4 and every LDS store a float4 (no transposition):
+//   k-contiguous operands (A_ROWS, B_NK) as [row][k], rows padded to 36 floats: eight
+//     threads read one full 128-byte line of a row per k-tile;
+//   m/n-contiguous operands (A_KROWS, B_KN, B_KROWS) as [k][m|n], rows padded to 80
+//     floats.
+// MFMA step ks (of 8) takes k = 4 ks + lane / 16, so lane l reads the A value
+// (row l % 16, that k) and the B value (that k, column l % 16) one float at a time; both
+// paddings make these 64-lane reads conflict-free (36 r mod 64 runs over distinct
+// multiples of 4, 80 = 16 mod 64 separates the four k rows of one read). Loads are
+// guarded per float4 against M, N and K, so those sizes need only be multiples of 4.
 
 #include "internal.h"
 
@@ -23,7 +30,9 @@ namespace moe {
 
 namespace {
 constexpr int BM = kF32BM, BN = kF32BN, BK = kF32BK;
-constexpr int LDP = 68;  // padded LDS row (floats)
+constexpr int KP = BK + 4;  // LDS row of a [row][k] operand (floats)
+constexpr int NP = 80;      // LDS row of a [k][m|n] operand (floats)
+static_assert(BM == 64 && BN == 64 && BK == 32, "load coordinates assume a 64 x 64 x 32 tile");
 
 __device__ __forceinline__ int logical_block_f32(int bid, int nblk) {
   const int q = nblk >> 3, r = nblk & 7;
@@ -46,8 +55,12 @@ __device__ __forceinline__ float gelu_erf_grad(float z) {
 template <int AM, int BMODE, bool GATED>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   constexpr int NB = GATED ? 2 : 1;
-  __shared__ float As[2][BK][LDP];
-  __shared__ float Bs[NB][2][BK][LDP];
+  constexpr bool AK = AM == A_ROWS;     // A stored [m][k]
+  constexpr bool BK_ = BMODE == B_NK;   // B stored [n][k]
+  constexpr int A_SZ = AK ? BM * KP : BK * NP;
+  constexpr int B_SZ = BK_ ? BN * KP : BK * NP;
+  __shared__ float As[2][A_SZ];
+  __shared__ float Bs[NB][2][B_SZ];
   const int lid = logical_block_f32(blockIdx.x, gridDim.x);
   const int per_group = P.m_tiles * P.n_tiles;
   const int g = lid / per_group;
@@ -70,81 +83,78 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   }
   const int N = P.N;
 
-  // ---- per-thread load coordinates ----
-  // transposing loads (k contiguous in HBM): row = tid / 4, k quad = tid % 4
-  // direct loads (m / n contiguous in HBM): k row = tid / 16, quad = tid % 16
-  const int tr_row = tid >> 2, tr_kq = tid & 3;
-  const int dr_k = tid >> 4, dr_q = tid & 15;
+  // ---- per-thread load coordinates (two float4 per operand per k-tile) ----
+  // [row][k] operands: row = tid / 8 (+ 32), k quad = tid % 8
+  // [k][m|n] operands: k row = tid / 16 (+ 16), quad = tid % 16
+  const int kr_row = tid >> 3, kr_q = tid & 7;
+  const int mr_k = tid >> 4, mr_q = tid & 15;
 
   const float* a_base = P.A + size_t(g) * P.a_gstride;
-  const float* a_row_ptr = nullptr;  // A_ROWS
+  const float* a_row_ptr[2] = {nullptr, nullptr};  // A_ROWS
   if (AM == A_ROWS) {
-    int r = m0 + tr_row;
-    if (r >= M) r = m0;
-    const int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + r] / P.row_div : r;
-    a_row_ptr = a_base + size_t(src) * P.lda + tr_kq * 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int r = m0 + kr_row + 32 * h;
+      if (r >= M) r = m0;
+      const int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + r] / P.row_div : r;
+      a_row_ptr[h] = a_base + size_t(src) * P.lda + kr_q * 4;
+    }
   }
   const float* b_base = P.B + size_t(g) * P.b_gstride;
   const float* b1_base = GATED ? P.B1 + size_t(g) * P.b_gstride : nullptr;
   const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  float4 ra, rb[NB];
+  float4 ra[2], rb[NB][2];
   auto load = [&](int kt) {
     const int k0 = kt * BK;
-    if (AM == A_ROWS) {
-      ra = (k0 + tr_kq * 4 < Kg) ? ld4(a_row_ptr + k0) : zero;
-    } else {
-      const int kk = k0 + dr_k;
-      ra = zero;
-      if (kk < Kg && m0 + dr_q * 4 < M) {
-        const int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + kk] / P.row_div : kk;
-        ra = ld4(a_base + size_t(src) * P.lda + m0 + dr_q * 4);
-      }
-    }
-    if (BMODE == B_KN) {
-      const int kk = k0 + dr_k;
-      const int n = n0 + dr_q * 4;
-      const bool ok = kk < Kg && n < N;
-      rb[0] = ok ? ld4(b_base + size_t(kk) * P.ldb + n) : zero;
-      if constexpr (GATED) rb[1] = ok ? ld4(b1_base + size_t(kk) * P.ldb + n) : zero;
-    } else if (BMODE == B_NK) {
-      const int n = n0 + tr_row;
-      const int kq = k0 + tr_kq * 4;
-      rb[0] = (n < N && kq < Kg) ? ld4(b_base + size_t(n) * P.ldb + kq) : zero;
-    } else {
-      const int kk = k0 + dr_k;
-      const int n = n0 + dr_q * 4;
-      rb[0] = zero;
-      if (kk < Kg && n < N) {
-        int src = kk;
-        float sc = 1.f;
-        if (P.b_row_map) {
-          const int a = P.b_row_map[size_t(g) * P.row_map_ld + kk];
-          src = a / P.row_div;
-          if (P.gate) sc = P.gate[a];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (AM == A_ROWS) {
+        ra[h] = (k0 + kr_q * 4 < Kg) ? ld4(a_row_ptr[h] + k0) : zero;
+      } else {
+        const int kk = k0 + mr_k + 16 * h;
+        ra[h] = zero;
+        if (kk < Kg && m0 + mr_q * 4 < M) {
+          const int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + kk] / P.row_div : kk;
+          ra[h] = ld4(a_base + size_t(src) * P.lda + m0 + mr_q * 4);
         }
-        const float4 v = ld4(b_base + size_t(src) * P.ldb + n);
-        rb[0] = make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc);
+      }
+      if (BMODE == B_KN) {
+        const int kk = k0 + mr_k + 16 * h;
+        const int n = n0 + mr_q * 4;
+        const bool ok = kk < Kg && n < N;
+        rb[0][h] = ok ? ld4(b_base + size_t(kk) * P.ldb + n) : zero;
+        if constexpr (GATED) rb[1][h] = ok ? ld4(b1_base + size_t(kk) * P.ldb + n) : zero;
+      } else if (BMODE == B_NK) {
+        const int n = n0 + kr_row + 32 * h;
+        const int kq = k0 + kr_q * 4;
+        rb[0][h] = (n < N && kq < Kg) ? ld4(b_base + size_t(n) * P.ldb + kq) : zero;
+      } else {
+        const int kk = k0 + mr_k + 16 * h;
+        const int n = n0 + mr_q * 4;
+        rb[0][h] = zero;
+        if (kk < Kg && n < N) {
+          int src = kk;
+          float sc = 1.f;
+          if (P.b_row_map) {
+            const int a = P.b_row_map[size_t(g) * P.row_map_ld + kk];
+            src = a / P.row_div;
+            if (P.gate) sc = P.gate[a];
+          }
+          const float4 v = ld4(b_base + size_t(src) * P.ldb + n);
+          rb[0][h] = make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc);
+        }
       }
     }
   };
   auto store = [&](int buf) {
-    if (AM == A_ROWS) {
-      As[buf][tr_kq * 4 + 0][tr_row] = ra.x;
-      As[buf][tr_kq * 4 + 1][tr_row] = ra.y;
-      As[buf][tr_kq * 4 + 2][tr_row] = ra.z;
-      As[buf][tr_kq * 4 + 3][tr_row] = ra.w;
-    } else {
-      *reinterpret_cast<float4*>(&As[buf][dr_k][dr_q * 4]) = ra;
-    }
-    if (BMODE == B_NK) {
-      Bs[0][buf][tr_kq * 4 + 0][tr_row] = rb[0].x;
-      Bs[0][buf][tr_kq * 4 + 1][tr_row] = rb[0].y;
-      Bs[0][buf][tr_kq * 4 + 2][tr_row] = rb[0].z;
-      Bs[0][buf][tr_kq * 4 + 3][tr_row] = rb[0].w;
-    } else {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) *reinterpret_cast<float4*>(&Bs[b][buf][dr_k][dr_q * 4]) = rb[b];
+    for (int h = 0; h < 2; ++h) {
+      const int a_off = AK ? (kr_row + 32 * h) * KP + kr_q * 4 : (mr_k + 16 * h) * NP + mr_q * 4;
+      *reinterpret_cast<float4*>(&As[buf][a_off]) = ra[h];
+      const int b_off = BK_ ? (kr_row + 32 * h) * KP + kr_q * 4 : (mr_k + 16 * h) * NP + mr_q * 4;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) *reinterpret_cast<float4*>(&Bs[b][buf][b_off]) = rb[b][h];
     }
   };
 
@@ -167,14 +177,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
       if (kt + 1 < nk) load(kt + 1);
 #pragma unroll
       for (int ks = 0; ks < BK / 4; ++ks) {
+        const int kl = ks * 4 + fc;
         float af[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = As[cur][ks * 4 + fc][wm * 32 + i * 16 + fr];
+        for (int i = 0; i < 2; ++i) {
+          const int row = wm * 32 + i * 16 + fr;
+          af[i] = As[cur][AK ? row * KP + kl : kl * NP + row];
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           float bf[2];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) bf[j] = Bs[b][cur][ks * 4 + fc][wn * 32 + j * 16 + fr];
+          for (int j = 0; j < 2; ++j) {
+            const int col = wn * 32 + j * 16 + fr;
+            bf[j] = Bs[b][cur][BK_ ? col * KP + kl : kl * NP + col];
+          }
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll

@@ -147,7 +147,7 @@ struct GemmF32Problem {
   int32_t epi;
   int32_t tiles;
 };
-constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
+constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 32;
 moe_status_t launch_gemm_f32(GemmF32Problem& p, int amode, int bmode, const char* name,
                              hipStream_t s);
 // Column sums per group: out[g*out_gstride + n] = sum over rows r < M_g (in row order,
