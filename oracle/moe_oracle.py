@@ -27,6 +27,9 @@ Readings where the pages are silent or disagree (each one is listed in the design doc
   * the top-k key is the fp32 logit, exact ties to the lower expert index (P2, P3);
   * -0.0 and +0.0 compare equal;
   * gates are renormalised over the k choices before any drop and never after (P1);
+    P3's renormalisation of the survivors is a flag, off by default;
+  * with sigmoid scoring (P3) the aux loss keeps the softmax probabilities for P_e
+    and the counts of the selection actually made for f_e;
   * capacity is the exact ceil(T*k*cf/E) of the given double cf, with no clamp, so
     cf = 0 gives C = 0;
   * the aux loss uses f_e = count_e/(T*k) (P1 trap 6, P3), so it is 1 at uniform load;
@@ -65,6 +68,11 @@ __all__ = [
     "silu_grad",
     "router_grad",
     "aux_grad",
+    "sigmoid",
+    "log_sigmoid",
+    "renormalise_kept",
+    "z_loss",
+    "z_loss_grad",
 ]
 
 
@@ -139,27 +147,67 @@ def top_k(s, k):
     return idx
 
 
-def route(logits, k):
-    """Softmax router with top-k selection, renormalised gates and pre-drop statistics.
+def sigmoid(s):
+    """Logistic function evaluated without overflow (P3 stable_sigmoid): 1/(1+e^-s) for
+    s >= 0, e^s/(1+e^s) below."""
+    s = np.asarray(s, dtype=np.float64)
+    out = np.empty_like(s)
+    pos = s >= 0.0
+    out[pos] = 1.0 / (1.0 + np.exp(-s[pos]))
+    ex = np.exp(s[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def log_sigmoid(s):
+    """log(sigmoid(s)) = -log(1 + e^-s), finite for any finite s (P3 _log_sigmoid)."""
+    return -np.logaddexp(0.0, -np.asarray(s, dtype=np.float64))
+
+
+def route(logits, k, *, scoring="softmax", selection_bias=None):
+    """Token-choice router with top-k selection, renormalised gates and pre-drop
+    statistics.
 
     * p = softmax over all E experts (P1 section 2 top_k_gating; P5 TopKMoE).
-    * idx = top-k by logit with lower-index tie-break (see ``top_k``). Softmax is
-      strictly increasing, so ranking the logits is ranking p in exact arithmetic
-      (P3 route_logits makes the same argument).
-    * gate[t, j] = p[t, idx_tj] / sum_r p[t, idx_tr] (P1 top_k_gating; equals the
-      softmax over the selected logits, P2 alpha equation).
+    * clean scores: p for softmax scoring, sigmoid(s) for sigmoid scoring (P3
+      route_logits, V3-style independent scores).
+    * idx = top-k with lower-index tie-break (see ``top_k``) of the logits when no
+      selection bias is given (both score functions are strictly increasing, so this
+      is the ranking of the clean scores in exact arithmetic; P3 route_logits makes
+      the same argument), else of clean + bias: the bias moves selection only (P3
+      route_logits, selection_bias).
+    * gates, from the clean scores of the selected experts only: softmax scoring,
+      gate[t, j] = p[t, idx_tj] / sum_r p[t, idx_tr] (P1 top_k_gating; the softmax of
+      the selected logits, P2 alpha equation); sigmoid scoring, the softmax over the
+      selected experts of log sigmoid(s) (P3: normalised in log space), i.e.
+      sigmoid(s_j) / sum_r sigmoid(s_r).
     * count[e] = number of (t, j) with idx = e, before any capacity drop;
       prob_sum[e] = sum_t p[t, e] (P2 f_e / m_e equations, P3 bincount).
     * aux = E * sum_e (count_e / (T*k)) * (prob_sum_e / T) (P1 trap 6; P3
       switch_auxiliary_loss).
+    * z_loss = mean_t (logsumexp_e s[t, e])^2 (P3 router_z_loss, ST-MoE).
     """
     s = _finite("logits", logits, ndim=2)
     T, E = s.shape
     k = _check_k(k, E)
+    if scoring not in ("softmax", "sigmoid"):
+        raise ValueError("scoring must be 'softmax' or 'sigmoid'")
     p = softmax(s)
-    idx = top_k(s, k)
-    p_sel = np.take_along_axis(p, idx, axis=1)
-    gate = p_sel / np.sum(p_sel, axis=1, keepdims=True)
+    clean = p if scoring == "softmax" else sigmoid(s)
+    if selection_bias is None:
+        idx = top_k(s, k)
+    else:
+        b = _finite("selection_bias", selection_bias, ndim=1)
+        if b.shape != (E,):
+            raise ValueError("selection_bias must have shape [E]")
+        idx = top_k(clean + b[None, :], k)
+    if scoring == "softmax":
+        p_sel = np.take_along_axis(p, idx, axis=1)
+        gate = p_sel / np.sum(p_sel, axis=1, keepdims=True)
+    else:
+        ls = log_sigmoid(np.take_along_axis(s, idx, axis=1))
+        w = np.exp(ls - np.max(ls, axis=1, keepdims=True))
+        gate = w / np.sum(w, axis=1, keepdims=True)
     count = np.bincount(idx.ravel(), minlength=E).astype(np.int64)
     prob_sum = np.sum(p, axis=0)
     f = count / (T * k)
@@ -167,14 +215,34 @@ def route(logits, k):
     aux = float(E * np.sum(f * P))
     return {
         "p": p,
+        "clean": clean,
         "idx": idx,
         "gate": gate,
         "count": count,
         "prob_sum": prob_sum,
         "aux": aux,
+        "z_loss": z_loss(s),
         "token_fraction": count / T,
         "probability_mass": P,
     }
+
+
+def z_loss(logits):
+    """Router z-loss: the token mean of the squared log-partition, mean_t lse_t^2 with
+    lse_t = log sum_e exp(s[t, e]) (P3 router_z_loss; squared per token, then averaged)."""
+    s = np.asarray(logits, dtype=np.float64)
+    m = np.max(s, axis=1)
+    lse = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
+    return float(np.mean(lse ** 2))
+
+
+def z_loss_grad(logits):
+    """d z_loss / d s[t, e] = (2 / T) lse_t p[t, e], since d lse_t / d s[t, e] = p[t, e]."""
+    s = np.asarray(logits, dtype=np.float64)
+    T = s.shape[0]
+    m = np.max(s, axis=1)
+    lse = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
+    return (2.0 / T) * lse[:, None] * softmax(s)
 
 
 # ----------------------------------------------------------------------------------
@@ -351,27 +419,41 @@ def shared_apply(shared, xr, bf16=False):
     return o
 
 
-def combine(x, shared_out, o, gate, kept, residual):
+def renormalise_kept(gate, kept):
+    """Gates after P3's drop-then-renormalise-survivors policy (dispatch_with_capacity,
+    renormalize_kept_gates): kept gates divided by the token's kept gate mass, dropped
+    ones 0; a token with nothing kept keeps all zeros (no division by zero)."""
+    g = np.where(np.asarray(kept, dtype=bool), _f64(gate), 0.0)
+    mass = np.sum(g, axis=1, keepdims=True)
+    return np.divide(g, mass, out=np.zeros_like(g), where=mass > 0.0)
+
+
+def combine(x, shared_out, o, gate, kept, residual, renormalize=False):
     """y_t = r x_t + Sh_t + sum over kept j of gate_tj o_tj, j ascending (P1 trap 4 and
-    section 2; P2 y equation; P4 step 6). A dropped assignment contributes nothing."""
+    section 2; P2 y equation; P4 step 6). A dropped assignment contributes nothing.
+    With ``renormalize`` the kept gates are first renormalised over the survivors
+    (``renormalise_kept``)."""
     o = _f64(o)
     T, k, D = o.shape
+    g = renormalise_kept(gate, kept) if renormalize else np.where(kept, _f64(gate), 0.0)
     y = np.zeros((T, D))
     if residual:
         y = y + _f64(x)
     if shared_out is not None:
         y = y + _f64(shared_out)
     for j in range(k):
-        w = np.where(kept[:, j], gate[:, j], 0.0)
+        w = np.where(kept[:, j], g[:, j], 0.0)
         y = y + w[:, None] * o[:, j, :]
     return y
 
 
 def forward(x, k, kind, weights, *, logits=None, w_router=None, C=None, cf=None,
-            residual=True, shared=None, bf16=False, tokens=None):
+            residual=True, shared=None, bf16=False, tokens=None, scoring="softmax",
+            selection_bias=None, renormalize=False):
     """The whole layer: router scores (if w_router is given), routing, capacity,
     dispatch, experts, combine, aux loss (P1 section 2 moe_forward; P3
-    EducationalMoE.forward; P5 TopKMoE.forward).
+    EducationalMoE.forward; P5 TopKMoE.forward). ``scoring``, ``selection_bias`` and
+    ``renormalize`` select P3's router variants (see ``route`` and ``combine``).
 
     ``tokens`` restricts the expert/combine part to a subset of tokens (routing and
     dispatch always run over the whole batch, since slots depend on every earlier
@@ -384,7 +466,7 @@ def forward(x, k, kind, weights, *, logits=None, w_router=None, C=None, cf=None,
         if w_router is None:
             raise ValueError("need logits or w_router")
         logits = _f64(x) @ _f64(w_router)   # P2 score equation s = x^T w_e
-    r = route(logits, k)
+    r = route(logits, k, scoring=scoring, selection_bias=selection_bias)
     E = r["p"].shape[1]
     if C is None:
         C = capacity(T, k, E, cf)
@@ -392,7 +474,8 @@ def forward(x, k, kind, weights, *, logits=None, w_router=None, C=None, cf=None,
     toks = np.arange(T) if tokens is None else np.asarray(tokens)
     o = expert_outputs(kind, weights, x, r["idx"], d["kept"], tokens=toks, bf16=bf16)
     sh = shared_apply(shared, np.asarray(x)[toks], bf16=bf16) if shared is not None else None
-    y = combine(np.asarray(x)[toks], sh, o, r["gate"][toks], d["kept"][toks], residual)
+    y = combine(np.asarray(x)[toks], sh, o, r["gate"][toks], d["kept"][toks], residual,
+                renormalize=renormalize)
     out = dict(r)
     out.update(d)
     out.update({"C": C, "logits": _f64(logits), "o": o, "shared_out": sh, "y": y,
@@ -430,18 +513,33 @@ def dense_forward(x, k, kind, weights, *, logits, C, residual=True, shared=None)
 # Backward (single-linear experts): P1 section 2 moe_backward and trap 7
 # ----------------------------------------------------------------------------------
 
-def router_grad(logits, idx, gate, dgate):
+def router_grad(logits, idx, gate, dgate, scoring="softmax"):
     """Gradient of the loss through the renormalised gates back to the logits, with the
-    top-k set held fixed (P1 trap 7: quotient rule, then the softmax Jacobian).
+    top-k set held fixed (P1 trap 7: quotient rule, then the derivative of the scores).
 
-    With q_j = p[t, idx_tj] and S_t = sum_r q_r, gate_j = q_j / S_t gives
+    With q_j the clean score of the j-th choice and S_t = sum_r q_r, gate_j = q_j / S_t
+    gives
         dq_j = (dgate_j - sum_r gate_r dgate_r) / S_t          (quotient rule)
+    Softmax scoring, q = p[t, idx_tj]:
         dp[t, i] = sum_j [i == idx_tj] dq_j
         ds[t, i] = p_i (dp_i - sum_l p_l dp_l)                 (softmax Jacobian)
+    Sigmoid scoring, q = sigmoid(s[t, idx_tj]) (P3's log-space normalisation is the
+    same function): each score depends on its own logit only, so
+        ds[t, idx_tj] = dq_j q_j (1 - q_j),  0 for experts not chosen.
     """
-    p = softmax(logits)
-    T, E = p.shape
+    s = np.asarray(logits, dtype=np.float64)
+    T, E = s.shape
     k = idx.shape[1]
+    if scoring == "sigmoid":
+        q = sigmoid(np.take_along_axis(s, idx, axis=1))
+        S = np.sum(q, axis=1, keepdims=True)
+        G = np.sum(gate * dgate, axis=1, keepdims=True)
+        dq = (dgate - G) / S
+        ds = np.zeros((T, E))
+        for j in range(k):
+            np.add.at(ds, (np.arange(T), idx[:, j]), dq[:, j] * q[:, j] * (1.0 - q[:, j]))
+        return ds
+    p = softmax(s)
     q = np.take_along_axis(p, idx, axis=1)
     S = np.sum(q, axis=1, keepdims=True)
     G = np.sum(gate * dgate, axis=1, keepdims=True)
@@ -544,7 +642,8 @@ def _mlp_backward(kind, w, e, xr, dO):
 
 
 def backward(dy, x, kind, weights, logits, idx, gate, kept, count, *, residual=True,
-             aux_grad_scale=0.0, shared=None, w_router=None):
+             aux_grad_scale=0.0, shared=None, w_router=None, scoring="softmax",
+             renormalize=False, z_grad_scale=0.0):
     """Backward of the whole layer for every expert kind, in float64, with the discrete
     choices (top-k set, kept mask) held constant (P1 section 2 moe_backward and trap 7,
     extended through the expert MLPs by the chain rule).
@@ -557,6 +656,13 @@ def backward(dy, x, kind, weights, logits, idx, gate, kept, count, *, residual=T
     parameter gradients and adds its input gradient to dx. With ``w_router`` (logits =
     x W_r) the router weights get dW_r = x^T dlogits and dx gets dlogits W_r^T; without
     it the logits are an independent input and dx has no router term.
+
+    P3's variants: ``scoring`` is the router's score function (see ``router_grad``);
+    with ``renormalize`` the experts see the survivor-renormalised gates g'_a = gate_a /
+    K_t (K_t the token's kept gate mass), so dgate' = <dy_t, o_a> is taken back to the
+    pre-drop gates by the quotient rule, dgate_a = (dgate'_a - sum_kept g'_r dgate'_r) /
+    K_t on kept a and 0 on dropped ones; ``z_grad_scale`` adds that multiple of the
+    router z-loss gradient to dlogits.
 
     Returns dgate, dlogits, dx, a dict ``dexperts`` of [E, ...] gradients named like the
     weights (w_in, w_up, w_out, b_in, b_out as the kind has them), ``dshared`` (or None)
@@ -571,13 +677,15 @@ def backward(dy, x, kind, weights, logits, idx, gate, kept, count, *, residual=T
     names = {"linear": ["w_in"], "gelu": ["w_in", "b_in", "w_out", "b_out"],
              "swiglu": ["w_in", "w_up", "w_out"]}[kind]
     dexp = {n: np.zeros(np.asarray(weights[n]).shape) for n in names}
+    kept = np.asarray(kept, dtype=bool)
+    geff = renormalise_kept(gate, kept) if renormalize else np.where(kept, _f64(gate), 0.0)
     for e in range(E):
         tt, jj = np.nonzero((idx == e) & kept)
         if tt.size == 0:
             continue
         o = expert_apply(kind, weights, e, x[tt])
         dgate[tt, jj] = np.sum(dy[tt] * o, axis=1)
-        dO = gate[tt, jj][:, None] * dy[tt]
+        dO = geff[tt, jj][:, None] * dy[tt]
         g, dxr = _mlp_backward(kind, weights, e, x[tt], dO)
         for n in names:
             dexp[n][e] = g[n]
@@ -588,9 +696,16 @@ def backward(dy, x, kind, weights, logits, idx, gate, kept, count, *, residual=T
                                0, x, dy)
         dshared = g
         dx = dx + dxr
-    dlogits = router_grad(logits, idx, gate, dgate)
+    if renormalize:
+        mass = np.sum(np.where(kept, _f64(gate), 0.0), axis=1, keepdims=True)
+        Gp = np.sum(geff * dgate, axis=1, keepdims=True)
+        dgate = np.where(kept & (mass > 0.0),
+                         (dgate - Gp) / np.where(mass > 0.0, mass, 1.0), 0.0)
+    dlogits = router_grad(logits, idx, gate, dgate, scoring)
     if aux_grad_scale:
         dlogits = dlogits + aux_grad_scale * aux_grad(logits, count, k)
+    if z_grad_scale:
+        dlogits = dlogits + z_grad_scale * z_loss_grad(logits)
     dw_router = None
     if w_router is not None:
         dw_router = x.T @ dlogits

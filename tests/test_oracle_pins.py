@@ -473,6 +473,158 @@ def test_mlp_backward_finite_differences(kind, shared, router, aux, residual):
         np.testing.assert_allclose(fd(lambda: s, lambda a: loss(x, w, sh, wr, a)), g["dlogits"], atol=2e-6)
 
 
+# ---------------------------------------------------------------------------------
+# P3 router variants: sigmoid scoring, selection bias, survivor renormalisation, z-loss
+# ---------------------------------------------------------------------------------
+
+def check_p3_sigmoid_router():
+    """Module 7, the asserts after router_z_loss: the REFERENCE router entry (sigmoid
+    scoring, top-4 of 8, with and without the selection bias; atol 1e-12 as printed) and
+    the extreme-logit cases (finite log-space gates)."""
+    ref = _load("p3_reference.json")["router"]
+    s = np.array([ref["logits"]])
+    base = om.route(s, 4, scoring="sigmoid")
+    assert base["idx"][0].tolist() == ref["selected"]
+    np.testing.assert_allclose(base["gate"][0], ref["gates"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(base["clean"][0], ref["scores"], rtol=0, atol=1e-15)
+    biased = om.route(s, 4, scoring="sigmoid", selection_bias=np.array(ref["bias"]))
+    assert biased["idx"][0].tolist() == ref["selected_with_bias"]
+    np.testing.assert_allclose(biased["gate"][0], ref["gates_with_bias"], rtol=0, atol=1e-12)
+    ext = om.route(np.array([[-1002.0, -1000.0, -1001.0]]), 2, scoring="sigmoid")
+    assert ext["idx"].tolist() == [[1, 2]]
+    assert np.all(np.isfinite(ext["gate"]))
+    np.testing.assert_allclose(ext["gate"], [[1 / (1 + np.exp(-1)), 1 / (1 + np.exp(1))]],
+                               rtol=0, atol=1e-15)
+    ext4 = om.route(np.array([[-1002.0, -1000.0, -1001.0, -1003.0]]), 2, scoring="sigmoid")
+    assert ext4["idx"].tolist() == [[1, 2]]
+
+
+def test_p3_sigmoid_router():
+    check_p3_sigmoid_router()
+
+
+def check_p3_renormalise_survivors():
+    """Module 7, REFERENCE capacity entry under its fifo_drop_then_renormalize_survivors
+    policy: every token keeps at least one choice, so its renormalised gates sum to 1;
+    and the all-same case (k = 1, cf = 0.5): tokens 1-3 fully dropped with zero gates."""
+    ref = _load("p3_reference.json")["capacity"]
+    assert ref["policy"] == "fifo_drop_then_renormalize_survivors"
+    s = np.array(ref["logits"])
+    r = om.route(s, 2)
+    C = om.capacity(12, 2, 4, 1.0)
+    d = om.dispatch(r["idx"], 4, C)
+    g = om.renormalise_kept(r["gate"], d["kept"])
+    assert C == ref["capacity_per_expert"]
+    assert d["used"].tolist() == ref["after_counts"]
+    np.testing.assert_allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(g[~d["kept"]] == 0.0)
+    r1 = om.route(np.tile([9.0, 0.0], (4, 1)), 1)
+    d1 = om.dispatch(r1["idx"], 2, om.capacity(4, 1, 2, 0.5))
+    g1 = om.renormalise_kept(r1["gate"], d1["kept"])
+    assert d1["kept"][:, 0].tolist() == [True, False, False, False]
+    assert g1[0, 0] == 1.0 and np.all(g1[1:] == 0.0)
+
+
+def test_p3_renormalise_survivors():
+    check_p3_renormalise_survivors()
+
+
+def check_p3_z_loss():
+    """Module 7: router_z_loss on the REFERENCE aux logits (rel 1e-12), and squaring per
+    token before the token mean (the two-token example and its wrong alternative)."""
+    ref = _load("p3_reference.json")["losses"]
+    z_ref = ref["z_loss"]
+    s = np.array(ref["aux_logits"])
+    assert math.isclose(om.z_loss(s), z_ref, rel_tol=1e-12)
+    assert math.isclose(om.route(s, 1)["z_loss"], z_ref, rel_tol=1e-12)
+    two = np.array([[0.0, 0.0], [2.0, 2.0]])
+    want = (math.log(2) ** 2 + (2 + math.log(2)) ** 2) / 2
+    assert math.isclose(om.z_loss(two), want, rel_tol=1e-12)
+    assert not math.isclose(om.z_loss(two), (1 + math.log(2)) ** 2)
+
+
+def test_p3_z_loss():
+    check_p3_z_loss()
+
+
+def test_z_loss_grad_fd():
+    """The z-loss gradient against central differences, and its closed-form row sum
+    (2/T) lse_t (the softmax row sums to 1)."""
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((6, 5)) * 2
+    h = 1e-6
+    fd = np.zeros_like(s)
+    for i in np.ndindex(s.shape):
+        a = s.copy(); a[i] += h; lp = om.z_loss(a)
+        a = s.copy(); a[i] -= h; lm = om.z_loss(a)
+        fd[i] = (lp - lm) / (2 * h)
+    g = om.z_loss_grad(s)
+    np.testing.assert_allclose(g, fd, atol=1e-8)
+    lse = scipy.special.logsumexp(s, axis=1)
+    np.testing.assert_allclose(g.sum(axis=1), 2.0 / s.shape[0] * lse, rtol=1e-12)
+
+
+def check_sigmoid_router_grad():
+    """Sigmoid-scored gates: router_grad against central differences of <w, gate>, the
+    top-k set held fixed; with k = 1 the gate is the constant 1, so the gradient is 0
+    (Module 7, the gradcheck and k = 1 asserts of the explicit router)."""
+    rng = np.random.default_rng(9)
+    T, E, k = 5, 6, 3
+    s = np.stack([rng.permutation(E) * 0.41 + rng.standard_normal() for _ in range(T)])
+    w = rng.standard_normal((T, k))
+    r = om.route(s, k, scoring="sigmoid")
+    g = om.router_grad(s, r["idx"], r["gate"], w, scoring="sigmoid")
+    h = 1e-6
+    fd = np.zeros_like(s)
+    for i in np.ndindex(s.shape):
+        a = s.copy(); a[i] += h; rp = om.route(a, k, scoring="sigmoid")
+        a = s.copy(); a[i] -= h; rm = om.route(a, k, scoring="sigmoid")
+        assert np.array_equal(rp["idx"], r["idx"]) and np.array_equal(rm["idx"], r["idx"])
+        fd[i] = (np.sum(w * rp["gate"]) - np.sum(w * rm["gate"])) / (2 * h)
+    np.testing.assert_allclose(g, fd, atol=1e-8)
+    r1 = om.route(s, 1, scoring="sigmoid")
+    assert np.all(r1["gate"] == 1.0)
+    assert np.all(om.router_grad(s, r1["idx"], r1["gate"], w[:, :1], scoring="sigmoid") == 0.0)
+
+
+def test_sigmoid_router_grad():
+    check_sigmoid_router_grad()
+
+
+@pytest.mark.parametrize("kind,scoring,renorm,zscale,bias", [
+    ("gelu", "sigmoid", False, 0.0, False), ("swiglu", "softmax", True, 0.0, False),
+    ("linear", "sigmoid", True, 0.7, True), ("gelu", "softmax", True, 0.3, True)])
+def test_router_variants_backward_fd(kind, scoring, renorm, zscale, bias):
+    """The whole-layer backward under P3's router variants against central differences
+    of <dy, y> + 0.5 aux + zscale * z_loss, the top-k set and kept mask constant."""
+    x, w, sh, wr, s, dy, k = _mlp_problem(kind, seed=23 + len(kind), with_shared=True)
+    E = w["w_in"].shape[0]
+    sb = np.array([0.05, -0.02, 0.03])[:E] if bias else None
+    C, aux = 3, 0.5
+    f = om.forward(x, k, kind, w, logits=s, C=C, shared=sh, scoring=scoring, selection_bias=sb,
+                   renormalize=renorm)
+    g = om.backward(dy, x, kind, w, f["logits"], f["idx"], f["gate"], f["kept"], f["count"],
+                    aux_grad_scale=aux, shared=sh, scoring=scoring, renormalize=renorm,
+                    z_grad_scale=zscale)
+    assert (~f["kept"]).any()
+    h = 1e-6
+
+    def loss(x_, s_):
+        ff = om.forward(x_, k, kind, w, logits=s_, C=C, shared=sh, scoring=scoring,
+                        selection_bias=sb, renormalize=renorm)
+        assert np.array_equal(ff["idx"], f["idx"]) and np.array_equal(ff["kept"], f["kept"])
+        return float(np.sum(dy * ff["y"]) + aux * ff["aux"] + zscale * ff["z_loss"])
+
+    for arr, want, put in ((s, g["dlogits"], lambda a: loss(x, a)),
+                           (x, g["dx"], lambda a: loss(a, s))):
+        fd = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            a = arr.copy(); a[i] += h; lp = put(a)
+            a = arr.copy(); a[i] -= h; lm = put(a)
+            fd[i] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(fd, want, atol=2e-6)
+
+
 def test_general_backward_matches_linear_backward():
     """For single-linear experts the general backward reduces to backward_linear."""
     x, W, s, dy, k, C = _fd_problem(C=2)
@@ -623,7 +775,41 @@ def _capacity_floor(T, k, E, cf):
     return int(math.floor(cf * T * k / E))
 
 
+def _route_gates_with_bias(logits, k, *, scoring="softmax", selection_bias=None):
+    r = _ORIG_ROUTE(logits, k, scoring=scoring, selection_bias=selection_bias)
+    if selection_bias is not None:       # the bias leaks into the mixture weights
+        q = np.take_along_axis(r["clean"] + np.asarray(selection_bias)[None, :], r["idx"], axis=1)
+        r["gate"] = q / q.sum(axis=1, keepdims=True)
+    return r
+
+
+def _z_loss_square_after_mean(logits):
+    s = np.asarray(logits, dtype=np.float64)
+    return float(np.mean(scipy.special.logsumexp(s, axis=1)) ** 2)
+
+
+def _renorm_over_all_choices(gate, kept):
+    g = np.where(kept, gate, 0.0)
+    return g / np.sum(gate, axis=1, keepdims=True)
+
+
+def _sigmoid_grad_no_derivative(logits, idx, gate, dgate, scoring="softmax"):
+    if scoring != "sigmoid":
+        return _ORIG_ROUTER_GRAD(logits, idx, gate, dgate, scoring)
+    q = om.sigmoid(np.take_along_axis(logits, idx, axis=1))
+    dq = (dgate - np.sum(gate * dgate, axis=1, keepdims=True)) / q.sum(axis=1, keepdims=True)
+    ds = np.zeros(np.shape(logits))
+    for j in range(idx.shape[1]):
+        np.add.at(ds, (np.arange(idx.shape[0]), idx[:, j]), dq[:, j] * q[:, j])   # (1 - q) dropped
+    return ds
+
+
+def _sigmoid_flipped(s):
+    return 1.0 / (1.0 + np.exp(np.asarray(s, dtype=np.float64)))
+
+
 _ORIG_ROUTE = om.route
+_ORIG_ROUTER_GRAD = om.router_grad
 
 MUTATIONS = [
     ("top_k", _tie_to_higher, lambda: (check_p2_examples(), check_p3_tie_break())),
@@ -632,6 +818,11 @@ MUTATIONS = [
     ("route", _route_no_renorm, check_p2_examples),
     ("router_grad", _router_grad_no_centering, lambda: check_backward_fd(True, 0.0, 2)),
     ("capacity", _capacity_floor, check_capacity),
+    ("route", _route_gates_with_bias, check_p3_sigmoid_router),
+    ("z_loss", _z_loss_square_after_mean, check_p3_z_loss),
+    ("renormalise_kept", _renorm_over_all_choices, check_p3_renormalise_survivors),
+    ("router_grad", _sigmoid_grad_no_derivative, check_sigmoid_router_grad),
+    ("sigmoid", _sigmoid_flipped, check_p3_sigmoid_router),
 ]
 
 
