@@ -93,6 +93,33 @@ typedef struct {
   const void* b_out;    /* GELU b2 (may be NULL = no bias), else NULL               */
 } moe_experts_t;
 
+/*
+ * Router variants of "Module 7. Mixture of Experts" (route_logits, dispatch_with_capacity,
+ * router_z_loss). The all-zero struct (or a NULL pointer where one is taken) is the
+ * default softmax router of the other pages.
+ *   scoring          MOE_SCORE_SOFTMAX: gates p[idx] / sum over the k of p[idx].
+ *                    MOE_SCORE_SIGMOID: gates sigmoid(s[idx]) / sum over the k of
+ *                    sigmoid(s[idx]), evaluated as a softmax of log sigmoid(s) over the k
+ *                    chosen experts (finite for any finite logits).
+ *   selection_bias   device [E] fp32 or NULL. When given, experts are chosen by the
+ *                    fp32 value clean + bias[e] (clean = p or sigmoid(s)), ties to the
+ *                    lower index; the gates still come from the clean scores only.
+ *                    NULL: chosen by logit.
+ *   renormalize_kept 1: after the capacity drop the kept gates of a token are divided
+ *                    by their sum (a token with nothing kept gets no expert term).
+ *                    Used by moe_forward's combine and by moe_backward.
+ *   z_loss           device [1] fp32 or NULL: mean over tokens of (log sum_e exp s)^2.
+ * The aux loss keeps P_e = mean softmax probability and the counts of the selection
+ * actually made under every variant.
+ */
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring_t;
+typedef struct {
+  int32_t scoring;
+  const float* selection_bias;
+  int32_t renormalize_kept;
+  float* z_loss;
+} moe_router_opts_t;
+
 /* Library version string, e.g. "moe-gfx950 0.1". */
 const char* moe_version(void);
 
@@ -120,6 +147,8 @@ int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double capacity_factor);
  *   expert_count device, [E] int32: choices per expert before any drop.
  *   prob_sum  device, [E] fp32: sum over tokens of p[t, e].
  *   aux_loss  device, [1] fp32: E * sum_e (count_e / (T k)) * (prob_sum_e / T).
+ *   opts      host pointer to router options, or NULL for the defaults above
+ *             (scoring, selection bias and the z-loss output apply here).
  *   ws        device workspace of at least moe_route_workspace_size(T, E) bytes.
  * Non-finite logits violate the precondition; results are then undefined.
  */
@@ -127,8 +156,8 @@ size_t moe_route_workspace_size(int32_t T, int32_t E);
 moe_status_t moe_route(const void* x, int32_t x_dtype, int64_t ldx, const void* w_router,
                        float* logits, int32_t T, int32_t D, int32_t E, int32_t k,
                        int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
-                       float* prob_sum, float* aux_loss, void* ws, size_t ws_bytes,
-                       void* stream);
+                       float* prob_sum, float* aux_loss, const moe_router_opts_t* opts,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Position-priority dispatch ("Sparse MoE Layer in NumPy", trap 3 and
@@ -173,7 +202,9 @@ moe_status_t moe_expert_mlp(const moe_experts_t* ex, const void* x, int64_t ldx,
  * equation; "32. Sparse MoE Token Dispatch & Combine", step 6):
  *   y[t] = residual[t] + shared_out[t] + sum_{j = 0..k-1, slot[t,j] >= 0}
  *          topk_gate[t,j] * expert_out[topk_idx[t,j], slot[t,j]]
- * accumulated in fp32 in exactly that order, rounded once to dt.
+ * accumulated in fp32 in exactly that order, rounded once to dt. With
+ * renormalize_kept = 1 each kept gate is first divided by the token's kept gate sum
+ * ("Module 7. Mixture of Experts", dispatch_with_capacity, renormalize_kept_gates).
  *   residual, shared_out  device, [T, D] of dt, each may be NULL (term omitted).
  *   expert_out            device, [E, C, D] of dt.
  * Precondition: 0 <= topk_idx < E and slot < C (violations are skipped).
@@ -181,7 +212,8 @@ moe_status_t moe_expert_mlp(const moe_experts_t* ex, const void* x, int64_t ldx,
 moe_status_t moe_combine(int32_t dt, const void* residual, const void* shared_out,
                          const void* expert_out, const int32_t* topk_idx,
                          const int32_t* slot, const float* topk_gate, int32_t T,
-                         int32_t k, int32_t E, int32_t C, int32_t D, void* y, void* stream);
+                         int32_t k, int32_t E, int32_t C, int32_t D,
+                         int32_t renormalize_kept, void* y, void* stream);
 
 /* The whole forward pass in one call: routing, dispatch, experts, shared expert,
  * combine and aux loss, all enqueued on one stream with no host synchronisation. */
@@ -212,6 +244,7 @@ typedef struct {
   void* expert_out;         /* [E, C, D], kept for the backward                       */
   void* shared_out;         /* [T, D] or NULL (then kept in the workspace)            */
   void* y;                  /* [T, D]   */
+  moe_router_opts_t router; /* router variants; all zero = the default softmax router  */
 } moe_forward_args_t;
 
 size_t moe_forward_workspace_size(const moe_forward_args_t* a);
@@ -224,11 +257,16 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
  * SwiGLU expert MLPs of "Module 7" / llm-atlas "Mixture of Experts", Expert), with the
  * discrete choices (top-k set, kept mask) held constant. For a kept assignment
  * a = (t, j) -> e with expert output o_a (ungated, from the forward) the expert's output
- * gradient is dO_a = gate_a dy_t, and
- *   dgate[a]  = kept_a <dy_t, o_a>
- *   dlogits   = p * (dp - <p, dp>), dp[t, idx_tj] = (dgate_tj - sum_r g_tr dgate_tr) / S_t,
- *               S_t = sum_r p[t, idx_tr]; plus aux_grad_scale * (E/T) p (f - <p, f>),
- *               f_e = count_e / (T k)
+ * gradient is dO_a = g'_a dy_t, g' the effective gate (topk_gate, or with
+ * router.renormalize_kept topk_gate / K_t, K_t the token's kept gate sum), and
+ *   dgate[a]  = kept_a <dy_t, o_a> (the gradient of topk_gate; with renormalize_kept
+ *               taken through the survivor quotient: (d'_a - sum_kept g'_r d'_r) / K_t,
+ *               d' = <dy_t, o_a>, 0 for dropped a)
+ *   dlogits   = softmax scoring: p * (dp - <p, dp>), dp[t, idx_tj] = dq_tj,
+ *               dq_tj = (dgate_tj - sum_r g_tr dgate_tr) / S_t, S_t = sum_r q_tr over the
+ *               chosen clean scores q (p or sigmoid(s)); sigmoid scoring: dq_tj q_tj
+ *               (1 - q_tj) at the chosen experts, 0 elsewhere; plus aux_grad_scale (E/T)
+ *               p (f - <p, f>), f_e = count_e / (T k); plus z_grad_scale (2/T) lse_t p
  *   expert parameter gradients = sums over the expert's kept rows of the MLP's chain
  *               rule with input x_t and output gradient dO_a (LINEAR: dW = x^T dO;
  *               GELU_MLP: Z = x W_in + b_in, dZ = (dO W_out^T) gelu'(Z), dW_in = x^T dZ,
@@ -282,6 +320,10 @@ typedef struct {
   /* router weights, or NULL (see dx above); E must be a multiple of 4 */
   const void* w_router;     /* [D, E] */
   void* dw_router;          /* [D, E] */
+  /* the forward's router variant (scoring and renormalize_kept are used; the
+   * selection is the given topk_idx) and the weight of the z-loss in the loss */
+  moe_router_opts_t router;
+  float z_grad_scale;
 } moe_backward_args_t;
 
 size_t moe_backward_workspace_size(const moe_backward_args_t* a);

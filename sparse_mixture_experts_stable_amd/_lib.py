@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_EXPERT_LINEAR, MOE_EXPERT_GELU_MLP, MOE_EXPERT_SWIGLU = 0, 1, 2
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 
 EXPORTED = [
     "moe_version", "moe_status_string", "moe_capacity",
@@ -45,6 +46,11 @@ class Experts(ctypes.Structure):
                 ("b_out", vp)]
 
 
+class RouterOpts(ctypes.Structure):
+    _fields_ = [("scoring", i32), ("selection_bias", vp), ("renormalize_kept", i32),
+                ("z_loss", vp)]
+
+
 class ForwardArgs(ctypes.Structure):
     _fields_ = [("x", vp), ("ldx", i64), ("T", i32), ("w_router", vp), ("logits", vp),
                 ("experts", Experts), ("shared", Experts), ("k", i32), ("capacity", i32),
@@ -52,7 +58,7 @@ class ForwardArgs(ctypes.Structure):
                 ("expert_count", vp), ("prob_sum", vp), ("aux_loss", vp), ("slot", vp),
                 ("kept", vp), ("slot_assign", vp), ("expert_used", vp),
                 ("expert_overflow", vp), ("token_drops", vp), ("hidden_cache", vp),
-                ("expert_out", vp), ("shared_out", vp), ("y", vp)]
+                ("expert_out", vp), ("shared_out", vp), ("y", vp), ("router", RouterOpts)]
 
 
 class BackwardArgs(ctypes.Structure):
@@ -63,7 +69,8 @@ class BackwardArgs(ctypes.Structure):
                 ("expert_out", vp), ("dx", vp), ("dW", vp), ("dgate", vp), ("dlogits", vp),
                 ("dW_up", vp), ("dW_out", vp), ("db_in", vp), ("db_out", vp),
                 ("shared", Experts), ("dshared_w_in", vp), ("dshared_w_up", vp),
-                ("dshared_w_out", vp), ("w_router", vp), ("dw_router", vp)]
+                ("dshared_w_out", vp), ("w_router", vp), ("dw_router", vp),
+                ("router", RouterOpts), ("z_grad_scale", f32)]
 
 
 _lib = None
@@ -79,7 +86,8 @@ def _declare(L):
     L.moe_route_workspace_size.restype = sz
     L.moe_route_workspace_size.argtypes = [i32, i32]
     L.moe_route.restype = i32
-    L.moe_route.argtypes = [vp, i32, i64, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route.argtypes = [vp, i32, i64, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                            P(RouterOpts), vp, sz, vp]
     L.moe_dispatch_workspace_size.restype = sz
     L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32]
     L.moe_dispatch.restype = i32
@@ -89,7 +97,7 @@ def _declare(L):
     L.moe_expert_mlp.restype = i32
     L.moe_expert_mlp.argtypes = [P(Experts), vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.moe_combine.restype = i32
-    L.moe_combine.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    L.moe_combine.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     L.moe_forward_workspace_size.restype = sz
     L.moe_forward_workspace_size.argtypes = [P(ForwardArgs)]
     L.moe_forward.restype = i32

@@ -288,6 +288,18 @@ moe_status_t router_gemm(const void* x, int dt, int64_t ldx, const void* w, int 
   return launch_router_simt(x, dt, ldx, w, T, D, E, logits, s);
 }
 
+bool opts_ok(const moe_router_opts_t* o) {
+  return !o || o->scoring == MOE_SCORE_SOFTMAX || o->scoring == MOE_SCORE_SIGMOID;
+}
+
+RouteOpts route_opts(const moe_router_opts_t* o) {
+  RouteOpts r{};
+  r.scoring = o ? o->scoring : MOE_SCORE_SOFTMAX;
+  r.bias = o ? o->selection_bias : nullptr;
+  r.with_z = (o && o->z_loss) ? 1 : 0;
+  return r;
+}
+
 bool route_shape_ok(int T, int E, int k) {
   return T >= 1 && E >= 1 && E <= 1024 && k >= 1 && k <= E;
 }
@@ -388,8 +400,8 @@ size_t moe_route_workspace_size(int32_t T, int32_t E) {
 moe_status_t moe_route(const void* x, int32_t x_dtype, int64_t ldx, const void* w_router,
                        float* logits, int32_t T, int32_t D, int32_t E, int32_t k,
                        int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
-                       float* prob_sum, float* aux_loss, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       float* prob_sum, float* aux_loss, const moe_router_opts_t* opts,
+                       void* ws, size_t ws_bytes, void* stream) {
   if (!route_shape_ok(T, E, k)) return k > 256 && k <= E ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG;
   if (k > 256) return MOE_ERR_UNSUPPORTED;
   if (!logits || !topk_idx || !topk_gate || !expert_count || !prob_sum || !aux_loss || !ws)
@@ -397,6 +409,7 @@ moe_status_t moe_route(const void* x, int32_t x_dtype, int64_t ldx, const void* 
   if (w_router) {
     if (!x || !valid_dtype(x_dtype) || D < 1 || ldx < D) return MOE_ERR_INVALID_ARG;
   }
+  if (!opts_ok(opts)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe_route_workspace_size(T, E)) return MOE_ERR_WORKSPACE;
   hipStream_t s = S(stream);
   RouteWs w = carve_route_ws(ws, T, E);
@@ -405,10 +418,10 @@ moe_status_t moe_route(const void* x, int32_t x_dtype, int64_t ldx, const void* 
     st = router_gemm(x, x_dtype, ldx, w_router, T, D, E, logits, s);
     if (st != MOE_OK) return st;
   }
-  st = launch_route(logits, T, E, k, topk_idx, topk_gate, w, s);
+  st = launch_route(logits, T, E, k, topk_idx, topk_gate, route_opts(opts), w, s);
   if (st != MOE_OK) return st;
   return launch_reduce_scan(T, k, E, -1, true, expert_count, prob_sum, aux_loss, nullptr, nullptr,
-                            nullptr, w, s);
+                            nullptr, opts ? opts->z_loss : nullptr, w, s);
 }
 
 size_t moe_dispatch_workspace_size(int32_t T, int32_t k, int32_t E) {
@@ -432,7 +445,7 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t
   if (st != MOE_OK) return st;
   // expert_count is not an output of moe_dispatch; the totals land in fp scratch space
   st = launch_reduce_scan(T, k, E, C, false, reinterpret_cast<int32_t*>(w.fp), nullptr, nullptr,
-                          expert_used, expert_overflow, slot_assign, w, s);
+                          expert_used, expert_overflow, slot_assign, nullptr, w, s);
   if (st != MOE_OK) return st;
   return launch_assign(topk_idx, T, k, E, C, slot, kept, slot_assign, token_drops, expert_used,
                        w, s);
@@ -470,7 +483,7 @@ moe_status_t moe_expert_mlp(const moe_experts_t* ex, const void* x, int64_t ldx,
 moe_status_t moe_combine(int32_t dt, const void* residual, const void* shared_out,
                          const void* expert_out, const int32_t* topk_idx, const int32_t* slot,
                          const float* topk_gate, int32_t T, int32_t k, int32_t E, int32_t C,
-                         int32_t D, void* y, void* stream) {
+                         int32_t D, int32_t renormalize_kept, void* y, void* stream) {
   if (!valid_dtype(dt) || T < 1 || k < 1 || E < 1 || C < 0 || D < 1) return MOE_ERR_INVALID_ARG;
   if (!topk_idx || !slot || !topk_gate || !y || (C > 0 && !expert_out)) return MOE_ERR_INVALID_ARG;
   const int V = dt == MOE_BF16 ? 8 : 4;
@@ -478,7 +491,7 @@ moe_status_t moe_combine(int32_t dt, const void* residual, const void* shared_ou
   if (D % V || (per_row > 256 && per_row % 256) || (per_row < 256 && 256 % per_row))
     return MOE_ERR_UNSUPPORTED;
   return launch_combine(dt, residual, D, shared_out, expert_out, topk_idx, slot, topk_gate, T, k,
-                        E, C, D, y, S(stream));
+                        E, C, D, renormalize_kept ? 1 : 0, y, S(stream));
 }
 
 // ---- forward ------------------------------------------------------------------------
@@ -525,7 +538,7 @@ moe_status_t check_forward(const moe_forward_args_t* a) {
   if (st != MOE_OK) return st;
   const int T = a->T, E = a->experts.num_experts, k = a->k, C = a->capacity;
   const int D = a->experts.d_model;
-  if (!route_shape_ok(T, E, k) || C < 0) return MOE_ERR_INVALID_ARG;
+  if (!route_shape_ok(T, E, k) || C < 0 || !opts_ok(&a->router)) return MOE_ERR_INVALID_ARG;
   if (k > 256 || int64_t(T) * k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (!a->x || a->ldx < D || !a->logits || !a->y) return MOE_ERR_INVALID_ARG;
   if (!a->topk_idx || !a->topk_gate || !a->expert_count || !a->prob_sum || !a->aux_loss ||
@@ -564,10 +577,12 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
     st = router_gemm(a->x, a->experts.dtype, a->ldx, a->w_router, T, D, E, a->logits, s);
     if (st != MOE_OK) return st;
   }
-  st = launch_route(a->logits, T, E, k, a->topk_idx, a->topk_gate, f.rw, s);
+  st = launch_route(a->logits, T, E, k, a->topk_idx, a->topk_gate, route_opts(&a->router), f.rw,
+                    s);
   if (st != MOE_OK) return st;
   st = launch_reduce_scan(T, k, E, C, true, a->expert_count, a->prob_sum, a->aux_loss,
-                          a->expert_used, a->expert_overflow, a->slot_assign, f.rw, s);
+                          a->expert_used, a->expert_overflow, a->slot_assign, a->router.z_loss,
+                          f.rw, s);
   if (st != MOE_OK) return st;
   st = launch_assign(a->topk_idx, T, k, E, C, a->slot, a->kept, a->slot_assign, a->token_drops,
                      a->expert_used, f.rw, s);
@@ -593,8 +608,8 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
     if (st != MOE_OK) return st;
   }
   return launch_combine(a->experts.dtype, a->use_residual ? a->x : nullptr, a->ldx, shared_out,
-                        a->expert_out, a->topk_idx, a->slot, a->topk_gate, T, k, E, C, D, a->y,
-                        s);
+                        a->expert_out, a->topk_idx, a->slot, a->topk_gate, T, k, E, C, D,
+                        a->router.renormalize_kept ? 1 : 0, a->y, s);
 }
 
 // ---- backward -----------------------------------------------------------------------
@@ -629,6 +644,7 @@ struct BwdSet {
 };
 
 struct BwdWs {
+  float* eff_gate;           // [T, k] survivor-renormalised gates (renormalize_kept only)
   float* dxe;
   float *h, *g, *u;
   float *sh_h, *sh_g, *sh_u, *sh_dx;
@@ -648,6 +664,7 @@ BwdWs carve_bwd(const moe_backward_args_t* a, void* ws) {
   const moe_experts_t& ex = a->experts;
   const size_t E = ex.num_experts, C = a->capacity, D = ex.d_model, F = ex.d_hidden;
   const size_t T = a->T;
+  if (a->router.renormalize_kept) w.eff_gate = take(T * size_t(a->k));
   w.dxe = take(E * C * D);
   if (ex.kind != MOE_EXPERT_LINEAR) {
     w.h = take(E * C * F);
@@ -828,7 +845,7 @@ moe_status_t check_backward(const moe_backward_args_t* a) {
   if (ex.dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   const int T = a->T, E = ex.num_experts, k = a->k, C = a->capacity;
   const int D = ex.d_model;
-  if (!route_shape_ok(T, E, k) || C < 0) return MOE_ERR_INVALID_ARG;
+  if (!route_shape_ok(T, E, k) || C < 0 || !opts_ok(&a->router)) return MOE_ERR_INVALID_ARG;
   if (k > 256 || int64_t(T) * k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (!a->dy || !a->x || a->ld < D || !a->logits || !a->topk_idx || !a->topk_gate ||
       !a->expert_count || !a->slot || !a->expert_used || !a->dx || !a->dW || !a->dgate ||
@@ -874,10 +891,30 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
   const float* x = static_cast<const float*>(a->x);
   BwdWs w = carve_bwd(a, ws);
 
-  st = launch_dgate_router_bwd(dy, static_cast<const float*>(a->expert_out), a->logits,
-                               a->topk_idx, a->topk_gate, a->slot, a->expert_count, T, k, E, C,
-                               D, a->aux_grad_scale, a->dgate, a->dlogits, s);
+  DgateArgs da{};
+  da.dy = dy;
+  da.o = static_cast<const float*>(a->expert_out);
+  da.logits = a->logits;
+  da.idx = a->topk_idx;
+  da.gate = a->topk_gate;
+  da.slot = a->slot;
+  da.count = a->expert_count;
+  da.T = T;
+  da.k = k;
+  da.E = E;
+  da.C = C;
+  da.D = D;
+  da.aux_scale = a->aux_grad_scale;
+  da.z_scale = a->z_grad_scale;
+  da.scoring = a->router.scoring;
+  da.renorm = a->router.renormalize_kept ? 1 : 0;
+  da.dgate = a->dgate;
+  da.dlogits = a->dlogits;
+  da.eff_gate = w.eff_gate;
+  st = launch_dgate_router_bwd(da, s);
   if (st != MOE_OK) return st;
+  // the gates the experts saw in the forward
+  const float* gate_eff = w.eff_gate ? w.eff_gate : a->topk_gate;
 
   // with C == 0 no row is kept: every weight gradient is zero (K = 0 products)
   const int32_t* used = C > 0 ? a->expert_used : nullptr;
@@ -919,7 +956,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
     pw.B = dy;
     pw.ldb = a->ld;
     pw.b_row_map = a->slot_assign;
-    pw.gate = a->topk_gate;
+    pw.gate = gate_eff;
     pw.N = D;
     pw.groups = E;
     pw.epi = EPI_STORE;
@@ -937,7 +974,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
     r.row_div = k;
     r.count = used;
     r.cnt_const = 0;
-    r.gate = a->topk_gate;
+    r.gate = gate_eff;
     r.dw_in = static_cast<float*>(a->dW);
     r.dw_up = static_cast<float*>(a->dW_up);
     r.dw_out = static_cast<float*>(a->dW_out);
@@ -972,8 +1009,8 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
   // dx = r dy + shared input gradient + sum over kept choices of the routed rows'
   // input gradients (gated here for single-linear experts, already gated for MLPs)
   st = launch_combine(MOE_F32, a->use_residual ? a->dy : nullptr, a->ld, w.sh_dx, w.dxe,
-                      a->topk_idx, a->slot, ex.kind == MOE_EXPERT_LINEAR ? a->topk_gate : nullptr,
-                      T, k, E, C, D, a->dx, s);
+                      a->topk_idx, a->slot, ex.kind == MOE_EXPERT_LINEAR ? gate_eff : nullptr,
+                      T, k, E, C, D, 0, a->dx, s);
   if (st != MOE_OK) return st;
 
   if (a->w_router) {

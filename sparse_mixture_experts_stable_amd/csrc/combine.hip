@@ -13,6 +13,10 @@
 //   dq_j = (dgate_j - sum_r g_r dgate_r) / S_t,  S_t = sum_r p[t, e_tr]
 //   dlogits[t, i] = p_i (dp_i - sum_l p_l dp_l), dp[t, e_tj] = dq_j
 //   (+ aux_scale * (E / T) p_i (f_i - sum_l f_l p_l), f = count / (T k))
+// with the variants of "Module 7. Mixture of Experts": sigmoid scores (S_t sums the
+// chosen sigmoid(s), and dlogits[t, e_tj] = dq_j q_j (1 - q_j) without the softmax
+// coupling), survivor renormalisation (dgate through the quotient by the kept gate
+// mass) and the z-loss term z_scale (2 / T) lse_t p_i.
 
 #include "internal.h"
 
@@ -71,7 +75,9 @@ struct Vec<bf16_t> {
 // gate) triples, then all its row loads at once (kept packed until used), then the
 // fused multiply-adds in choice order, so a token costs ceil(k / KB) dependent round
 // trips instead of k. gate == NULL weights every choice by 1 (exact: fma(1, v, acc) is
-// acc + v), for expert rows that already carry their gate. A dropped choice is skipped (not added as zero), so a fully
+// acc + v), for expert rows that already carry their gate. With renorm each kept gate
+// is divided by the token's kept gate sum ("Module 7. Mixture of Experts",
+// dispatch_with_capacity with renormalize_kept_gates). A dropped choice is skipped (not added as zero), so a fully
 // dropped token keeps y == residual bit for bit, signed zeros included.
 template <typename T, int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ residual,
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
                                                       const int32_t* __restrict__ slot,
                                                       const float* __restrict__ gate, int T_,
                                                       int k, int E, int C, int D, int64_t ldr,
-                                                      T* __restrict__ y) {
+                                                      int renorm, T* __restrict__ y) {
   constexpr int V = Vec<T>::N;
   const int per_row = D / V;
   int t, col;
@@ -109,6 +115,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] += v[i];
   }
+  // survivor renormalisation: the token's kept gate mass
+  float K = 1.0f;
+  if (renorm) {
+    K = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[size_t(t) * k + j];
+      const int sl = slot[size_t(t) * k + j];
+      if (sl >= 0 && sl < C && e >= 0 && e < E) K += gate[size_t(t) * k + j];
+    }
+  }
   for (int j0 = 0; j0 < k; j0 += KB) {
     int off[KB];
     float g[KB];
@@ -123,6 +139,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
         if (sl >= 0 && sl < C && e >= 0 && e < E) {
           off[b] = e * C + sl;
           g[b] = gate ? gate[size_t(t) * k + j] : 1.0f;
+          if (renorm) g[b] = g[b] / K;
         }
       }
     }
@@ -139,8 +156,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
 
 moe_status_t launch_combine(int dt, const void* residual, int64_t ldr, const void* shared_out,
                             const void* expert_out, const int32_t* idx, const int32_t* slot,
-                            const float* gate, int T, int k, int E, int C, int D, void* y,
-                            hipStream_t s) {
+                            const float* gate, int T, int k, int E, int C, int D, int renorm,
+                            void* y, hipStream_t s) {
   const int V = dt == MOE_BF16 ? 8 : 4;
   const int per_row = D / V;
   int blocks;
@@ -154,28 +171,31 @@ moe_status_t launch_combine(int dt, const void* residual, int64_t ldr, const voi
     MOE_LAUNCH("combine", (combine_kernel<bf16_t, 4>), dim3(blocks), dim3(256), 0, s,
                static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(shared_out),
                static_cast<const bf16_t*>(expert_out), idx, slot, gate, T, k, E, C, D,
-               ldr, static_cast<bf16_t*>(y));
+               ldr, renorm && gate ? 1 : 0, static_cast<bf16_t*>(y));
   } else {
     MOE_LAUNCH("combine", (combine_kernel<float, 4>), dim3(blocks), dim3(256), 0, s,
                static_cast<const float*>(residual), static_cast<const float*>(shared_out),
                static_cast<const float*>(expert_out), idx, slot, gate, T, k, E, C, D,
-               ldr, static_cast<float*>(y));
+               ldr, renorm && gate ? 1 : 0, static_cast<float*>(y));
   }
   return MOE_OK;
 }
 
 // One wavefront per token (4 tokens per block). EPL = experts per lane (E <= 64*EPL).
+// Three passes over the token's k choices: d'_j = kept <dy, o_j> (with the kept gate
+// mass K and sum_kept g_j d'_j), then dgate_j (d'_j, or with survivor renormalisation
+// its quotient-rule image (d'_j - sum_kept g'_r d'_r) / K) with G = sum_j g_j dgate_j,
+// then dq_j = (dgate_j - G) / S into the score derivative (softmax Jacobian, or
+// q (1 - q) of the chosen sigmoid scores). Aux and z-loss terms are added per expert.
 template <int EPL>
-__global__ __launch_bounds__(256) void dgate_router_kernel(
-    const float* __restrict__ dy, const float* __restrict__ o, const float* __restrict__ logits,
-    const int32_t* __restrict__ idx, const float* __restrict__ gate,
-    const int32_t* __restrict__ slot, const int32_t* __restrict__ count, int T, int k, int E,
-    int C, int D, float aux_scale, float* __restrict__ dgate, float* __restrict__ dlogits) {
+__global__ __launch_bounds__(256) void dgate_router_kernel(DgateArgs A) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  if (t >= A.T) return;
+  const int k = A.k, E = A.E, C = A.C, D = A.D;
+  const bool sig = A.scoring == MOE_SCORE_SIGMOID;
   // softmax row
-  const float* row = logits + size_t(t) * E;
+  const float* row = A.logits + size_t(t) * E;
   float s[EPL], p[EPL], dp[EPL];
   float mx = -INFINITY;
 #pragma unroll
@@ -198,17 +218,21 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(
 #pragma unroll
   for (int i = 0; i < EPL; ++i) p[i] *= inv;
 
-  // dgate_j, S_t, G_t = sum_r g_r dgate_r. dgate_j is kept in lane (j % 64), register
-  // slot j / 64 (k <= 256).
-  const float* dyr = dy + size_t(t) * D;
-  float S = 0.f, G = 0.f;
+  // pass 1: d'_j kept in lane (j % 64), register slot j / 64 (k <= 256); S over the
+  // chosen clean scores; K and sum_kept g d' for the survivor quotient
+  const float* dyr = A.dy + size_t(t) * D;
+  const int32_t* idr = A.idx + size_t(t) * k;
+  const int32_t* slr = A.slot + size_t(t) * k;
+  const float* gr = A.gate + size_t(t) * k;
+  float S = 0.f, K = 0.f, Gk = 0.f;
   float dreg[4] = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
-    const int e = idx[size_t(t) * k + j];
-    const int sl = slot[size_t(t) * k + j];
+    const int e = idr[j];
+    const int sl = slr[j];
+    const bool kept = sl >= 0 && sl < C;
     float d = 0.f;
-    if (sl >= 0 && sl < C) {
-      const float* orow = o + (size_t(e) * C + sl) * D;
+    if (kept) {
+      const float* orow = A.o + (size_t(e) * C + sl) * D;
       for (int c = lane * 4; c < D; c += 256) {
         const float4 a = *reinterpret_cast<const float4*>(dyr + c);
         const float4 b = *reinterpret_cast<const float4*>(orow + c);
@@ -218,22 +242,45 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(
         d = fmaf(a.w, b.w, d);
       }
       d = wave_sum(d);
+      K += gr[j];
+      Gk += gr[j] * d;
     }
-    if (lane == 0) dgate[size_t(t) * k + j] = d;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (lane == (j & 63) && r == (j >> 6)) dreg[r] = d;
-    float pe = 0.f;
+    float q = 0.f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (i == (e >> 6)) pe = p[i];
-    pe = __shfl(pe, e & 63, kWave);
-    S += pe;
-    G += gate[size_t(t) * k + j] * d;
+      if (i == (e >> 6)) q = sig ? s[i] : p[i];
+    q = __shfl(q, e & 63, kWave);
+    if (sig) q = 1.0f / (1.0f + __expf(-q));
+    S += q;
   }
-  // dp at the selected experts
+  // pass 2: dgate_j and G = sum_j g_j dgate_j; effective gates
+  float G = 0.f;
   for (int j = 0; j < k; ++j) {
-    const int e = idx[size_t(t) * k + j];
+    float dv = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r == (j >> 6)) dv = dreg[r];
+    float d = __shfl(dv, j & 63, kWave);
+    const int sl = slr[j];
+    const bool kept = sl >= 0 && sl < C;
+    const float g = gr[j];
+    if (A.renorm) d = (kept && K > 0.f) ? (d - Gk / K) / K : 0.f;
+    G += g * d;
+    if (lane == 0) {
+      A.dgate[size_t(t) * k + j] = d;
+      if (A.eff_gate)
+        A.eff_gate[size_t(t) * k + j] = kept ? (A.renorm ? (K > 0.f ? g / K : 0.f) : g) : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (lane == (j & 63) && r == (j >> 6)) dreg[r] = d;
+  }
+  // pass 3: dq_j into the score derivative at the chosen experts
+  for (int j = 0; j < k; ++j) {
+    const int e = idr[j];
     float dv = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -241,53 +288,58 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(
     const float d = __shfl(dv, j & 63, kWave);
     const float dq = (d - G) / S;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + 64 * i == e) dp[i] += dq;
+    for (int i = 0; i < EPL; ++i) {
+      if (lane + 64 * i == e) {
+        if (sig) {
+          const float q = 1.0f / (1.0f + __expf(-s[i]));
+          dp[i] += dq * q * (1.0f - q);
+        } else {
+          dp[i] += dq;
+        }
+      }
+    }
   }
   float pdp = 0.f;
+  if (!sig) {
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) pdp += p[i] * dp[i];
-  pdp = wave_sum(pdp);
+    for (int i = 0; i < EPL; ++i) pdp += p[i] * dp[i];
+    pdp = wave_sum(pdp);
+  }
   float pf = 0.f;
   float f[EPL];
-  if (aux_scale != 0.f) {
-    const float inv_tk = 1.0f / (float(T) * float(k));
+  if (A.aux_scale != 0.f) {
+    const float inv_tk = 1.0f / (float(A.T) * float(k));
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      f[i] = e < E ? float(count[e]) * inv_tk : 0.f;
+      f[i] = e < E ? float(A.count[e]) * inv_tk : 0.f;
       pf += p[i] * f[i];
     }
     pf = wave_sum(pf);
   }
+  const float zc = A.z_scale != 0.f ? A.z_scale * (2.0f / float(A.T)) * (mx + __logf(sum)) : 0.f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
     if (e >= E) continue;
-    float v = p[i] * (dp[i] - pdp);
-    if (aux_scale != 0.f) v += aux_scale * (float(E) / float(T)) * p[i] * (f[i] - pf);
-    dlogits[size_t(t) * E + e] = v;
+    float v = sig ? dp[i] : p[i] * (dp[i] - pdp);
+    if (A.aux_scale != 0.f) v += A.aux_scale * (float(E) / float(A.T)) * p[i] * (f[i] - pf);
+    if (A.z_scale != 0.f) v += zc * p[i];
+    A.dlogits[size_t(t) * E + e] = v;
   }
 }
 
-moe_status_t launch_dgate_router_bwd(const float* dy, const float* expert_out,
-                                     const float* logits, const int32_t* idx,
-                                     const float* gate, const int32_t* slot,
-                                     const int32_t* count, int T, int k, int E, int C, int D,
-                                     float aux_scale, float* dgate, float* dlogits,
-                                     hipStream_t s) {
-  const dim3 grid((T + 3) / 4), block(256);
-#define MOE_DG(EPLV)                                                                      \
-  MOE_LAUNCH("dgate_router_bwd", dgate_router_kernel<EPLV>, grid, block, 0, s, dy,          \
-             expert_out, logits, idx, gate, slot, count, T, k, E, C, D, aux_scale, dgate,  \
-             dlogits)
-  if (E <= 64) {
+moe_status_t launch_dgate_router_bwd(const DgateArgs& a, hipStream_t s) {
+  const dim3 grid((a.T + 3) / 4), block(256);
+#define MOE_DG(EPLV) \
+  MOE_LAUNCH("dgate_router_bwd", dgate_router_kernel<EPLV>, grid, block, 0, s, a)
+  if (a.E <= 64) {
     MOE_DG(1);
-  } else if (E <= 128) {
+  } else if (a.E <= 128) {
     MOE_DG(2);
-  } else if (E <= 256) {
+  } else if (a.E <= 256) {
     MOE_DG(4);
-  } else if (E <= 512) {
+  } else if (a.E <= 512) {
     MOE_DG(8);
   } else {
     MOE_DG(16);

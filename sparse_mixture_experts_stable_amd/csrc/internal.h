@@ -28,18 +28,28 @@ struct RouteWs {
   float* chunk_prob;   // [nc][E]
   int32_t* chunk_off;  // [nc][E] exclusive offsets of the chunks
   float* fp;           // [E] f_e * P_e
+  float* zpart;        // [nb] per routing block, sum of lse_t^2 over its tokens
   size_t bytes;
+};
+
+// Router variants seen by the routing kernel (moe_router_opts_t, device side).
+struct RouteOpts {
+  int32_t scoring;       // MOE_SCORE_SOFTMAX / MOE_SCORE_SIGMOID
+  const float* bias;     // [E] selection bias or NULL
+  int32_t with_z;        // 1: write the per-block z partials
 };
 RouteWs carve_route_ws(void* ws, int T, int E);
 
 moe_status_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* gate,
-                          const RouteWs& w, hipStream_t s);
+                          const RouteOpts& o, const RouteWs& w, hipStream_t s);
 moe_status_t launch_count(const int32_t* idx, int T, int k, int E, const RouteWs& w,
                           hipStream_t s);
-// with_prob: prob_part is valid (computes prob_sum and aux); C < 0: routing only
+// with_prob: prob_part is valid (computes prob_sum and aux); C < 0: routing only;
+// z_loss != NULL: zpart is valid, z_loss = sum of zpart / T.
 moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int32_t* count,
                                 float* prob_sum, float* aux, int32_t* used, int32_t* overflow,
-                                int32_t* slot_assign, const RouteWs& w, hipStream_t s);
+                                int32_t* slot_assign, float* z_loss, const RouteWs& w,
+                                hipStream_t s);
 // `used` (from launch_reduce_scan) also drives the -1 fill of unfilled slots.
 moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32_t* slot,
                            uint8_t* kept, int32_t* slot_assign, int32_t* drops,
@@ -166,13 +176,25 @@ moe_status_t launch_router_simt(const void* x, int dtype, int64_t ldx, const voi
 // ---- combine / backward --------------------------------------------------------------
 moe_status_t launch_combine(int dt, const void* residual, int64_t ldr, const void* shared_out,
                             const void* expert_out, const int32_t* idx, const int32_t* slot,
-                            const float* gate, int T, int k, int E, int C, int D, void* y,
-                            hipStream_t s);
-moe_status_t launch_dgate_router_bwd(const float* dy, const float* expert_out,
-                                     const float* logits, const int32_t* idx,
-                                     const float* gate, const int32_t* slot,
-                                     const int32_t* count, int T, int k, int E, int C, int D,
-                                     float aux_scale, float* dgate, float* dlogits,
-                                     hipStream_t s);
+                            const float* gate, int T, int k, int E, int C, int D, int renorm,
+                            void* y, hipStream_t s);
+struct DgateArgs {
+  const float* dy;
+  const float* o;          // [E, C, D] expert outputs (ungated)
+  const float* logits;
+  const int32_t* idx;
+  const float* gate;       // topk_gate
+  const int32_t* slot;
+  const int32_t* count;
+  int T, k, E, C, D;
+  float aux_scale;
+  float z_scale;
+  int scoring;
+  int renorm;
+  float* dgate;
+  float* dlogits;
+  float* eff_gate;         // [T, k] effective gates (written when non-NULL)
+};
+moe_status_t launch_dgate_router_bwd(const DgateArgs& a, hipStream_t s);
 
 }  // namespace moe

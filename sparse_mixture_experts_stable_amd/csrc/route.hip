@@ -7,7 +7,10 @@
 //                  counts and probability sums (trap 6 of the same page). A token is
 //                  handled by a group of L lanes (8..64) holding V <= 16 logits each, so
 //                  a wavefront works on 64/L tokens at once and every reduction stays
-//                  inside the group.
+//                  inside the group. The variants of "Module 7. Mixture of Experts"
+//                  (route_logits, router_z_loss): a selection bias added to the fp32
+//                  clean score in the top-k key only; sigmoid scoring with gates
+//                  normalised in log space; per-block sums of lse_t^2 for the z-loss.
 // count_kernel     per-block expert histogram of caller-supplied choices.
 // chunk_sum        per chunk of kScanRows routing blocks, the per-expert sums.
 // scan_kernel      one block: per expert, the exclusive scan of the chunk sums in chunk
@@ -47,11 +50,25 @@ RouteWs carve_route_ws(void* ws, int T, int E) {
   off = align_up(off + sizeof(int32_t) * size_t(E) * nc, 256);
   w.fp = reinterpret_cast<float*>(p + off);
   off = align_up(off + sizeof(float) * size_t(E), 256);
+  w.zpart = reinterpret_cast<float*>(p + off);
+  off = align_up(off + sizeof(float) * size_t(nb), 256);
   w.bytes = off;
   return w;
 }
 
 namespace {
+
+// Logistic function without overflow, and log(sigmoid(s)) = min(s, 0) - log(1 + e^-|s|),
+// finite for every finite s ("Module 7. Mixture of Experts", stable_sigmoid and
+// _log_sigmoid).
+__device__ __forceinline__ float sigmoid_stable(float s) {
+  if (s >= 0.f) return 1.0f / (1.0f + __expf(-s));
+  const float e = __expf(s);
+  return e / (1.0f + e);
+}
+__device__ __forceinline__ float log_sigmoid(float s) {
+  return fminf(s, 0.f) - log1pf(__expf(-fabsf(s)));
+}
 
 template <int L>
 __device__ __forceinline__ float group_max(float v) {
@@ -83,10 +100,14 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
                                                     int E, int k, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
                                                     int32_t* __restrict__ cnt_part,
-                                                    float* __restrict__ prob_part) {
+                                                    float* __restrict__ prob_part, RouteOpts o,
+                                                    float* __restrict__ zpart) {
   constexpr int TPR = 256 / L;  // tokens per round of the block
   __shared__ int s_hist[L * V];
   __shared__ float s_prob[TPR][L * V];
+  __shared__ float s_z[TPR];
+  const bool sig = o.scoring == MOE_SCORE_SIGMOID;
+  float zacc = 0.f;
   const int tid = threadIdx.x;
   const int grp = tid / L;
   const int li = tid % L;
@@ -118,13 +139,19 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
     sum = group_sum<L>(sum);
     const float inv = 1.0f / sum;
+    if (o.with_z) {
+      const float lse = mx + __logf(sum);
+      zacc = fmaf(lse, lse, zacc);
+    }
     uint64_t key[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       p[i] *= inv;
       acc[i] += p[i];
       const int e = li * V + i;
-      key[i] = (e < E) ? ((uint64_t(orderable(s[i])) << 32) | uint32_t(0xffffffffu - uint32_t(e))) : 0ull;
+      float kv = s[i];
+      if (o.bias && e < E) kv = (sig ? sigmoid_stable(s[i]) : p[i]) + o.bias[e];
+      key[i] = (e < E) ? ((uint64_t(orderable(kv)) << 32) | uint32_t(0xffffffffu - uint32_t(e))) : 0ull;
     }
 
     int my_e[KR];
@@ -147,7 +174,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         if (li == owner && i == si) {
-          pv = p[i];
+          pv = sig ? log_sigmoid(s[i]) : p[i];
           key[i] = 0ull;
         }
       }
@@ -161,6 +188,23 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         }
       }
     }
+    if (sig) {
+      // gates = softmax over the chosen experts of log sigmoid(s)
+      float lm = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < KR; ++q)
+        if (li + L * q < k) lm = fmaxf(lm, my_p[q]);
+      lm = group_max<L>(lm);
+      float ws = 0.f;
+#pragma unroll
+      for (int q = 0; q < KR; ++q) {
+        if (li + L * q < k) {
+          my_p[q] = __expf(my_p[q] - lm);
+          ws += my_p[q];
+        }
+      }
+      gsum = group_sum<L>(ws);
+    }
 #pragma unroll
     for (int q = 0; q < KR; ++q) {
       const int j = li + L * q;
@@ -171,6 +215,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
       }
     }
   }
+  if (li == 0) s_z[grp] = zacc;
 
 #pragma unroll
   for (int i = 0; i < V; ++i) s_prob[grp][li * V + i] = acc[i];
@@ -181,6 +226,11 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     for (int g2 = 0; g2 < TPR; ++g2) v += s_prob[g2][e];
     prob_part[base + e] = v;
     cnt_part[base + e] = s_hist[e];
+  }
+  if (o.with_z && tid == 0) {
+    float z = 0.f;
+    for (int g2 = 0; g2 < TPR; ++g2) z += s_z[g2];
+    zpart[blockIdx.x] = z;
   }
 }
 
@@ -234,7 +284,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     int32_t* __restrict__ chunk_off, int nchunks, int P, int T, int k, int E, int C,
     int with_prob, int32_t* __restrict__ count_out, float* __restrict__ prob_out,
     float* __restrict__ aux_out, int32_t* __restrict__ used_out,
-    int32_t* __restrict__ overflow_out, int32_t* __restrict__ flags) {
+    int32_t* __restrict__ overflow_out, int32_t* __restrict__ flags,
+    const float* __restrict__ zpart, int nb, float* __restrict__ z_out) {
   __shared__ int s_c[1024];
   __shared__ float s_p[1024];
   const int tid = threadIdx.x;
@@ -292,6 +343,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     __syncthreads();
   }
   if (tid == 0) aux_out[0] = float(E) * s_p[0];
+  if (!z_out) return;
+  // z-loss: thread tid adds the block partials tid, tid + 1024, ... in order, then a
+  // fixed tree over the threads
+  float z = 0.f;
+  for (int b = tid; b < nb; b += 1024) z += zpart[b];
+  __syncthreads();
+  s_p[tid] = z;
+  __syncthreads();
+  for (int d = 512; d >= 1; d >>= 1) {
+    if (tid < d) s_p[tid] += s_p[tid + d];
+    __syncthreads();
+  }
+  if (tid == 0) z_out[0] = s_p[0] / float(T);
 }
 
 // Slot assignment. Block b covers tokens [b*G*kRouteTokens, ...) (G routing blocks) and
@@ -391,33 +455,34 @@ __global__ __launch_bounds__(256) void assign_kernel(
 
 template <int L, int V>
 static moe_status_t launch_route_lv(const float* logits, int T, int E, int k, int32_t* idx,
-                                    float* gate, const RouteWs& w, hipStream_t s) {
+                                    float* gate, const RouteOpts& o, const RouteWs& w,
+                                    hipStream_t s) {
   const int nb = route_blocks(T);
   if (k <= L) {
     MOE_LAUNCH("route", (route_kernel<L, V, 1>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
-               gate, w.cnt_part, w.prob_part);
+               gate, w.cnt_part, w.prob_part, o, w.zpart);
   } else if (k <= 4 * L) {
     MOE_LAUNCH("route", (route_kernel<L, V, 4>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
-               gate, w.cnt_part, w.prob_part);
+               gate, w.cnt_part, w.prob_part, o, w.zpart);
   } else {
     MOE_LAUNCH("route", (route_kernel<L, V, 32>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
-               gate, w.cnt_part, w.prob_part);
+               gate, w.cnt_part, w.prob_part, o, w.zpart);
   }
   return MOE_OK;
 }
 
 moe_status_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* gate,
-                          const RouteWs& w, hipStream_t s) {
+                          const RouteOpts& o, const RouteWs& w, hipStream_t s) {
   // L lanes per token with V = E / L <= 16 logits each (L >= 8 so that a round of the
   // block covers at most kRouteTokens tokens)
-  if (E <= 8) return launch_route_lv<8, 1>(logits, T, E, k, idx, gate, w, s);
-  if (E <= 16) return launch_route_lv<8, 2>(logits, T, E, k, idx, gate, w, s);
-  if (E <= 32) return launch_route_lv<8, 4>(logits, T, E, k, idx, gate, w, s);
-  if (E <= 64) return launch_route_lv<8, 8>(logits, T, E, k, idx, gate, w, s);
-  if (E <= 128) return launch_route_lv<8, 16>(logits, T, E, k, idx, gate, w, s);
-  if (E <= 256) return launch_route_lv<16, 16>(logits, T, E, k, idx, gate, w, s);
-  if (E <= 512) return launch_route_lv<32, 16>(logits, T, E, k, idx, gate, w, s);
-  return launch_route_lv<64, 16>(logits, T, E, k, idx, gate, w, s);
+  if (E <= 8) return launch_route_lv<8, 1>(logits, T, E, k, idx, gate, o, w, s);
+  if (E <= 16) return launch_route_lv<8, 2>(logits, T, E, k, idx, gate, o, w, s);
+  if (E <= 32) return launch_route_lv<8, 4>(logits, T, E, k, idx, gate, o, w, s);
+  if (E <= 64) return launch_route_lv<8, 8>(logits, T, E, k, idx, gate, o, w, s);
+  if (E <= 128) return launch_route_lv<8, 16>(logits, T, E, k, idx, gate, o, w, s);
+  if (E <= 256) return launch_route_lv<16, 16>(logits, T, E, k, idx, gate, o, w, s);
+  if (E <= 512) return launch_route_lv<32, 16>(logits, T, E, k, idx, gate, o, w, s);
+  return launch_route_lv<64, 16>(logits, T, E, k, idx, gate, o, w, s);
 }
 
 moe_status_t launch_count(const int32_t* idx, int T, int k, int E, const RouteWs& w,
@@ -430,7 +495,8 @@ moe_status_t launch_count(const int32_t* idx, int T, int k, int E, const RouteWs
 
 moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int32_t* count,
                                 float* prob_sum, float* aux, int32_t* used, int32_t* overflow,
-                                int32_t* slot_assign, const RouteWs& w, hipStream_t s) {
+                                int32_t* slot_assign, float* z_loss, const RouteWs& w,
+                                hipStream_t s) {
   (void)slot_assign;
   const int nb = route_blocks(T);
   const int nchunks = scan_chunks(T);
@@ -441,7 +507,7 @@ moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int3
   if (P > nchunks) P = nchunks;
   MOE_LAUNCH("scan", scan_kernel, dim3(1), dim3(1024), 0, s, w.chunk_cnt, w.chunk_prob,
              C >= 0 ? w.chunk_off : nullptr, nchunks, P, T, k, E, C, with_prob ? 1 : 0, count,
-             prob_sum, aux, used, overflow, w.flags);
+             prob_sum, aux, used, overflow, w.flags, w.zpart, nb, with_prob ? z_loss : nullptr);
   return MOE_OK;
 }
 

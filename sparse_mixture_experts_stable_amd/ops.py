@@ -20,6 +20,17 @@ from . import _lib as L
 
 _KIND = {"linear": L.MOE_EXPERT_LINEAR, "gelu": L.MOE_EXPERT_GELU_MLP,
          "swiglu": L.MOE_EXPERT_SWIGLU}
+_SCORING = {"softmax": L.MOE_SCORE_SOFTMAX, "sigmoid": L.MOE_SCORE_SIGMOID}
+
+
+def _router_opts(scoring, selection_bias, renormalize_kept, z_loss_out):
+    """moe_router_opts_t for the router variants; returns (struct, tensors to keep)."""
+    bias = None
+    if selection_bias is not None:
+        bias = selection_bias.to(torch.float32).contiguous()
+    o = L.RouterOpts(scoring=_SCORING[scoring], selection_bias=_p(bias),
+                     renormalize_kept=1 if renormalize_kept else 0, z_loss=_p(z_loss_out))
+    return o, bias
 
 
 def _dt(t):
@@ -68,8 +79,10 @@ def _experts_struct(ex):
     return s, keep
 
 
-def route(*, k, logits=None, x=None, w_router=None):
-    """moe_route. Either logits [T,E] fp32, or x [T,D] and w_router [D,E]."""
+def route(*, k, logits=None, x=None, w_router=None, scoring="softmax", selection_bias=None,
+          z_loss=False):
+    """moe_route. Either logits [T,E] fp32, or x [T,D] and w_router [D,E]. ``scoring``,
+    ``selection_bias`` ([E]) and ``z_loss`` select the router variants."""
     if w_router is not None:
         x = _c(x)
         w_router = _c(w_router)
@@ -89,13 +102,19 @@ def route(*, k, logits=None, x=None, w_router=None):
     count = torch.empty(E, dtype=torch.int32, device=dev)
     prob = torch.empty(E, dtype=torch.float32, device=dev)
     aux = torch.empty(1, dtype=torch.float32, device=dev)
+    zl = torch.empty(1, dtype=torch.float32, device=dev) if z_loss else None
+    opts, bias = _router_opts(scoring, selection_bias, False, zl)
     ws = _ws(L.lib().moe_route_workspace_size(T, E), dev)
     st = L.lib().moe_route(_p(x) if w_router is not None else None, xdt, D, _p(w_router), _p(logits),
-                           T, D, E, k, _p(idx), _p(gate), _p(count), _p(prob), _p(aux), _p(ws),
-                           ws.numel(), _stream())
+                           T, D, E, k, _p(idx), _p(gate), _p(count), _p(prob), _p(aux),
+                           ctypes.byref(opts), _p(ws), ws.numel(), _stream())
     L.check("moe_route", st)
-    return {"logits": logits, "topk_idx": idx, "topk_gate": gate, "expert_count": count,
-            "prob_sum": prob, "aux_loss": aux}
+    del bias
+    out = {"logits": logits, "topk_idx": idx, "topk_gate": gate, "expert_count": count,
+           "prob_sum": prob, "aux_loss": aux}
+    if z_loss:
+        out["z_loss"] = zl
+    return out
 
 
 def dispatch(topk_idx, E, C, *, return_ws=False):
@@ -149,8 +168,10 @@ def expert_mlp(experts, x, *, k=1, C=0, slot_assign=None, expert_used=None, keep
     return {"expert_out": out, "hidden": hidden}
 
 
-def combine(expert_out, topk_idx, slot, topk_gate, *, residual=None, shared_out=None):
-    """moe_combine: y = residual + shared + sum_kept gate * expert_out[idx, slot]."""
+def combine(expert_out, topk_idx, slot, topk_gate, *, residual=None, shared_out=None,
+            renormalize_kept=False):
+    """moe_combine: y = residual + shared + sum_kept gate * expert_out[idx, slot] (gates
+    renormalised over the survivors with ``renormalize_kept``)."""
     eo = _c(expert_out)
     E, C, D = eo.shape
     T, k = topk_idx.shape
@@ -158,15 +179,18 @@ def combine(expert_out, topk_idx, slot, topk_gate, *, residual=None, shared_out=
     y = torch.empty(T, D, dtype=eo.dtype, device=eo.device)
     st = L.lib().moe_combine(_dt(eo), _p(_c(residual)), _p(_c(shared_out)), _p(eo),
                              _p(_c(topk_idx)), _p(_c(slot)), _p(_c(topk_gate)), T, k, E, C, D,
-                             _p(y), _stream())
+                             1 if renormalize_kept else 0, _p(y), _stream())
     L.check("moe_combine", st)
     del ref
     return y
 
 
 def forward(x, experts, *, k, capacity, w_router=None, logits=None, shared=None,
-            use_residual=True, keep_hidden=False, keep_shared_out=False, _ws_cache=None):
-    """moe_forward: the whole layer. Returns every output of the call (see moe.h)."""
+            use_residual=True, keep_hidden=False, keep_shared_out=False, scoring="softmax",
+            selection_bias=None, renormalize_kept=False, z_loss=False, _ws_cache=None):
+    """moe_forward: the whole layer. Returns every output of the call (see moe.h);
+    ``scoring``, ``selection_bias``, ``renormalize_kept`` and ``z_loss`` select the
+    router variants."""
     x = _c(x)
     T, D = x.shape
     dev = x.device
@@ -199,7 +223,10 @@ def forward(x, experts, *, k, capacity, w_router=None, logits=None, shared=None,
         "shared_out": (torch.empty(T, D, dtype=x.dtype, device=dev)
                        if keep_shared_out and shared is not None else None),
         "capacity": C,
+        "z_loss": torch.empty(1, dtype=torch.float32, device=dev) if z_loss else None,
+        "router": {"scoring": scoring, "renormalize_kept": bool(renormalize_kept)},
     }
+    ropts, bias = _router_opts(scoring, selection_bias, renormalize_kept, o["z_loss"])
     a = L.ForwardArgs(
         x=_p(x), ldx=x.stride(0), T=T, w_router=_p(w_router), logits=_p(logits), experts=es,
         shared=shs, k=k, capacity=C, use_residual=1 if use_residual else 0,
@@ -209,7 +236,7 @@ def forward(x, experts, *, k, capacity, w_router=None, logits=None, shared=None,
         slot_assign=_p(o["slot_assign"]), expert_used=_p(o["expert_used"]),
         expert_overflow=_p(o["expert_overflow"]), token_drops=_p(o["token_drops"]),
         hidden_cache=_p(o["hidden"]), expert_out=_p(o["expert_out"]),
-        shared_out=_p(o["shared_out"]), y=_p(o["y"]))
+        shared_out=_p(o["shared_out"]), y=_p(o["y"]), router=ropts)
     need = L.lib().moe_forward_workspace_size(ctypes.byref(a))
     if _ws_cache is not None and _ws_cache.numel() >= need:
         ws = _ws_cache
@@ -219,7 +246,7 @@ def forward(x, experts, *, k, capacity, w_router=None, logits=None, shared=None,
     L.check("moe_forward", st)
     o["ws"] = ws
     # everything a repeat call needs, kept alive together
-    o["_call"] = PreparedCall("moe_forward", a, ws, (x, w_router, keep, shkeep))
+    o["_call"] = PreparedCall("moe_forward", a, ws, (x, w_router, keep, shkeep, bias))
     return o
 
 
@@ -246,10 +273,12 @@ class PreparedCall:
 
 
 def backward(dy, x, experts, fwd, *, k, use_residual=True, aux_grad_scale=0.0, shared=None,
-             w_router=None):
+             w_router=None, z_grad_scale=0.0):
     """moe_backward for fp32 experts of any kind. ``fwd`` is the dict returned by
     forward(). ``shared``: the shared SwiGLU expert of the forward; ``w_router``: the
-    router weights, for dw_router and the router term of dx.
+    router weights, for dw_router and the router term of dx. The router variant
+    (scoring, survivor renormalisation) is the forward's; ``z_grad_scale`` weights the
+    z-loss gradient in dlogits.
 
     Returns dx, dgate, dlogits, ``dexperts`` (gradients named like the expert weights),
     ``dW`` (= dexperts["w_in"]), ``dshared`` (or None) and ``dw_router`` (or None)."""
@@ -306,7 +335,10 @@ def backward(dy, x, experts, fwd, *, k, use_residual=True, aux_grad_scale=0.0, s
         dshared_w_in=_p(dsh["w_in"]) if dsh else None,
         dshared_w_up=_p(dsh["w_up"]) if dsh else None,
         dshared_w_out=_p(dsh["w_out"]) if dsh else None,
-        w_router=_p(w_router), dw_router=_p(dwr))
+        w_router=_p(w_router), dw_router=_p(dwr),
+        router=L.RouterOpts(scoring=_SCORING[fwd.get("router", {}).get("scoring", "softmax")],
+                            renormalize_kept=1 if fwd.get("router", {}).get("renormalize_kept") else 0),
+        z_grad_scale=float(z_grad_scale))
     ws = _ws(L.lib().moe_backward_workspace_size(ctypes.byref(a)), dev)
     st = L.lib().moe_backward(ctypes.byref(a), _p(ws), ws.numel(), _stream())
     L.check("moe_backward", st)

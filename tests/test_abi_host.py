@@ -62,10 +62,11 @@ def test_route_rejects_bad_arguments():
     p = ctypes.c_void_p(1 << 21)
     common = dict(x=None, dt=L.MOE_F32, ldx=0, w=None, logits=p)
 
-    def call(T, E, k, ws_bytes=1 << 30, idx=p):
+    def call(T, E, k, ws_bytes=1 << 30, idx=p, opts=None):
         return lib.moe_route(common["x"], common["dt"], common["ldx"], common["w"], common["logits"],
-                             T, 0, E, k, idx, p, p, p, p, ws, ws_bytes, None)
+                             T, 0, E, k, idx, p, p, p, p, opts, ws, ws_bytes, None)
     assert call(8, 4, 0) == L.MOE_ERR_INVALID_ARG
+    assert call(8, 4, 2, opts=ctypes.byref(L.RouterOpts(scoring=2))) == L.MOE_ERR_INVALID_ARG
     assert call(8, 4, 5) == L.MOE_ERR_INVALID_ARG
     assert call(0, 4, 1) == L.MOE_ERR_INVALID_ARG
     assert call(8, 2000, 1) == L.MOE_ERR_INVALID_ARG
