@@ -95,7 +95,9 @@ __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
 }  // namespace
 
 // L lanes per token, V logits per lane (E <= L*V), KR result slots per lane (k <= L*KR).
-template <int L, int V, int KR>
+// VAR: the router variants are compiled in (sigmoid scoring, selection bias, z partials,
+// chosen at run time from o); without it the kernel is the plain softmax router.
+template <int L, int V, int KR, bool VAR>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
                                                     int E, int k, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
@@ -106,7 +108,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   __shared__ int s_hist[L * V];
   __shared__ float s_prob[TPR][L * V];
   __shared__ float s_z[TPR];
-  const bool sig = o.scoring == MOE_SCORE_SIGMOID;
+  const bool sig = VAR && o.scoring == MOE_SCORE_SIGMOID;
+  const bool with_z = VAR && o.with_z;
+  const float* bias = VAR ? o.bias : nullptr;
   float zacc = 0.f;
   const int tid = threadIdx.x;
   const int grp = tid / L;
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
     sum = group_sum<L>(sum);
     const float inv = 1.0f / sum;
-    if (o.with_z) {
+    if (with_z) {
       const float lse = mx + __logf(sum);
       zacc = fmaf(lse, lse, zacc);
     }
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
       acc[i] += p[i];
       const int e = li * V + i;
       float kv = s[i];
-      if (o.bias && e < E) kv = (sig ? sigmoid_stable(s[i]) : p[i]) + o.bias[e];
+      if (bias && e < E) kv = (sig ? sigmoid_stable(s[i]) : p[i]) + bias[e];
       key[i] = (e < E) ? ((uint64_t(orderable(kv)) << 32) | uint32_t(0xffffffffu - uint32_t(e))) : 0ull;
     }
 
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     prob_part[base + e] = v;
     cnt_part[base + e] = s_hist[e];
   }
-  if (o.with_z && tid == 0) {
+  if (with_z && tid == 0) {
     float z = 0.f;
     for (int g2 = 0; g2 < TPR; ++g2) z += s_z[g2];
     zpart[blockIdx.x] = z;
@@ -458,16 +462,23 @@ static moe_status_t launch_route_lv(const float* logits, int T, int E, int k, in
                                     float* gate, const RouteOpts& o, const RouteWs& w,
                                     hipStream_t s) {
   const int nb = route_blocks(T);
-  if (k <= L) {
-    MOE_LAUNCH("route", (route_kernel<L, V, 1>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
-               gate, w.cnt_part, w.prob_part, o, w.zpart);
-  } else if (k <= 4 * L) {
-    MOE_LAUNCH("route", (route_kernel<L, V, 4>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
-               gate, w.cnt_part, w.prob_part, o, w.zpart);
-  } else {
-    MOE_LAUNCH("route", (route_kernel<L, V, 32>), dim3(nb), dim3(256), 0, s, logits, T, E, k, idx,
-               gate, w.cnt_part, w.prob_part, o, w.zpart);
+  const bool var = o.scoring != MOE_SCORE_SOFTMAX || o.bias || o.with_z;
+#define MOE_ROUTE(KRV)                                                                        \
+  if (var) {                                                                                \
+    MOE_LAUNCH("route", (route_kernel<L, V, KRV, true>), dim3(nb), dim3(256), 0, s, logits, T, \
+               E, k, idx, gate, w.cnt_part, w.prob_part, o, w.zpart);                        \
+  } else {                                                                                  \
+    MOE_LAUNCH("route", (route_kernel<L, V, KRV, false>), dim3(nb), dim3(256), 0, s, logits,   \
+               T, E, k, idx, gate, w.cnt_part, w.prob_part, o, w.zpart);                     \
   }
+  if (k <= L) {
+    MOE_ROUTE(1)
+  } else if (k <= 4 * L) {
+    MOE_ROUTE(4)
+  } else {
+    MOE_ROUTE(32)
+  }
+#undef MOE_ROUTE
   return MOE_OK;
 }
 
