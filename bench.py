@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
                     [--backward | --forward-only] [--dtype f32] [--router-grad]
+    python bench.py --vendor-gemm      (the vendor library's GEMMs on the same shapes)
 
 A step is one moe_forward call over the whole hot path (router GEMM, routing, dispatch,
 grouped expert GEMMs with the shared expert, combine, aux loss) on one batch of seeded
@@ -55,6 +56,10 @@ def parse():
     ap.add_argument("--router-grad", action="store_true",
                     help="with the backward: also the router weight gradient and dx's "
                          "router term (logits = x W_r)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="instead of the layer: time the vendor library's bf16 GEMMs (torch "
+                         "bmm / mm) on the expert GEMM shapes of the SwiGLU workload, as a "
+                         "reference point for the MFMA fraction")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MiB (a "
                          "known-size reference for hardware byte counters)")
@@ -191,8 +196,56 @@ def cpu_baseline(w, inp, n_tokens, backward=False, router_grad=False):
     return n_tokens / dt, dt, threads
 
 
+def vendor_gemm(steps):
+    """The vendor library's bf16 GEMMs on the expert GEMM shapes of the SwiGLU workload
+    (E=256 experts x C=512 rows, d_model 2048, intermediate 512): batched (one GEMM per
+    expert, gate and up stacked as 1024 columns) and as one dense GEMM over all E*C rows;
+    plus a square 8192 GEMM. Same FLOP accounting as the layer's GEMMs."""
+    import torch
+    bf = torch.bfloat16
+    E, C, D, F = 256, 512, 2048, 512
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn(E, C, D, device="cuda", dtype=bf, generator=g)
+    w1 = torch.randn(E, D, 2 * F, device="cuda", dtype=bf, generator=g)
+    h = torch.randn(E, C, F, device="cuda", dtype=bf, generator=g)
+    w2 = torch.randn(E, F, D, device="cuda", dtype=bf, generator=g)
+    o1 = torch.empty(E, C, 2 * F, device="cuda", dtype=bf)
+    o2 = torch.empty(E, C, D, device="cuda", dtype=bf)
+    X, W1, O1 = x.reshape(E * C, D), w1[0].contiguous(), o1.reshape(E * C, 2 * F)
+    H, W2, O2 = h.reshape(E * C, F), w2[0].contiguous(), o2.reshape(E * C, D)
+    A = torch.randn(8192, 8192, device="cuda", dtype=bf, generator=g)
+    B = torch.randn(8192, 8192, device="cuda", dtype=bf, generator=g)
+    Cc = torch.empty_like(A)
+    cases = [
+        ("bmm [256,512,2048] x [256,2048,1024] (GEMM-1 shape)", lambda: torch.bmm(x, w1, out=o1), 2.0 * E * C * D * 2 * F),
+        ("bmm [256,512,512] x [256,512,2048] (GEMM-2 shape)", lambda: torch.bmm(h, w2, out=o2), 2.0 * E * C * F * D),
+        ("mm [131072,2048] x [2048,1024]", lambda: torch.mm(X, W1, out=O1), 2.0 * E * C * D * 2 * F),
+        ("mm [131072,512] x [512,2048]", lambda: torch.mm(H, W2, out=O2), 2.0 * E * C * F * D),
+        ("mm [8192,8192] x [8192,8192]", lambda: torch.mm(A, B, out=Cc), 2.0 * 8192 ** 3),
+    ]
+    res = {}
+    for name, fn, fl in cases:
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = fl / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    print(json.dumps({"vendor_gemm": "torch (hipBLASLt) bf16", "peak_tflops": PEAK_BF16_TFLOPS,
+                      "results": res}), flush=True)
+
+
 def main():
     args = parse()
+    if args.vendor_gemm:
+        vendor_gemm(args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "expert-parallel path is not part of this build.", file=sys.stderr)
