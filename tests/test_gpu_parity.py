@@ -169,15 +169,31 @@ BWD = {
     "swiglu_shared": WORKLOADS[3].scaled(T=1024, D=256, E=32, F=128, shared_F=128, dtype="f32",
                                          backward=True),
     "linear": SMALL[5],
+    # fp32 tiles of 64 x 64 x 32: partial N tiles (F = 80, E = 8) and K tails (F = 80,
+    # D = 16, F = 48, shared 32), every GEMM mode and epilogue of the backward
+    "gelu_odd": WORKLOADS[1].scaled(T=300, D=64, E=8, F=80, backward=True),
+    "swiglu_tiny": WORKLOADS[3].scaled(T=129, D=16, E=4, k=1, F=48, shared_F=32, dtype="f32",
+                                       backward=True, cf=1.5),
 }
 
 
 @pytest.mark.parametrize("case,aux_scale,router", [
     ("gelu_bias", 0.0, False), ("gelu_bias", 1.0, True), ("gelu_wide", 0.0, True),
     ("swiglu_shared", 0.0, False), ("swiglu_shared", 0.5, True), ("linear", 0.0, True),
+    ("gelu_odd", 0.0, True), ("swiglu_tiny", 1.0, True),
 ])
 def test_backward_general(case, aux_scale, router):
     _backward_general(BWD[case], aux_scale, router)
+
+
+@pytest.mark.parametrize("case", ["gelu_odd", "swiglu_tiny"])
+def test_forward_odd_fp32_shapes(case):
+    w = BWD[case]
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp)
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.check_outputs(w, inp, h, r, d)
 
 
 def test_backward_general_no_residual_tiny_capacity():
