@@ -245,3 +245,78 @@ def test_combine_renormalize_standalone():
     full = np.flatnonzero(d["drops"] == k)
     assert full.size > 0
     assert np.array_equal(y[full], x[full])
+
+
+# ---------------------------------------------------------------------------------
+# full sizes, in the launch configuration the bench uses
+# ---------------------------------------------------------------------------------
+
+def _sample(T, d, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    toks = set(range(4)) | set(range(T - 4, T)) | set(rng.integers(0, T, n).tolist())
+    full = np.flatnonzero(d["drops"] == d["slot"].shape[1])
+    toks |= set(full[:4].tolist())
+    return np.array(sorted(toks))
+
+
+@pytest.mark.parametrize("cfg,scoring,renorm", [(3, "sigmoid", True), (4, "sigmoid", True),
+                                                (3, "softmax", True)])
+def test_forward_variants_full_size(cfg, scoring, renorm):
+    """The SwiGLU workload and the drop/tie stress workload at full size with a selection
+    bias: routing, dispatch and the z-loss everywhere, y on sampled tokens."""
+    ops = _ops()
+    w = WORKLOADS[cfg]
+    inp = make_inputs(w)
+    g = H.gpu_inputs(inp)
+    rng = np.random.default_rng(11)
+    bias = (rng.standard_normal(w.E) * 0.02).astype(np.float32)
+    C = ops.capacity(w.T, w.k, w.E, w.cf)
+    kw = {"logits": g["logits"]} if "logits" in g else {"w_router": g["w_router"]}
+    out = ops.forward(g["x"], H.experts_dict(w, g), k=w.k, capacity=C, shared=H.shared_dict(w, g),
+                      use_residual=w.residual, keep_shared_out=True, scoring=scoring,
+                      selection_bias=torch.tensor(bias, device="cuda"), renormalize_kept=renorm,
+                      z_loss=True, **kw)
+    torch.cuda.synchronize()
+    h = H.host(out)
+    lg = h["logits"].astype(np.float64)
+    r = om.route(lg, w.k, scoring=scoring, selection_bias=bias.astype(np.float64))
+    _check_selection(h["topk_idx"], r, bias.astype(np.float64), w.k, max_frac=1e-3)
+    # dispatch follows the GPU's selection exactly
+    d = om.dispatch(h["topk_idx"], w.E, C)
+    for key, wk in (("slot", "slot"), ("slot_assign", "slot_assign"), ("expert_used", "used"),
+                    ("expert_overflow", "overflow"), ("token_drops", "drops")):
+        assert np.array_equal(h[key], d[wk]), key
+    H.assert_close(h["z_loss"], np.array([r["z_loss"]]), 1e-4, "z_loss")
+    toks = _sample(w.T, d)
+    same = np.all(h["topk_idx"][toks] == r["idx"][toks], axis=1)
+    toks = toks[same]
+    x = to_numpy_f32(inp["x"])
+    o = om.expert_outputs(w.kind, H.oracle_weights(inp), x, h["topk_idx"], d["kept"], tokens=toks,
+                          bf16=True)
+    sh = om.shared_apply(H.oracle_shared(inp), x[toks], bf16=True) if w.shared_F else None
+    y = om.bf16_round(om.combine(x[toks], sh, o, r["gate"][toks], d["kept"][toks], w.residual,
+                                 renormalize=renorm))
+    H.assert_close(h["y"][toks], y, H.RTOL["bf16"], "y")
+
+
+def test_backward_variants_full_size():
+    """The single-linear forward + backward workload at full size under the sigmoid router
+    with a selection bias, survivor renormalisation and the z-loss term: every gradient."""
+    ops = _ops()
+    w = WORKLOADS[5]
+    inp, g, out, bias, C = _variant_forward(w, "sigmoid", True, True)
+    grads = ops.backward(g["dy"], g["x"], H.experts_dict(w, g), out, k=w.k,
+                         use_residual=w.residual, aux_grad_scale=1.0, z_grad_scale=0.5)
+    torch.cuda.synchronize()
+    h = H.host(out)
+    lg = h["logits"].astype(np.float64)
+    r = om.route(lg, w.k, scoring="sigmoid", selection_bias=bias.astype(np.float64))
+    assert np.array_equal(h["topk_idx"], r["idx"]), "selection (no near-tie at this seed)"
+    d = om.dispatch(h["topk_idx"], w.E, C)
+    want = om.backward(to_numpy_f32(inp["dy"]), to_numpy_f32(inp["x"]), w.kind,
+                       H.oracle_weights(inp), lg, h["topk_idx"], r["gate"], d["kept"], r["count"],
+                       residual=w.residual, aux_grad_scale=1.0, scoring="sigmoid",
+                       renormalize=True, z_grad_scale=0.5)
+    for key in ("dgate", "dlogits", "dx"):
+        H.assert_close(grads[key].cpu().numpy(), want[key], 1e-4, key)
+    H.assert_close(grads["dW"].cpu().numpy(), want["dexperts"]["w_in"], 1e-4, "dW")
