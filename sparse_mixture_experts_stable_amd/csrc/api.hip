@@ -161,7 +161,7 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
     a.row_div = k;
     a.g_count = dense ? nullptr : used;
     a.g_const = T;
-    a.m_tiles = (rows + kF32BM - 1) / kF32BM;
+    a.m_rows = rows;
     a.B = static_cast<const float*>(ex->w_in);
     a.B1 = static_cast<const float*>(ex->kind == MOE_EXPERT_SWIGLU ? ex->w_up : nullptr);
     a.N = pl.two_stage ? F : D;
@@ -186,7 +186,7 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
       b.row_div = 1;
       b.g_count = dense ? nullptr : used;
       b.g_const = T;
-      b.m_tiles = a.m_tiles;
+      b.m_rows = a.m_rows;
       b.B = static_cast<const float*>(ex->w_out);
       b.ldb = D;
       b.b_gstride = int64_t(F) * D;
@@ -274,7 +274,7 @@ moe_status_t router_gemm(const void* x, int dt, int64_t ldx, const void* w, int 
     p.lda = ldx;
     p.row_div = 1;
     p.g_const = T;
-    p.m_tiles = (T + kF32BM - 1) / kF32BM;
+    p.m_rows = T;
     p.B = static_cast<const float*>(w);
     p.ldb = E;
     p.K = D;
@@ -693,7 +693,6 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
   const moe_experts_t* ex = S.ex;
   const int E = ex->num_experts, D = ex->d_model, F = ex->d_hidden, R = S.rows;
   const bool swiglu = ex->kind == MOE_EXPERT_SWIGLU;
-  const int mt_rows = (R + kF32BM - 1) / kF32BM;
   moe_status_t st;
 
   // dH = dO W_out^T, ungated here (the gate is applied in the recompute epilogue)
@@ -705,7 +704,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
   p.row_div = S.row_div;
   p.g_count = S.count;
   p.g_const = S.cnt_const;
-  p.m_tiles = mt_rows;
+  p.m_rows = R;
   p.B = static_cast<const float*>(ex->w_out);
   p.ldb = D;
   p.b_gstride = int64_t(F) * D;
@@ -729,7 +728,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
   p.row_div = S.row_div;
   p.g_count = S.count;
   p.g_const = S.cnt_const;
-  p.m_tiles = mt_rows;
+  p.m_rows = R;
   p.B = static_cast<const float*>(ex->w_in);
   p.B1 = swiglu ? static_cast<const float*>(ex->w_up) : nullptr;
   p.ldb = F;
@@ -759,7 +758,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
   p.g_count = S.count;
   p.g_const = S.cnt_const;
   p.M = F;
-  p.m_tiles = (F + kF32BM - 1) / kF32BM;
+  p.m_rows = F;
   p.B = dy;
   p.ldb = ld;
   p.b_row_map = S.row_map;
@@ -784,7 +783,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
     p.g_count = S.count;
     p.g_const = S.cnt_const;
     p.M = D;
-    p.m_tiles = (D + kF32BM - 1) / kF32BM;
+    p.m_rows = D;
     p.B = w == 0 ? S.g : S.u;
     p.ldb = F;
     p.b_gstride = int64_t(R) * F;
@@ -820,7 +819,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
     p.row_div = 1;
     p.g_count = S.count;
     p.g_const = S.cnt_const;
-    p.m_tiles = mt_rows;
+    p.m_rows = R;
     p.B = static_cast<const float*>(w == 0 ? ex->w_in : ex->w_up);
     p.ldb = F;
     p.b_gstride = int64_t(D) * F;
@@ -927,7 +926,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
     px.row_map_ld = C;
     px.row_div = k;
     px.g_count = a->expert_used;
-    px.m_tiles = (C + kF32BM - 1) / kF32BM;
+    px.m_rows = C;
     px.B = static_cast<const float*>(ex.w_in);
     px.ldb = D;
     px.b_gstride = int64_t(D) * D;
@@ -952,7 +951,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
     pw.g_count = used;
     pw.g_const = 0;
     pw.M = D;
-    pw.m_tiles = (D + kF32BM - 1) / kF32BM;
+    pw.m_rows = D;
     pw.B = dy;
     pw.ldb = a->ld;
     pw.b_row_map = a->slot_assign;
@@ -1021,7 +1020,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
     pr.row_div = 1;
     pr.g_const = T;
     pr.M = D;
-    pr.m_tiles = (D + kF32BM - 1) / kF32BM;
+    pr.m_rows = D;
     pr.B = a->dlogits;
     pr.ldb = E;
     pr.N = E;
@@ -1037,7 +1036,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
     pd.lda = E;
     pd.row_div = 1;
     pd.g_const = T;
-    pd.m_tiles = (T + kF32BM - 1) / kF32BM;
+    pd.m_rows = T;
     pd.B = static_cast<const float*>(a->w_router);
     pd.ldb = E;
     pd.K = E;

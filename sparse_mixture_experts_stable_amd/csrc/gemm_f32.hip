@@ -11,17 +11,20 @@
 //   dW2  = H^T dO,  dW1 = X^T dZ             A_KROWS x B_KROWS (K = the expert's rows)
 //   dX_e = dZ W1^T                           A_ROWS x B_NK (+ EPI_ACCUM for SwiGLU's 2nd)
 //
-// Tile 64 x 64 x 32 per 256-thread block; four waves in 2 x 2, each 32 x 32 (2 x 2
-// MFMA tiles). An operand keeps its HBM orientation in LDS, so every global load is a
-// float4 and every LDS store a float4 (no transposition):
+// Tiles of BM x BN x 32 (BM, BN each 64 or 128) per 256-thread block; four waves in
+// 2 x 2, each (BM/2) x (BN/2) in 16 x 16 MFMA tiles. An operand keeps its HBM
+// orientation in LDS, so every global load is a float4 and every LDS store a float4 (no
+// transposition):
 //   k-contiguous operands (A_ROWS, B_NK) as [row][k], rows padded to 36 floats: eight
 //     threads read one full 128-byte line of a row per k-tile;
-//   m/n-contiguous operands (A_KROWS, B_KN, B_KROWS) as [k][m|n], rows padded to 80
-//     floats.
+//   m/n-contiguous operands (A_KROWS, B_KN, B_KROWS) as [k][m|n], rows padded to 16
+//     floats beyond the tile width.
 // MFMA step ks (of 8) takes k = 4 ks + lane / 16, so lane l reads the A value
 // (row l % 16, that k) and the B value (that k, column l % 16) one float at a time; both
 // paddings make these 64-lane reads conflict-free (36 r mod 64 runs over distinct
-// multiples of 4, 80 = 16 mod 64 separates the four k rows of one read). Loads are
+// multiples of 4; a row of 80 or 144 floats is 16 mod 64, which separates the four k
+// rows of one read). The 128-wide tiles read half as many fragment values per MFMA as
+// the 64-wide ones, which is what bounds the small tile (LDS read bandwidth). Loads are
 // guarded per float4 against M, N and K, so those sizes need only be multiples of 4.
 
 #include "internal.h"
@@ -29,10 +32,8 @@
 namespace moe {
 
 namespace {
-constexpr int BM = kF32BM, BN = kF32BN, BK = kF32BK;
+constexpr int BK = 32;
 constexpr int KP = BK + 4;  // LDS row of a [row][k] operand (floats)
-constexpr int NP = 80;      // LDS row of a [k][m|n] operand (floats)
-static_assert(BM == 64 && BN == 64 && BK == 32, "load coordinates assume a 64 x 64 x 32 tile");
 
 __device__ __forceinline__ int logical_block_f32(int bid, int nblk) {
   const int q = nblk >> 3, r = nblk & 7;
@@ -52,13 +53,17 @@ __device__ __forceinline__ float gelu_erf_grad(float z) {
 }
 }  // namespace
 
-template <int AM, int BMODE, bool GATED>
+template <int AM, int BMODE, bool GATED, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   constexpr int NB = GATED ? 2 : 1;
   constexpr bool AK = AM == A_ROWS;     // A stored [m][k]
   constexpr bool BK_ = BMODE == B_NK;   // B stored [n][k]
-  constexpr int A_SZ = AK ? BM * KP : BK * NP;
-  constexpr int B_SZ = BK_ ? BN * KP : BK * NP;
+  constexpr int NPA = BM + 16, NPB = BN + 16;  // LDS rows of [k][m|n] operands (floats)
+  constexpr int A_SZ = AK ? BM * KP : BK * NPA;
+  constexpr int B_SZ = BK_ ? BN * KP : BK * NPB;
+  constexpr int TM = BM / 32, TN = BN / 32;    // 16 x 16 MFMA tiles per wave
+  constexpr int AL = BM / 32, BL = BN / 32;    // float4 loads per thread per k-tile
+  static_assert((BM == 64 || BM == 128) && (BN == 64 || BN == 128), "tile size");
   __shared__ float As[2][A_SZ];
   __shared__ float Bs[NB][2][B_SZ];
   const int lid = logical_block_f32(blockIdx.x, gridDim.x);
@@ -83,17 +88,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   }
   const int N = P.N;
 
-  // ---- per-thread load coordinates (two float4 per operand per k-tile) ----
-  // [row][k] operands: row = tid / 8 (+ 32), k quad = tid % 8
-  // [k][m|n] operands: k row = tid / 16 (+ 16), quad = tid % 16
+  // ---- per-thread load coordinates ----
+  // [row][k] operands: row = tid / 8 + 32 h, k quad = tid % 8
+  // [k][m|n] operands of width W: k row = tid / (W/4) + (1024 / W) h, quad = tid % (W/4)
   const int kr_row = tid >> 3, kr_q = tid & 7;
-  const int mr_k = tid >> 4, mr_q = tid & 15;
+  const int am_q = tid % (BM / 4), am_k = tid / (BM / 4);
+  const int bn_q = tid % (BN / 4), bn_k = tid / (BN / 4);
+  constexpr int AM_STEP = 1024 / BM, BN_STEP = 1024 / BN;
 
   const float* a_base = P.A + size_t(g) * P.a_gstride;
-  const float* a_row_ptr[2] = {nullptr, nullptr};  // A_ROWS
+  const float* a_row_ptr[AL];  // A_ROWS
   if (AM == A_ROWS) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < AL; ++h) {
       int r = m0 + kr_row + 32 * h;
       if (r >= M) r = m0;
       const int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + r] / P.row_div : r;
@@ -104,24 +111,27 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   const float* b1_base = GATED ? P.B1 + size_t(g) * P.b_gstride : nullptr;
   const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  float4 ra[2], rb[NB][2];
+  float4 ra[AL], rb[NB][BL];
   auto load = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < AL; ++h) {
       if (AM == A_ROWS) {
         ra[h] = (k0 + kr_q * 4 < Kg) ? ld4(a_row_ptr[h] + k0) : zero;
       } else {
-        const int kk = k0 + mr_k + 16 * h;
+        const int kk = k0 + am_k + AM_STEP * h;
         ra[h] = zero;
-        if (kk < Kg && m0 + mr_q * 4 < M) {
+        if (kk < Kg && m0 + am_q * 4 < M) {
           const int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + kk] / P.row_div : kk;
-          ra[h] = ld4(a_base + size_t(src) * P.lda + m0 + mr_q * 4);
+          ra[h] = ld4(a_base + size_t(src) * P.lda + m0 + am_q * 4);
         }
       }
+    }
+#pragma unroll
+    for (int h = 0; h < BL; ++h) {
       if (BMODE == B_KN) {
-        const int kk = k0 + mr_k + 16 * h;
-        const int n = n0 + mr_q * 4;
+        const int kk = k0 + bn_k + BN_STEP * h;
+        const int n = n0 + bn_q * 4;
         const bool ok = kk < Kg && n < N;
         rb[0][h] = ok ? ld4(b_base + size_t(kk) * P.ldb + n) : zero;
         if constexpr (GATED) rb[1][h] = ok ? ld4(b1_base + size_t(kk) * P.ldb + n) : zero;
@@ -130,8 +140,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
         const int kq = k0 + kr_q * 4;
         rb[0][h] = (n < N && kq < Kg) ? ld4(b_base + size_t(n) * P.ldb + kq) : zero;
       } else {
-        const int kk = k0 + mr_k + 16 * h;
-        const int n = n0 + mr_q * 4;
+        const int kk = k0 + bn_k + BN_STEP * h;
+        const int n = n0 + bn_q * 4;
         rb[0][h] = zero;
         if (kk < Kg && n < N) {
           int src = kk;
@@ -149,22 +159,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int a_off = AK ? (kr_row + 32 * h) * KP + kr_q * 4 : (mr_k + 16 * h) * NP + mr_q * 4;
-      *reinterpret_cast<float4*>(&As[buf][a_off]) = ra[h];
-      const int b_off = BK_ ? (kr_row + 32 * h) * KP + kr_q * 4 : (mr_k + 16 * h) * NP + mr_q * 4;
+    for (int h = 0; h < AL; ++h) {
+      const int off = AK ? (kr_row + 32 * h) * KP + kr_q * 4 : (am_k + AM_STEP * h) * NPA + am_q * 4;
+      *reinterpret_cast<float4*>(&As[buf][off]) = ra[h];
+    }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) *reinterpret_cast<float4*>(&Bs[b][buf][b_off]) = rb[b][h];
+    for (int h = 0; h < BL; ++h) {
+      const int off = BK_ ? (kr_row + 32 * h) * KP + kr_q * 4 : (bn_k + BN_STEP * h) * NPB + bn_q * 4;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) *reinterpret_cast<float4*>(&Bs[b][buf][off]) = rb[b][h];
     }
   };
 
-  f32x4 acc[NB][2][2];
+  f32x4 acc[NB][TM][TN];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TN; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (Kg + BK - 1) / BK;
   const int fr = lane & 15, fc = lane >> 4;
@@ -178,24 +191,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
 #pragma unroll
       for (int ks = 0; ks < BK / 4; ++ks) {
         const int kl = ks * 4 + fc;
-        float af[2];
+        float af[TM];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int row = wm * 32 + i * 16 + fr;
-          af[i] = As[cur][AK ? row * KP + kl : kl * NP + row];
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm * (BM / 2) + i * 16 + fr;
+          af[i] = As[cur][AK ? row * KP + kl : kl * NPA + row];
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          float bf[2];
+          float bf[TN];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = wn * 32 + j * 16 + fr;
-            bf[j] = Bs[b][cur][BK_ ? col * KP + kl : kl * NP + col];
+          for (int j = 0; j < TN; ++j) {
+            const int col = wn * (BN / 2) + j * 16 + fr;
+            bf[j] = Bs[b][cur][BK_ ? col * KP + kl : kl * NPB + col];
           }
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < TN; ++j)
               acc[b][i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j], af[i], acc[b][i][j], 0, 0, 0);
         }
       }
@@ -208,15 +221,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   const int epi = P.epi;
   const bool bwd = epi == EPI_GELU_BWD || epi == EPI_SWIGLU_BWD;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = m0 + wm * 32 + i * 16 + fr;
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * (BM / 2) + i * 16 + fr;
     if (m >= M) continue;
     float rg = 1.f;
     if (bwd && AM == A_ROWS && P.gate && P.row_map)
       rg = P.gate[P.row_map[size_t(g) * P.row_map_ld + m]];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 32 + j * 16 + fc * 4;
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * (BN / 2) + j * 16 + fc * 4;
       if (n >= N) continue;
       const size_t off = size_t(g) * P.c_gstride + size_t(m) * P.ldc + n;
       float v[4] = {acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]};
@@ -274,31 +287,47 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   }
 }
 
-moe_status_t launch_gemm_f32(GemmF32Problem& p, int amode, int bmode, const char* name,
-                             hipStream_t s) {
+namespace {
+template <int AM, int BMODE, bool GATED, int BM, int BN>
+moe_status_t launch_tile(GemmF32Problem& p, const char* name, hipStream_t s) {
+  p.m_tiles = (p.m_rows + BM - 1) / BM;
   p.n_tiles = (p.N + BN - 1) / BN;
   p.tiles = p.groups * p.m_tiles * p.n_tiles;
   if (p.tiles == 0) return MOE_OK;
+  MOE_LAUNCH(name, (gemm_f32_kernel<AM, BMODE, GATED, BM, BN>), dim3(p.tiles), dim3(256), 0, s, p);
+  return MOE_OK;
+}
+
+// 128 x 128 tiles when the grid still holds two of them per CU (they read half as many
+// LDS values per MFMA as 64 x 64 tiles); gated products take 128 x 64 (two B matrices).
+template <int AM, int BMODE, bool GATED>
+moe_status_t launch_sized(GemmF32Problem& p, const char* name, hipStream_t s) {
+  const long big = long(p.groups) * ((p.m_rows + 127) / 128) * ((p.N + 127) / 128);
+  if (p.m_rows >= 128 && p.N >= 128 && big >= 512) {
+    if constexpr (GATED)
+      return launch_tile<AM, BMODE, GATED, 128, 64>(p, name, s);
+    else
+      return launch_tile<AM, BMODE, GATED, 128, 128>(p, name, s);
+  }
+  return launch_tile<AM, BMODE, GATED, 64, 64>(p, name, s);
+}
+}  // namespace
+
+moe_status_t launch_gemm_f32(GemmF32Problem& p, int amode, int bmode, const char* name,
+                             hipStream_t s) {
   const bool gated = p.epi == EPI_SWIGLU || p.epi == EPI_SWIGLU_BWD;
   if (gated && (!p.B1 || amode != A_ROWS || bmode != B_KN)) return MOE_ERR_UNSUPPORTED;
   if ((p.epi == EPI_GELU_BWD || p.epi == EPI_SWIGLU_BWD) && (!p.G || amode != A_ROWS))
     return MOE_ERR_UNSUPPORTED;
   if (p.epi == EPI_SWIGLU_BWD && !p.C2) return MOE_ERR_UNSUPPORTED;
-  const dim3 grid(p.tiles), block(256);
+  if (p.m_rows < 0) return MOE_ERR_INVALID_ARG;
   if (amode == A_ROWS && bmode == B_KN) {
-    if (gated) {
-      MOE_LAUNCH(name, (gemm_f32_kernel<A_ROWS, B_KN, true>), grid, block, 0, s, p);
-    } else {
-      MOE_LAUNCH(name, (gemm_f32_kernel<A_ROWS, B_KN, false>), grid, block, 0, s, p);
-    }
-  } else if (amode == A_ROWS && bmode == B_NK) {
-    MOE_LAUNCH(name, (gemm_f32_kernel<A_ROWS, B_NK, false>), grid, block, 0, s, p);
-  } else if (amode == A_KROWS && bmode == B_KROWS) {
-    MOE_LAUNCH(name, (gemm_f32_kernel<A_KROWS, B_KROWS, false>), grid, block, 0, s, p);
-  } else {
-    return MOE_ERR_UNSUPPORTED;
+    if (gated) return launch_sized<A_ROWS, B_KN, true>(p, name, s);
+    return launch_sized<A_ROWS, B_KN, false>(p, name, s);
   }
-  return MOE_OK;
+  if (amode == A_ROWS && bmode == B_NK) return launch_sized<A_ROWS, B_NK, false>(p, name, s);
+  if (amode == A_KROWS && bmode == B_KROWS) return launch_sized<A_KROWS, B_KROWS, false>(p, name, s);
+  return MOE_ERR_UNSUPPORTED;
 }
 
 }  // namespace moe

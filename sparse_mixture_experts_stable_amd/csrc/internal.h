@@ -136,7 +136,8 @@ struct GemmF32Problem {
   const int32_t* g_count;   // A_ROWS: M per group; A_KROWS: K per group (NULL: g_const)
   int32_t g_const;
   int32_t M;                // A_KROWS: fixed M
-  int32_t m_tiles;
+  int32_t m_rows;           // rows to tile: A_ROWS the most rows of any group, A_KROWS M
+  int32_t m_tiles;          // filled by the launcher for its tile height
   const float* B;
   const float* B1;          // gated kernels: second weight (the SwiGLU up projection)
   int64_t ldb;
@@ -157,7 +158,6 @@ struct GemmF32Problem {
   int32_t epi;
   int32_t tiles;
 };
-constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 32;
 moe_status_t launch_gemm_f32(GemmF32Problem& p, int amode, int bmode, const char* name,
                              hipStream_t s);
 // Column sums per group: out[g*out_gstride + n] = sum over rows r < M_g (in row order,
