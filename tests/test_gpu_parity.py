@@ -346,3 +346,37 @@ def test_forward_is_deterministic():
                 assert torch.equal(ta[e, : used[e]], tb[e, : used[e]])
         else:
             assert torch.equal(ta, tb), key
+
+
+def test_backward_is_deterministic():
+    """Every reduction of the backward has a fixed order (no atomics): two calls give
+    the same bits, for MLP experts with a shared expert, router weights and survivor
+    renormalisation under the sigmoid router, with the aux and z-loss terms."""
+    ops = _ops()
+    w = BWD["swiglu_shared"]
+    inp = make_inputs(w)
+    g = H.gpu_inputs(inp)
+    C = ops.capacity(w.T, w.k, w.E, w.cf)
+    out = ops.forward(g["x"], H.experts_dict(w, g), k=w.k, capacity=C, w_router=g["w_router"],
+                      shared=H.shared_dict(w, g), scoring="sigmoid", renormalize_kept=True,
+                      z_loss=True)
+    runs = []
+    for _ in range(2):
+        gr = ops.backward(g["dy"], g["x"], H.experts_dict(w, g), out, k=w.k, aux_grad_scale=0.5,
+                          shared=H.shared_dict(w, g), w_router=g["w_router"], z_grad_scale=0.3)
+        torch.cuda.synchronize()
+        runs.append(gr)
+    a, b = runs
+    for key in ("dx", "dgate", "dlogits", "dw_router"):
+        assert torch.equal(a[key], b[key]), key
+    for key in a["dexperts"]:
+        assert torch.equal(a["dexperts"][key], b["dexperts"][key]), key
+    for key in a["dshared"]:
+        assert torch.equal(a["dshared"][key], b["dshared"][key]), key
+    # and the forward's z-loss
+    out2 = ops.forward(g["x"], H.experts_dict(w, g), k=w.k, capacity=C, w_router=g["w_router"],
+                       shared=H.shared_dict(w, g), scoring="sigmoid", renormalize_kept=True,
+                       z_loss=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out["z_loss"], out2["z_loss"])
+    assert torch.equal(out["y"], out2["y"])
