@@ -94,17 +94,21 @@ __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
 
 }  // namespace
 
-// L lanes per token, V logits per lane (E <= L*V), KR result slots per lane (k <= L*KR).
+// L lanes per token, V logits per lane (E <= L*V), KR result slots per lane (k <= L*KR),
+// NT threads per block (NT / L tokens per round; the block's kRouteTokens tokens take
+// kRouteTokens * L / NT rounds, one when NT = kRouteTokens * L, so more waves are in
+// flight for the latency-bound selection rounds).
 // VAR: the router variants are compiled in (sigmoid scoring, selection bias, z partials,
 // chosen at run time from o); without it the kernel is the plain softmax router.
-template <int L, int V, int KR, bool VAR>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
+template <int L, int V, int KR, bool VAR, int NT>
+__global__ __launch_bounds__(NT) void route_kernel(const float* __restrict__ logits, int T,
                                                     int E, int k, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
                                                     int32_t* __restrict__ cnt_part,
                                                     float* __restrict__ prob_part, RouteOpts o,
                                                     float* __restrict__ zpart) {
-  constexpr int TPR = 256 / L;  // tokens per round of the block
+  constexpr int TPR = NT / L;  // tokens per round of the block
+  static_assert(kRouteTokens % TPR == 0, "whole rounds");
   __shared__ int s_hist[L * V];
   __shared__ float s_prob[TPR][L * V];
   __shared__ float s_z[TPR];
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int tid = threadIdx.x;
   const int grp = tid / L;
   const int li = tid % L;
-  for (int e = tid; e < L * V; e += 256) s_hist[e] = 0;
+  for (int e = tid; e < L * V; e += NT) s_hist[e] = 0;
   __syncthreads();
 
   float acc[V];
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   for (int i = 0; i < V; ++i) s_prob[grp][li * V + i] = acc[i];
   __syncthreads();
   const size_t base = size_t(blockIdx.x) * E;
-  for (int e = tid; e < E; e += 256) {
+  for (int e = tid; e < E; e += NT) {
     float v = 0.f;
     for (int g2 = 0; g2 < TPR; ++g2) v += s_prob[g2][e];
     prob_part[base + e] = v;
@@ -463,13 +467,15 @@ static moe_status_t launch_route_lv(const float* logits, int T, int E, int k, in
                                     hipStream_t s) {
   const int nb = route_blocks(T);
   const bool var = o.scoring != MOE_SCORE_SOFTMAX || o.bias || o.with_z;
+  // one round per block where the LDS staging of the probability sums fits
+  constexpr int NT = (L == 16 || L == 32) ? 512 : 256;
 #define MOE_ROUTE(KRV)                                                                        \
   if (var) {                                                                                \
-    MOE_LAUNCH("route", (route_kernel<L, V, KRV, true>), dim3(nb), dim3(256), 0, s, logits, T, \
-               E, k, idx, gate, w.cnt_part, w.prob_part, o, w.zpart);                        \
-  } else {                                                                                  \
-    MOE_LAUNCH("route", (route_kernel<L, V, KRV, false>), dim3(nb), dim3(256), 0, s, logits,   \
+    MOE_LAUNCH("route", (route_kernel<L, V, KRV, true, NT>), dim3(nb), dim3(NT), 0, s, logits, \
                T, E, k, idx, gate, w.cnt_part, w.prob_part, o, w.zpart);                     \
+  } else {                                                                                  \
+    MOE_LAUNCH("route", (route_kernel<L, V, KRV, false, NT>), dim3(nb), dim3(NT), 0, s,        \
+               logits, T, E, k, idx, gate, w.cnt_part, w.prob_part, o, w.zpart);             \
   }
   if (k <= L) {
     MOE_ROUTE(1)
