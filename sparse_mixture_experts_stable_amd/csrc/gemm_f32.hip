@@ -44,6 +44,9 @@ __device__ __forceinline__ int logical_block_f32(int bid, int nblk) {
 __device__ __forceinline__ float4 ld4(const float* p) {
   return *reinterpret_cast<const float4*>(p);
 }
+__device__ __forceinline__ f32x4 ld4v(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
 
 // d/dz of z * Phi(z): Phi(z) + z phi(z), with the standard normal cdf / pdf.
 __device__ __forceinline__ float gelu_erf_grad(float z) {
@@ -109,50 +112,86 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   }
   const float* b_base = P.B + size_t(g) * P.b_gstride;
   const float* b1_base = GATED ? P.B1 + size_t(g) * P.b_gstride : nullptr;
-  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int* a_map = (AM == A_KROWS && P.row_map) ? P.row_map + size_t(g) * P.row_map_ld : nullptr;
+  const int* b_map = (BMODE == B_KROWS && P.b_row_map) ? P.b_row_map + size_t(g) * P.row_map_ld : nullptr;
+  const float* b_gate = b_map ? P.gate : nullptr;
 
-  float4 ra[AL], rb[NB][BL];
-  auto load = [&](int kt) {
+  // Staging registers are plain vectors, each filled by one guarded 16-byte load; a
+  // zero default keeps the guard a predicated load (no select between addresses, which
+  // would turn into generic-address-space loads).
+  // Gathered K rows (A_KROWS, B_KROWS): the map entries of a k-tile are fetched one step
+  // before its data, and load() first takes them into source rows, then requests the
+  // entries of the following k-tile, then the data; the gate of a B row is applied when
+  // the row is written to LDS. So no load waits on a load issued in the same step.
+  f32x4 ra[AL], rb[NB][BL];
+  int ia[AL], ib[BL];  // raw map entries (or k itself without a map) of the next k-tile
+  float sc[BL];        // gates of the B rows held in rb
+  auto fetch_map = [&](int kt) {
     const int k0 = kt * BK;
+    if constexpr (AM == A_KROWS) {
+#pragma unroll
+      for (int h = 0; h < AL; ++h) {
+        const int kk = k0 + am_k + AM_STEP * h;
+        ia[h] = kk;
+        if (a_map && kk < Kg) ia[h] = a_map[kk];
+      }
+    }
+    if constexpr (BMODE == B_KROWS) {
+#pragma unroll
+      for (int h = 0; h < BL; ++h) {
+        const int kk = k0 + bn_k + BN_STEP * h;
+        ib[h] = kk;
+        if (b_map && kk < Kg) ib[h] = b_map[kk];
+      }
+    }
+  };
+  auto load = [&](int kt, bool fetch_next) {
+    const int k0 = kt * BK;
+    int sa[AL], sb[BL], gb[BL];
+    if constexpr (AM == A_KROWS) {
+#pragma unroll
+      for (int h = 0; h < AL; ++h) sa[h] = a_map ? ia[h] / P.row_div : ia[h];
+    }
+    if constexpr (BMODE == B_KROWS) {
+#pragma unroll
+      for (int h = 0; h < BL; ++h) {
+        gb[h] = ib[h];
+        sb[h] = b_map ? ib[h] / P.row_div : ib[h];
+      }
+    }
+    if ((AM == A_KROWS || BMODE == B_KROWS) && fetch_next) fetch_map(kt + 1);
 #pragma unroll
     for (int h = 0; h < AL; ++h) {
+      ra[h] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (AM == A_ROWS) {
-        ra[h] = (k0 + kr_q * 4 < Kg) ? ld4(a_row_ptr[h] + k0) : zero;
+        if (k0 + kr_q * 4 < Kg) ra[h] = ld4v(a_row_ptr[h] + k0);
       } else {
         const int kk = k0 + am_k + AM_STEP * h;
-        ra[h] = zero;
-        if (kk < Kg && m0 + am_q * 4 < M) {
-          const int src = P.row_map ? P.row_map[size_t(g) * P.row_map_ld + kk] / P.row_div : kk;
-          ra[h] = ld4(a_base + size_t(src) * P.lda + m0 + am_q * 4);
-        }
+        if (kk < Kg && m0 + am_q * 4 < M) ra[h] = ld4v(a_base + size_t(sa[h]) * P.lda + m0 + am_q * 4);
       }
     }
 #pragma unroll
     for (int h = 0; h < BL; ++h) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) rb[b][h] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (BMODE == B_KN) {
         const int kk = k0 + bn_k + BN_STEP * h;
         const int n = n0 + bn_q * 4;
-        const bool ok = kk < Kg && n < N;
-        rb[0][h] = ok ? ld4(b_base + size_t(kk) * P.ldb + n) : zero;
-        if constexpr (GATED) rb[1][h] = ok ? ld4(b1_base + size_t(kk) * P.ldb + n) : zero;
+        if (kk < Kg && n < N) {
+          rb[0][h] = ld4v(b_base + size_t(kk) * P.ldb + n);
+          if constexpr (GATED) rb[NB - 1][h] = ld4v(b1_base + size_t(kk) * P.ldb + n);
+        }
       } else if (BMODE == B_NK) {
         const int n = n0 + kr_row + 32 * h;
         const int kq = k0 + kr_q * 4;
-        rb[0][h] = (n < N && kq < Kg) ? ld4(b_base + size_t(n) * P.ldb + kq) : zero;
+        if (n < N && kq < Kg) rb[0][h] = ld4v(b_base + size_t(n) * P.ldb + kq);
       } else {
         const int kk = k0 + bn_k + BN_STEP * h;
         const int n = n0 + bn_q * 4;
-        rb[0][h] = zero;
+        sc[h] = 1.f;
         if (kk < Kg && n < N) {
-          int src = kk;
-          float sc = 1.f;
-          if (P.b_row_map) {
-            const int a = P.b_row_map[size_t(g) * P.row_map_ld + kk];
-            src = a / P.row_div;
-            if (P.gate) sc = P.gate[a];
-          }
-          const float4 v = ld4(b_base + size_t(src) * P.ldb + n);
-          rb[0][h] = make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc);
+          if (b_gate) sc[h] = b_gate[gb[h]];
+          rb[0][h] = ld4v(b_base + size_t(sb[h]) * P.ldb + n);
         }
       }
     }
@@ -161,13 +200,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
 #pragma unroll
     for (int h = 0; h < AL; ++h) {
       const int off = AK ? (kr_row + 32 * h) * KP + kr_q * 4 : (am_k + AM_STEP * h) * NPA + am_q * 4;
-      *reinterpret_cast<float4*>(&As[buf][off]) = ra[h];
+      *reinterpret_cast<f32x4*>(&As[buf][off]) = ra[h];
     }
 #pragma unroll
     for (int h = 0; h < BL; ++h) {
       const int off = BK_ ? (kr_row + 32 * h) * KP + kr_q * 4 : (bn_k + BN_STEP * h) * NPB + bn_q * 4;
+      if constexpr (BMODE == B_KROWS) {
+        *reinterpret_cast<f32x4*>(&Bs[0][buf][off]) = rb[0][h] * sc[h];
+      } else {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) *reinterpret_cast<float4*>(&Bs[b][buf][off]) = rb[b][h];
+        for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(&Bs[b][buf][off]) = rb[b][h];
+      }
     }
   };
 
@@ -182,12 +225,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   const int nk = (Kg + BK - 1) / BK;
   const int fr = lane & 15, fc = lane >> 4;
   if (nk > 0) {
-    load(0);
+    fetch_map(0);
+    load(0, nk > 1);
     store(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) load(kt + 1);
+      if (kt + 1 < nk) load(kt + 1, kt + 2 < nk);
 #pragma unroll
       for (int ks = 0; ks < BK / 4; ++ks) {
         const int kl = ks * 4 + fc;
