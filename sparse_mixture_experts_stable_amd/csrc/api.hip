@@ -2,6 +2,7 @@
 // every entry point. No entry point allocates device memory or synchronises (except
 // moe_read_error and moe_profile_read, which exist to wait).
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -638,6 +639,7 @@ struct BwdSet {
   const int32_t* count;      // expert_used or NULL (then every group has `cnt_const` rows)
   int cnt_const;
   const float* gate;         // topk_gate or NULL
+  float* kpart;              // split-K workspace for constant-K weight gradients, or NULL
   float *dw_in, *dw_up, *dw_out, *db_in, *db_out;
   float *h, *g, *u;          // [E, rows, F] scratch: H, dH -> dZ / dA, dU
   float* dxr;                // [E, rows, D] input gradient of each row
@@ -649,6 +651,7 @@ struct BwdWs {
   float *h, *g, *u;
   float *sh_h, *sh_g, *sh_u, *sh_dx;
   float* part;
+  float* kpart;              // split-K partials of the constant-K weight gradients
   size_t bytes;
 };
 
@@ -683,6 +686,14 @@ BwdWs carve_bwd(const moe_backward_args_t* a, void* ws) {
     const size_t pd = colsum_part_floats(int(E), int(C), int(D));
     w.part = take(pf > pd ? pf : pd);
   }
+  // the shared expert's and the router's weight gradients reduce over all T rows
+  size_t kp = 0;
+  if (a->shared.w_in) {
+    const int Fs = a->shared.d_hidden;
+    kp = std::max(f32_kpart_floats(1, Fs, int(D), int(T)), f32_kpart_floats(1, int(D), Fs, int(T)));
+  }
+  if (a->w_router) kp = std::max(kp, f32_kpart_floats(1, int(D), int(E), int(T)));
+  if (kp) w.kpart = take(kp);
   w.bytes = off + 256;
   return w;
 }
@@ -769,6 +780,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
   p.C = S.dw_out;
   p.ldc = D;
   p.c_gstride = int64_t(F) * D;
+  p.kpart = S.kpart;
   st = launch_gemm_f32(p, A_KROWS, B_KROWS, nm.dw_out, s);
   if (st != MOE_OK) return st;
 
@@ -793,6 +805,7 @@ moe_status_t mlp_backward(const BwdSet& S, const float* x, const float* dy, int6
     p.C = w == 0 ? S.dw_in : S.dw_up;
     p.ldc = F;
     p.c_gstride = int64_t(D) * F;
+    p.kpart = S.kpart;
     st = launch_gemm_f32(p, A_KROWS, B_KROWS, w == 0 ? nm.dw_in : nm.dw_up, s);
     if (st != MOE_OK) return st;
   }
@@ -1001,6 +1014,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
     sh.g = w.sh_g;
     sh.u = w.sh_u;
     sh.dxr = w.sh_dx;
+    sh.kpart = w.kpart;
     st = mlp_backward(sh, x, dy, a->ld, nullptr, s);
     if (st != MOE_OK) return st;
   }
@@ -1028,6 +1042,7 @@ moe_status_t moe_backward(const moe_backward_args_t* a, void* ws, size_t ws_byte
     pr.epi = EPI_STORE;
     pr.C = static_cast<float*>(a->dw_router);
     pr.ldc = E;
+    pr.kpart = w.kpart;
     st = launch_gemm_f32(pr, A_KROWS, B_KROWS, "bwd_dw_router_gemm", s);
     if (st != MOE_OK) return st;
     // dx += dlogits W_r^T

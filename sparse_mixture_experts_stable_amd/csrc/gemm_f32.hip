@@ -69,8 +69,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   static_assert((BM == 64 || BM == 128) && (BN == 64 || BN == 128), "tile size");
   __shared__ float As[2][A_SZ];
   __shared__ float Bs[NB][2][B_SZ];
-  const int lid = logical_block_f32(blockIdx.x, gridDim.x);
+  int lid = logical_block_f32(blockIdx.x, gridDim.x);
   const int per_group = P.m_tiles * P.n_tiles;
+  // split K: blocks split * tiles .. + tiles - 1 take k rows [split * k_chunk, + k_chunk)
+  const bool split_k = AM == A_KROWS && P.k_splits > 1;
+  int split = 0;
+  if (split_k) {
+    split = lid / (P.groups * per_group);
+    lid -= split * (P.groups * per_group);
+  }
   const int g = lid / per_group;
   int rem = lid - g * per_group;
   const int nt = rem / P.m_tiles;
@@ -90,6 +97,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
     Kg = P.g_count ? P.g_count[g] : P.g_const;
   }
   const int N = P.N;
+  int kbeg = 0, kend = Kg;  // this block's k rows
+  if (split_k) {
+    kbeg = split * P.k_chunk;
+    kend = min(Kg, kbeg + P.k_chunk);
+  }
 
   // ---- per-thread load coordinates ----
   // [row][k] operands: row = tid / 8 + 32 h, k quad = tid % 8
@@ -127,13 +139,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   int ia[AL], ib[BL];  // raw map entries (or k itself without a map) of the next k-tile
   float sc[BL];        // gates of the B rows held in rb
   auto fetch_map = [&](int kt) {
-    const int k0 = kt * BK;
+    const int k0 = kbeg + kt * BK;
     if constexpr (AM == A_KROWS) {
 #pragma unroll
       for (int h = 0; h < AL; ++h) {
         const int kk = k0 + am_k + AM_STEP * h;
         ia[h] = kk;
-        if (a_map && kk < Kg) ia[h] = a_map[kk];
+        if (a_map && kk < kend) ia[h] = a_map[kk];
       }
     }
     if constexpr (BMODE == B_KROWS) {
@@ -141,12 +153,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
       for (int h = 0; h < BL; ++h) {
         const int kk = k0 + bn_k + BN_STEP * h;
         ib[h] = kk;
-        if (b_map && kk < Kg) ib[h] = b_map[kk];
+        if (b_map && kk < kend) ib[h] = b_map[kk];
       }
     }
   };
   auto load = [&](int kt, bool fetch_next) {
-    const int k0 = kt * BK;
+    const int k0 = kbeg + kt * BK;
     int sa[AL], sb[BL], gb[BL];
     if constexpr (AM == A_KROWS) {
 #pragma unroll
@@ -164,10 +176,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
     for (int h = 0; h < AL; ++h) {
       ra[h] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (AM == A_ROWS) {
-        if (k0 + kr_q * 4 < Kg) ra[h] = ld4v(a_row_ptr[h] + k0);
+        if (k0 + kr_q * 4 < kend) ra[h] = ld4v(a_row_ptr[h] + k0);
       } else {
         const int kk = k0 + am_k + AM_STEP * h;
-        if (kk < Kg && m0 + am_q * 4 < M) ra[h] = ld4v(a_base + size_t(sa[h]) * P.lda + m0 + am_q * 4);
+        if (kk < kend && m0 + am_q * 4 < M) ra[h] = ld4v(a_base + size_t(sa[h]) * P.lda + m0 + am_q * 4);
       }
     }
 #pragma unroll
@@ -177,19 +189,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
       if (BMODE == B_KN) {
         const int kk = k0 + bn_k + BN_STEP * h;
         const int n = n0 + bn_q * 4;
-        if (kk < Kg && n < N) {
+        if (kk < kend && n < N) {
           rb[0][h] = ld4v(b_base + size_t(kk) * P.ldb + n);
           if constexpr (GATED) rb[NB - 1][h] = ld4v(b1_base + size_t(kk) * P.ldb + n);
         }
       } else if (BMODE == B_NK) {
         const int n = n0 + kr_row + 32 * h;
         const int kq = k0 + kr_q * 4;
-        if (n < N && kq < Kg) rb[0][h] = ld4v(b_base + size_t(n) * P.ldb + kq);
+        if (n < N && kq < kend) rb[0][h] = ld4v(b_base + size_t(n) * P.ldb + kq);
       } else {
         const int kk = k0 + bn_k + BN_STEP * h;
         const int n = n0 + bn_q * 4;
         sc[h] = 1.f;
-        if (kk < Kg && n < N) {
+        if (kk < kend && n < N) {
           if (b_gate) sc[h] = b_gate[gb[h]];
           rb[0][h] = ld4v(b_base + size_t(sb[h]) * P.ldb + n);
         }
@@ -222,7 +234,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (Kg + BK - 1) / BK;
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int fr = lane & 15, fc = lane >> 4;
   if (nk > 0) {
     fetch_map(0);
@@ -261,8 +273,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
     }
   }
 
-  // ---- epilogue: lane holds C[m][n..n+3] ----
+  // ---- epilogue: lane holds C[m][n..n+3] (a split-K block: its partial) ----
   const int epi = P.epi;
+  float* Cout = P.C;
+  int64_t ldc = P.ldc, c_gstride = P.c_gstride;
+  if (split_k) {
+    Cout = P.kpart + size_t(split) * P.groups * size_t(P.M) * N;
+    ldc = N;
+    c_gstride = int64_t(P.M) * N;
+  }
   const bool bwd = epi == EPI_GELU_BWD || epi == EPI_SWIGLU_BWD;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -275,7 +294,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
     for (int j = 0; j < TN; ++j) {
       const int n = n0 + wn * (BN / 2) + j * 16 + fc * 4;
       if (n >= N) continue;
-      const size_t off = size_t(g) * P.c_gstride + size_t(m) * P.ldc + n;
+      const size_t off = size_t(g) * c_gstride + size_t(m) * ldc + n;
       float v[4] = {acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]};
       if ((epi == EPI_BIAS || epi == EPI_GELU_BIAS || epi == EPI_GELU_BWD) && P.bias) {
         const float4 bb = ld4(P.bias + size_t(g) * P.bias_gstride + n);
@@ -326,19 +345,52 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
           *reinterpret_cast<float4*>(P.C2 + off) = make_float4(du[0], du[1], du[2], du[3]);
         }
       }
-      *reinterpret_cast<float4*>(P.C + off) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(Cout + off) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
 
+// Sum of the split-K partials in split order: out[i] = part[0][i] + part[1][i] + ...
+__global__ __launch_bounds__(256) void ksum_kernel(const float* __restrict__ part, int splits,
+                                                   size_t n4, float* __restrict__ out) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += size_t(gridDim.x) * 256) {
+    f32x4 v = ld4v(part + 4 * i);
+    for (int q = 1; q < splits; ++q) v += ld4v(part + (size_t(q) * n4 + i) * 4);
+    *reinterpret_cast<f32x4*>(out + 4 * i) = v;
+  }
+}
+
 namespace {
+// K split of a constant-K A_KROWS product: enough splits for about two blocks per CU
+// (512 blocks), each split keeping at least 512 k rows (16 k-tiles), at most 16 splits.
+// The tiles are 128 x 128 when both M and N allow it, else 64 x 64.
+struct KSplitPlan {
+  int splits, chunk;
+  bool big;
+};
+KSplitPlan ksplit_plan(int groups, int M, int N, int K) {
+  KSplitPlan r{1, 0, M >= 128 && N >= 128};
+  const int bm = r.big ? 128 : 64;
+  const long tiles = long(groups) * ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
+  if (tiles <= 0 || tiles >= 256 || K < 1024) return r;
+  long sp = (512 + tiles - 1) / tiles;
+  if (sp > K / 512) sp = K / 512;
+  if (sp > 16) sp = 16;
+  if (sp < 2) return r;
+  const int chunk = int((K + sp - 1) / sp + BK - 1) / BK * BK;
+  r.splits = (K + chunk - 1) / chunk;
+  r.chunk = chunk;
+  return r;
+}
+
 template <int AM, int BMODE, bool GATED, int BM, int BN>
 moe_status_t launch_tile(GemmF32Problem& p, const char* name, hipStream_t s) {
   p.m_tiles = (p.m_rows + BM - 1) / BM;
   p.n_tiles = (p.N + BN - 1) / BN;
   p.tiles = p.groups * p.m_tiles * p.n_tiles;
   if (p.tiles == 0) return MOE_OK;
-  MOE_LAUNCH(name, (gemm_f32_kernel<AM, BMODE, GATED, BM, BN>), dim3(p.tiles), dim3(256), 0, s, p);
+  const int blocks = p.tiles * (p.k_splits > 1 ? p.k_splits : 1);
+  MOE_LAUNCH(name, (gemm_f32_kernel<AM, BMODE, GATED, BM, BN>), dim3(blocks), dim3(256), 0, s, p);
   return MOE_OK;
 }
 
@@ -370,8 +422,32 @@ moe_status_t launch_gemm_f32(GemmF32Problem& p, int amode, int bmode, const char
     return launch_sized<A_ROWS, B_KN, false>(p, name, s);
   }
   if (amode == A_ROWS && bmode == B_NK) return launch_sized<A_ROWS, B_NK, false>(p, name, s);
-  if (amode == A_KROWS && bmode == B_KROWS) return launch_sized<A_KROWS, B_KROWS, false>(p, name, s);
+  if (amode == A_KROWS && bmode == B_KROWS) {
+    p.k_splits = 1;
+    p.k_chunk = 0;
+    const bool dense_c = p.ldc == p.N && (p.groups == 1 || p.c_gstride == int64_t(p.M) * p.N);
+    if (p.kpart && !p.g_count && p.epi == EPI_STORE && dense_c && p.M == p.m_rows) {
+      const KSplitPlan kp = ksplit_plan(p.groups, p.M, p.N, p.g_const);
+      if (kp.splits > 1) {
+        p.k_splits = kp.splits;
+        p.k_chunk = kp.chunk;
+        const moe_status_t st = kp.big ? launch_tile<A_KROWS, B_KROWS, false, 128, 128>(p, name, s)
+                                       : launch_tile<A_KROWS, B_KROWS, false, 64, 64>(p, name, s);
+        if (st != MOE_OK || p.tiles == 0) return st;
+        const size_t n4 = size_t(p.groups) * p.M * p.N / 4;
+        const int grid = int(n4 / 256 < 2048 ? (n4 + 255) / 256 : 2048);
+        MOE_LAUNCH("ksum_f32", ksum_kernel, dim3(grid), dim3(256), 0, s, p.kpart, p.k_splits, n4, p.C);
+        return MOE_OK;
+      }
+    }
+    return launch_sized<A_KROWS, B_KROWS, false>(p, name, s);
+  }
   return MOE_ERR_UNSUPPORTED;
+}
+
+size_t f32_kpart_floats(int groups, int M, int N, int K) {
+  const KSplitPlan kp = ksplit_plan(groups, M, N, K);
+  return kp.splits > 1 ? size_t(kp.splits) * groups * size_t(M) * N : 0;
 }
 
 }  // namespace moe

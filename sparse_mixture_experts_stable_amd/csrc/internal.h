@@ -157,9 +157,20 @@ struct GemmF32Problem {
   int32_t groups;
   int32_t epi;
   int32_t tiles;
+  // A_KROWS with a constant K (g_count NULL), EPI_STORE and C dense ([groups][M][N]):
+  // when the output has too few tiles to fill the GPU, the launcher splits K into
+  // k_splits ranges of k_chunk rows, each writing a partial to kpart, and sums them in a
+  // fixed order into C. kpart (caller-owned, >= f32_kpart_floats(...) floats) may be
+  // NULL, which disables the split. k_splits and k_chunk are filled by the launcher.
+  float* kpart;
+  int32_t k_splits;
+  int32_t k_chunk;
 };
 moe_status_t launch_gemm_f32(GemmF32Problem& p, int amode, int bmode, const char* name,
                              hipStream_t s);
+// Floats of kpart that launch_gemm_f32 uses for a constant-K A_KROWS product of this
+// shape (0 if it does not split it).
+size_t f32_kpart_floats(int groups, int M, int N, int K);
 // Column sums per group: out[g*out_gstride + n] = sum over rows r < M_g (in row order,
 // fixed chunking) of scale(r) * row(r)[n], rows addressed like B_KROWS (map / identity,
 // gate). Deterministic. part: >= colsum_part_floats(groups, max_rows, N) floats.

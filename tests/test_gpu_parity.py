@@ -174,13 +174,17 @@ BWD = {
     "gelu_odd": WORKLOADS[1].scaled(T=300, D=64, E=8, F=80, backward=True),
     "swiglu_tiny": WORKLOADS[3].scaled(T=129, D=16, E=4, k=1, F=48, shared_F=32, dtype="f32",
                                        backward=True, cf=1.5),
+    # the shared expert's and the router's weight gradients (K = T = 5000 rows, few output
+    # tiles) run split over K: 9 ranges of 576 rows, the last one ragged (392 rows)
+    "split_k": WORKLOADS[3].scaled(T=5000, D=256, E=16, F=64, shared_F=128, dtype="f32",
+                                   backward=True),
 }
 
 
 @pytest.mark.parametrize("case,aux_scale,router", [
     ("gelu_bias", 0.0, False), ("gelu_bias", 1.0, True), ("gelu_wide", 0.0, True),
     ("swiglu_shared", 0.0, False), ("swiglu_shared", 0.5, True), ("linear", 0.0, True),
-    ("gelu_odd", 0.0, True), ("swiglu_tiny", 1.0, True),
+    ("gelu_odd", 0.0, True), ("swiglu_tiny", 1.0, True), ("split_k", 0.0, True),
 ])
 def test_backward_general(case, aux_scale, router):
     _backward_general(BWD[case], aux_scale, router)
