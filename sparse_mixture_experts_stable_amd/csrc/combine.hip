@@ -22,13 +22,25 @@
 
 namespace moe {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Loads of rows that are read exactly once (the expert output rows): non-temporal, so the
+// streamed rows do not evict the rows of x and the shared output the same tokens need.
+__device__ __forceinline__ u32x4 load_once(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 template <typename T>
 struct Vec;
 template <>
 struct Vec<float> {
   static constexpr int N = 4;
   typedef float4 Raw;
-  __device__ static Raw load_raw(const void* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static Raw load_raw(const void* p) {
+    const u32x4 q = load_once(p);
+    return make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z),
+                       __uint_as_float(q.w));
+  }
   __device__ static void fma_raw(float g, const Raw& r, float* acc) {
     acc[0] = fmaf(g, r.x, acc[0]);
     acc[1] = fmaf(g, r.y, acc[1]);
@@ -47,7 +59,10 @@ template <>
 struct Vec<bf16_t> {
   static constexpr int N = 8;
   typedef uint4 Raw;
-  __device__ static Raw load_raw(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static Raw load_raw(const void* p) {
+    const u32x4 q = load_once(p);
+    return make_uint4(q.x, q.y, q.z, q.w);
+  }
   __device__ static void fma_raw(float g, const Raw& r, float* acc) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll

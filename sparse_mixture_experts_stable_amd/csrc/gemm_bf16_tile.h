@@ -24,6 +24,7 @@ namespace tile {
 constexpr int BK = kBf16BK;  // 64
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -294,7 +295,7 @@ __device__ __forceinline__ void epi_math(const GemmProblem& P, const TileId& t, 
 // bf16 epilogue through LDS: the tile is written to `stage` (64 KiB) in rounds of
 // R = 64 KiB / (2 BNQ) rows, each lane's 8-byte pieces placed with the 16-byte chunk
 // index XORed by (row % 16), then read back as 16 bytes per lane along whole rows and
-// stored, so every store instruction writes complete row segments. All threads of the
+// stored (non-temporal), so every store instruction writes complete row segments. All threads of the
 // block take part (it synchronises); `stage` must be free on entry and is free again
 // on return.
 template <class CF, int EPI>
@@ -348,9 +349,12 @@ __device__ __forceinline__ void store_tile_staged(const GemmProblem& P, const Ti
       const int c = lane % CPR;
       const int m = t.m0 + rd * R + ml;
       const int n = t.n0 + 8 * c;
+      // non-temporal: the tile is read back once, by a later kernel, long after this
+      // launch has streamed far more than the caches hold
       if (m < t.M && n < P.N)
-        *reinterpret_cast<uint4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2) =
-            *reinterpret_cast<const uint4*>(stage + ml * RB + 16 * (c ^ (ml & 15)));
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4*>(stage + ml * RB + 16 * (c ^ (ml & 15))),
+            reinterpret_cast<u32x4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2));
     }
   }
   __syncthreads();  // every wave has read the stage back
