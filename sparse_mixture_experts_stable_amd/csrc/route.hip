@@ -70,26 +70,65 @@ __device__ __forceinline__ float log_sigmoid(float s) {
   return fminf(s, 0.f) - log1pf(__expf(-fabsf(s)));
 }
 
+// Lane exchanges inside 16-lane rows (DPP): quad permutations [1,0,3,2] and [2,3,0,1],
+// the half-row mirror (lane i <-> 7 - i) and the row mirror (i <-> 15 - i).
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141,
+              kDppRowMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __uint_as_float(dpp32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return (uint64_t(dpp32<CTRL>(uint32_t(v >> 32))) << 32) | dpp32<CTRL>(uint32_t(v));
+}
+struct MaxF {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct SumF {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxU64 {
+  __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return b > a ? b : a; }
+};
+template <int CTRL, class T>
+__device__ __forceinline__ T dpp_any(T v) {
+  if constexpr (sizeof(T) == 8) return dpp_u64<CTRL>(v);
+  else return dpp_f<CTRL>(v);
+}
+// All-reduce over aligned groups of L lanes (L a power of two): partner exchanges inside
+// each 16-lane row through DPP (pairs, quads, the two quads of a half-row, the two halves
+// of a row), then cross-row shuffles. At every step the two partners combine the same two
+// values, so every lane of the group ends with the same result, bit for bit.
+template <int L, class OP, class T>
+__device__ __forceinline__ T group_reduce(T v, OP op) {
+  if constexpr (L >= 2) v = op(v, dpp_any<kDppQuadXor1>(v));
+  if constexpr (L >= 4) v = op(v, dpp_any<kDppQuadXor2>(v));
+  if constexpr (L >= 8) v = op(v, dpp_any<kDppHalfMirror>(v));
+  if constexpr (L >= 16) v = op(v, dpp_any<kDppRowMirror>(v));
+  if constexpr (L >= 32) v = op(v, T(__shfl_xor(v, 16, L)));
+  if constexpr (L >= 64) v = op(v, T(__shfl_xor(v, 32, L)));
+  return v;
+}
 template <int L>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, L));
-  return v;
+  return group_reduce<L>(v, MaxF{});
 }
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, L);
-  return v;
+  return group_reduce<L>(v, SumF{});
 }
 template <int L>
 __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) {
-    const uint64_t o = __shfl_xor(v, m, L);
-    v = o > v ? o : v;
-  }
-  return v;
+  return group_reduce<L>(v, MaxU64{});
+}
+// Inverse of orderable() (negative zero comes back as +0).
+__device__ __forceinline__ float from_orderable(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
 }  // namespace
@@ -169,24 +208,39 @@ __global__ __launch_bounds__(NT) void route_kernel(const float* __restrict__ log
       my_e[q] = 0;
       my_p[q] = 0.f;
     }
+    // Selection: each lane keeps its best remaining key; a round takes the group maximum,
+    // and only the lane that held it retires that key (its high word cleared, which
+    // ranks it below every live key) and finds its next best.
+    auto lane_best = [&]() {
+      uint64_t b = key[0];
+#pragma unroll
+      for (int i = 1; i < V; ++i) b = key[i] > b ? key[i] : b;
+      return b;
+    };
+    uint64_t lb = lane_best();
     float gsum = 0.f;
     for (int j = 0; j < k; ++j) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int i = 1; i < V; ++i) best = key[i] > best ? key[i] : best;
-      best = group_max_u64<L>(best);
+      const uint64_t best = group_max_u64<L>(lb);
       const int e = int(0xffffffffu - uint32_t(best));
-      const int owner = e / V;
-      const int si = e - owner * V;
-      float pv = 0.f;
+      float pe;
+      if (!bias && !sig) {
+        // the key holds the logit: every lane forms p_e exactly as the owner did
+        pe = __expf(from_orderable(uint32_t(best >> 32)) - mx) * inv;
+      } else {
+        const int owner = e / V;
+        const int si = e - owner * V;
+        float pv = 0.f;
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        if (li == owner && i == si) {
-          pv = sig ? log_sigmoid(s[i]) : p[i];
-          key[i] = 0ull;
-        }
+        for (int i = 0; i < V; ++i)
+          if (li == owner && i == si) pv = sig ? log_sigmoid(s[i]) : p[i];
+        pe = __shfl(pv, owner, L);
       }
-      const float pe = __shfl(pv, owner, L);
+      if (lb == best) {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          if (uint32_t(key[i]) == uint32_t(best)) key[i] &= 0xffffffffull;
+        lb = lane_best();
+      }
       gsum += pe;
 #pragma unroll
       for (int q = 0; q < KR; ++q) {
