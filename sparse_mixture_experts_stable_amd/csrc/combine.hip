@@ -202,7 +202,9 @@ moe_status_t launch_combine(int dt, const void* residual, int64_t ldr, const voi
 // its quotient-rule image (d'_j - sum_kept g'_r d'_r) / K) with G = sum_j g_j dgate_j,
 // then dq_j = (dgate_j - G) / S into the score derivative (softmax Jacobian, or
 // q (1 - q) of the chosen sigmoid scores). Aux and z-loss terms are added per expert.
-template <int EPL>
+// DQ > 0: the token's dy row is held in registers (DQ float4 per lane, D <= 256 DQ) and
+// read from HBM once for all k choices; DQ = 0 streams it again for every choice.
+template <int EPL, int DQ>
 __global__ __launch_bounds__(256) void dgate_router_kernel(DgateArgs A) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -241,6 +243,12 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(DgateArgs A) {
   const float* gr = A.gate + size_t(t) * k;
   float S = 0.f, K = 0.f, Gk = 0.f;
   float dreg[4] = {0.f, 0.f, 0.f, 0.f};
+  float4 dyv[DQ > 0 ? DQ : 1];
+#pragma unroll
+  for (int q = 0; q < DQ; ++q) {
+    const int c = lane * 4 + 256 * q;
+    dyv[q] = c < D ? *reinterpret_cast<const float4*>(dyr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   for (int j = 0; j < k; ++j) {
     const int e = idr[j];
     const int sl = slr[j];
@@ -248,13 +256,31 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(DgateArgs A) {
     float d = 0.f;
     if (kept) {
       const float* orow = A.o + (size_t(e) * C + sl) * D;
-      for (int c = lane * 4; c < D; c += 256) {
-        const float4 a = *reinterpret_cast<const float4*>(dyr + c);
-        const float4 b = *reinterpret_cast<const float4*>(orow + c);
-        d = fmaf(a.x, b.x, d);
-        d = fmaf(a.y, b.y, d);
-        d = fmaf(a.z, b.z, d);
-        d = fmaf(a.w, b.w, d);
+      if constexpr (DQ > 0) {
+        float4 ov[DQ];
+#pragma unroll
+        for (int q = 0; q < DQ; ++q) {
+          const int c = lane * 4 + 256 * q;
+          ov[q] = c < D ? *reinterpret_cast<const float4*>(orow + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int q = 0; q < DQ; ++q) {
+          if (lane * 4 + 256 * q < D) {
+            d = fmaf(dyv[q].x, ov[q].x, d);
+            d = fmaf(dyv[q].y, ov[q].y, d);
+            d = fmaf(dyv[q].z, ov[q].z, d);
+            d = fmaf(dyv[q].w, ov[q].w, d);
+          }
+        }
+      } else {
+        for (int c = lane * 4; c < D; c += 256) {
+          const float4 a = *reinterpret_cast<const float4*>(dyr + c);
+          const float4 b = *reinterpret_cast<const float4*>(orow + c);
+          d = fmaf(a.x, b.x, d);
+          d = fmaf(a.y, b.y, d);
+          d = fmaf(a.z, b.z, d);
+          d = fmaf(a.w, b.w, d);
+        }
       }
       d = wave_sum(d);
       K += gr[j];
@@ -346,8 +372,16 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(DgateArgs A) {
 
 moe_status_t launch_dgate_router_bwd(const DgateArgs& a, hipStream_t s) {
   const dim3 grid((a.T + 3) / 4), block(256);
-#define MOE_DG(EPLV) \
-  MOE_LAUNCH("dgate_router_bwd", dgate_router_kernel<EPLV>, grid, block, 0, s, a)
+#define MOE_DGQ(EPLV, DQV) \
+  MOE_LAUNCH("dgate_router_bwd", (dgate_router_kernel<EPLV, DQV>), grid, block, 0, s, a)
+#define MOE_DG(EPLV)          \
+  if (a.D <= 1024) {          \
+    MOE_DGQ(EPLV, 4);         \
+  } else if (a.D <= 2048) {   \
+    MOE_DGQ(EPLV, 8);         \
+  } else {                    \
+    MOE_DGQ(EPLV, 0);         \
+  }
   if (a.E <= 64) {
     MOE_DG(1);
   } else if (a.E <= 128) {
@@ -360,6 +394,7 @@ moe_status_t launch_dgate_router_bwd(const DgateArgs& a, hipStream_t s) {
     MOE_DG(16);
   }
 #undef MOE_DG
+#undef MOE_DGQ
   return MOE_OK;
 }
 

@@ -178,6 +178,9 @@ BWD = {
     # tiles) run split over K: 9 ranges of 576 rows, the last one ragged (392 rows)
     "split_k": WORKLOADS[3].scaled(T=5000, D=256, E=16, F=64, shared_F=128, dtype="f32",
                                    backward=True),
+    # d_model above 2048: the router backward streams dy for every choice instead of
+    # holding it in registers
+    "wide_d": WORKLOADS[5].scaled(T=96, D=3072, E=4),
 }
 
 
@@ -185,6 +188,7 @@ BWD = {
     ("gelu_bias", 0.0, False), ("gelu_bias", 1.0, True), ("gelu_wide", 0.0, True),
     ("swiglu_shared", 0.0, False), ("swiglu_shared", 0.5, True), ("linear", 0.0, True),
     ("gelu_odd", 0.0, True), ("swiglu_tiny", 1.0, True), ("split_k", 0.0, True),
+    ("wide_d", 0.5, True),
 ])
 def test_backward_general(case, aux_scale, router):
     _backward_general(BWD[case], aux_scale, router)
