@@ -249,42 +249,63 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(DgateArgs A) {
     const int c = lane * 4 + 256 * q;
     dyv[q] = c < D ? *reinterpret_cast<const float4*>(dyr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int j = 0; j < k; ++j) {
-    const int e = idr[j];
-    const int sl = slr[j];
-    const bool kept = sl >= 0 && sl < C;
+  // choice metadata: with k <= 64, lane j holds choice j's expert, slot and gate, which
+  // every lane reads back with readlane, so no round waits on a load of its own
+  const bool meta_in_lanes = k <= 64;
+  int me = 0, msl = -1;
+  float mg = 0.f;
+  if (meta_in_lanes && lane < k) {
+    me = idr[lane];
+    msl = slr[lane];
+    mg = gr[lane];
+  }
+  auto choice = [&](int j, int& e, int& sl, float& g) {
+    if (meta_in_lanes) {
+      e = __builtin_amdgcn_readlane(me, j);
+      sl = __builtin_amdgcn_readlane(msl, j);
+      g = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mg), j));
+    } else {
+      e = idr[j];
+      sl = slr[j];
+      g = gr[j];
+    }
+  };
+  // <dy, o_j> of this lane's columns
+  auto dot_part = [&](const float* orow) {
     float d = 0.f;
-    if (kept) {
-      const float* orow = A.o + (size_t(e) * C + sl) * D;
-      if constexpr (DQ > 0) {
-        float4 ov[DQ];
+    if constexpr (DQ > 0) {
+      float4 ov[DQ];
 #pragma unroll
-        for (int q = 0; q < DQ; ++q) {
-          const int c = lane * 4 + 256 * q;
-          ov[q] = c < D ? *reinterpret_cast<const float4*>(orow + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+      for (int q = 0; q < DQ; ++q) {
+        const int c = lane * 4 + 256 * q;
+        ov[q] = c < D ? *reinterpret_cast<const float4*>(orow + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
-        for (int q = 0; q < DQ; ++q) {
-          if (lane * 4 + 256 * q < D) {
-            d = fmaf(dyv[q].x, ov[q].x, d);
-            d = fmaf(dyv[q].y, ov[q].y, d);
-            d = fmaf(dyv[q].z, ov[q].z, d);
-            d = fmaf(dyv[q].w, ov[q].w, d);
-          }
-        }
-      } else {
-        for (int c = lane * 4; c < D; c += 256) {
-          const float4 a = *reinterpret_cast<const float4*>(dyr + c);
-          const float4 b = *reinterpret_cast<const float4*>(orow + c);
-          d = fmaf(a.x, b.x, d);
-          d = fmaf(a.y, b.y, d);
-          d = fmaf(a.z, b.z, d);
-          d = fmaf(a.w, b.w, d);
+      for (int q = 0; q < DQ; ++q) {
+        if (lane * 4 + 256 * q < D) {
+          d = fmaf(dyv[q].x, ov[q].x, d);
+          d = fmaf(dyv[q].y, ov[q].y, d);
+          d = fmaf(dyv[q].z, ov[q].z, d);
+          d = fmaf(dyv[q].w, ov[q].w, d);
         }
       }
-      d = wave_sum(d);
-      K += gr[j];
-      Gk += gr[j] * d;
+    } else {
+      for (int c = lane * 4; c < D; c += 256) {
+        const float4 a = *reinterpret_cast<const float4*>(dyr + c);
+        const float4 b = *reinterpret_cast<const float4*>(orow + c);
+        d = fmaf(a.x, b.x, d);
+        d = fmaf(a.y, b.y, d);
+        d = fmaf(a.z, b.z, d);
+        d = fmaf(a.w, b.w, d);
+      }
+    }
+    return d;
+  };
+  // the sums over choices, in choice order
+  auto account = [&](int j, int e, bool kept, float g, float d) {
+    if (kept) {
+      K += g;
+      Gk += g * d;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -296,6 +317,22 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(DgateArgs A) {
     q = __shfl(q, e & 63, kWave);
     if (sig) q = 1.0f / (1.0f + __expf(-q));
     S += q;
+  };
+  // two choices per round: both expert rows are requested before either is reduced
+  for (int j = 0; j < k; j += 2) {
+    const bool two = j + 1 < k;
+    int e0, sl0, e1 = 0, sl1 = -1;
+    float g0, g1 = 0.f;
+    choice(j, e0, sl0, g0);
+    if (two) choice(j + 1, e1, sl1, g1);
+    const bool kept0 = sl0 >= 0 && sl0 < C;
+    const bool kept1 = two && sl1 >= 0 && sl1 < C;
+    float d0 = kept0 ? dot_part(A.o + (size_t(e0) * C + sl0) * D) : 0.f;
+    float d1 = kept1 ? dot_part(A.o + (size_t(e1) * C + sl1) * D) : 0.f;
+    if (kept0) d0 = wave_sum(d0);
+    if (kept1) d1 = wave_sum(d1);
+    account(j, e0, kept0, g0, d0);
+    if (two) account(j + 1, e1, kept1, g1, d1);
   }
   // pass 2: dgate_j and G = sum_j g_j dgate_j; effective gates
   float G = 0.f;
@@ -304,10 +341,11 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(DgateArgs A) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (r == (j >> 6)) dv = dreg[r];
-    float d = __shfl(dv, j & 63, kWave);
-    const int sl = slr[j];
+    float d = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dv), j & 63));
+    int e, sl;
+    float g;
+    choice(j, e, sl, g);
     const bool kept = sl >= 0 && sl < C;
-    const float g = gr[j];
     if (A.renorm) d = (kept && K > 0.f) ? (d - Gk / K) / K : 0.f;
     G += g * d;
     if (lane == 0) {
@@ -321,12 +359,14 @@ __global__ __launch_bounds__(256) void dgate_router_kernel(DgateArgs A) {
   }
   // pass 3: dq_j into the score derivative at the chosen experts
   for (int j = 0; j < k; ++j) {
-    const int e = idr[j];
+    int e, sl;
+    float g;
+    choice(j, e, sl, g);
     float dv = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (r == (j >> 6)) dv = dreg[r];
-    const float d = __shfl(dv, j & 63, kWave);
+    const float d = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dv), j & 63));
     const float dq = (d - G) / S;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {

@@ -181,6 +181,9 @@ BWD = {
     # d_model above 2048: the router backward streams dy for every choice instead of
     # holding it in registers
     "wide_d": WORKLOADS[5].scaled(T=96, D=3072, E=4),
+    # k > 64: the router backward reads each choice's metadata from memory, and the
+    # per-choice values span two register slots per lane
+    "many_choices": WORKLOADS[5].scaled(T=64, D=64, E=128, k=72),
 }
 
 
@@ -188,7 +191,7 @@ BWD = {
     ("gelu_bias", 0.0, False), ("gelu_bias", 1.0, True), ("gelu_wide", 0.0, True),
     ("swiglu_shared", 0.0, False), ("swiglu_shared", 0.5, True), ("linear", 0.0, True),
     ("gelu_odd", 0.0, True), ("swiglu_tiny", 1.0, True), ("split_k", 0.0, True),
-    ("wide_d", 0.5, True),
+    ("wide_d", 0.5, True), ("many_choices", 1.0, True),
 ])
 def test_backward_general(case, aux_scale, router):
     _backward_general(BWD[case], aux_scale, router)
