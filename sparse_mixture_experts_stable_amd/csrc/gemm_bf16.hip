@@ -162,13 +162,16 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
     store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, sbias, acc);
 }
 
-// Persistent form of the two-stage kernel: one block per CU walks a strided list of
+// Persistent form of the two-stage kernel: one block per CU works through a list of
 // tiles. XCD x (hardware blocks x, x+8, ...) owns a contiguous range of logical tiles, so
 // the blocks running together on one XCD work on neighbouring tiles, which share weight
-// panels in that XCD's L2. Empty tiles (no rows in the group) are skipped. On the last K
-// step of a tile the DMA request already targets step 0 of the block's next tile, so
-// that tile's first stage streams in while the epilogue of the current one runs; the
-// next tile's gathered row indices are read at the start of the current tile.
+// panels in that XCD's L2. At the start the block ranks the non-empty tiles of its XCD's
+// range in order (a block-wide prefix count) and keeps those of rank bi, bi + nb_x, ...
+// in LDS, so skewed groups (many nearly empty experts) still spread evenly over the
+// XCD's blocks. On the last K step of a tile the DMA request already targets step 0 of
+// the block's next tile, so that tile's first stage streams in while the epilogue of the
+// current one runs; the next tile's gathered row indices are read at the start of the
+// current tile.
 template <class CF, int EPI, bool OF32>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(GemmBatch batch) {
   static_assert(CF::STAGES == 2, "two-stage ring");
@@ -177,15 +180,41 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
   const int nblk = gridDim.x;
   const int x = blockIdx.x & 7, bi = blockIdx.x >> 3;
   const int nb_x = (nblk >> 3) + ((nblk & 7) > x ? 1 : 0);
-  // this block takes entries bi, bi + nb_x, ... of XCD x's tile list
-  int j = bi;
-  TileId tl;
-  for (;; j += nb_x) {
-    const int lt = xcd_tile(batch.total, batch.chunk, x, j);
-    if (lt < 0) return;
-    tl = decode_tile<CF>(batch, lt);
-    if (tl.m0 < tl.M) break;
+  int ranked = 0;  // non-empty tiles in XCD x's range
+  {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    int* s_list = reinterpret_cast<int*>(smem + CF::LDS);
+    int* s_wsum = s_list + batch.list_cap;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int j0 = 0;; j0 += CF::THREADS) {
+      const int lt = xcd_tile(batch.total, batch.chunk, x, j0 + tid);
+      const bool ne = lt >= 0 && tile_nonempty<CF>(batch, lt);
+      const uint64_t bal = __ballot(ne);
+      if (lane == 0) s_wsum[wv] = __popcll(bal);
+      __syncthreads();
+      int before = 0, tot = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < CF::WAVES; ++w2) {
+        const int c = s_wsum[w2];
+        before += w2 < wv ? c : 0;
+        tot += c;
+      }
+      if (ne) {
+        const int r = ranked + before + __popcll(bal & below);
+        if (r % nb_x == bi) s_list[r / nb_x] = lt;
+      }
+      ranked += tot;
+      __syncthreads();  // s_wsum is rewritten by the next pass; s_list complete after the last
+      if (xcd_tile(batch.total, batch.chunk, x, j0 + CF::THREADS) < 0) break;
+    }
   }
+  const int* s_list = reinterpret_cast<const int*>(smem + CF::LDS);
+  const int nmine = ranked > bi ? (ranked - bi + nb_x - 1) / nb_x : 0;
+  if (nmine == 0) return;
+  int qi = 0;  // position in the block's tile list
+  TileId tl = decode_tile<CF>(batch, __builtin_amdgcn_readfirstlane(s_list[0]));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -206,19 +235,10 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
   int g = 0;  // steps done by this block: stage g & 1 holds the current one
   while (true) {
     const GemmProblem& P = batch.p[tl.pi];
-    // the block's next non-empty tile, and its gathered A rows
-    int j2 = j + nb_x;
-    TileId tl2;
-    bool more = false;
-    for (;; j2 += nb_x) {
-      const int lt = xcd_tile(batch.total, batch.chunk, x, j2);
-      if (lt < 0) break;
-      tl2 = decode_tile<CF>(batch, lt);
-      if (tl2.m0 < tl2.M) {
-        more = true;
-        break;
-      }
-    }
+    // the block's next tile, and its gathered A rows
+    const bool more = qi + 1 < nmine;
+    TileId tl2 = tl;
+    if (more) tl2 = decode_tile<CF>(batch, __builtin_amdgcn_readfirstlane(s_list[qi + 1]));
     int rows2[CF::A_INST];
     if (more) {
 #pragma unroll
@@ -253,7 +273,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    j = j2;
+    ++qi;
     tl = tl2;
   }
 }
@@ -300,6 +320,9 @@ moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
   return MOE_OK;
 }
 
+// LDS of a persistent block: the ring plus its tile list (at most 24 KiB of entries)
+constexpr int kPersistentLdsMax = 2 * 65536 + 24576;
+
 int cu_count() {
   static int n = 0;
   if (n == 0) {
@@ -318,13 +341,17 @@ moe_status_t launch_persistent(GemmBatch& b, const char* name, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_persistent_kernel<CF, EPI, OF32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPersistentLdsMax) != hipSuccess)
       return MOE_ERR_HIP;
     attr_set = true;
   }
   const int grid = b.total < cu_count() ? int(b.total) : cu_count();
+  const int nb_min = grid / 8 > 0 ? grid / 8 : 1;  // blocks of the XCD with the fewest
+  b.list_cap = (b.xcd_max + nb_min - 1) / nb_min;
+  const size_t lds = CF::LDS + sizeof(int) * (size_t(b.list_cap) + CF::WAVES);
+  if (lds > size_t(kPersistentLdsMax)) return launch_cfg<CF, EPI, OF32>(b, name, s);
   MOE_LAUNCH(name, (gemm_bf16_persistent_kernel<CF, EPI, OF32>), dim3(grid), dim3(CF::THREADS),
-             CF::LDS, s, b);
+             lds, s, b);
   return MOE_OK;
 }
 

@@ -150,6 +150,23 @@ __device__ __forceinline__ TileId decode_tile(const GemmBatch& batch, int lid) {
   return t;
 }
 
+// Whether logical tile `lid` holds rows (its first row is below the group's row count),
+// evaluated per lane: lanes may look at different tiles and problems.
+template <class CF>
+__device__ __forceinline__ bool tile_nonempty(const GemmBatch& batch, int lid) {
+  const bool second = batch.nprob > 1 && lid >= batch.p[0].tiles;
+  const int rem = second ? lid - batch.p[0].tiles : lid;
+  const int mtiles = second ? batch.p[1].m_tiles : batch.p[0].m_tiles;
+  const int ntiles = second ? batch.p[1].n_tiles : batch.p[0].n_tiles;
+  const int32_t* cnt = second ? batch.p[1].m_count : batch.p[0].m_count;
+  const int mconst = second ? batch.p[1].m_const : batch.p[0].m_const;
+  const int per_group = mtiles * ntiles;
+  const int g = rem / per_group;
+  const int mt = (rem - g * per_group) % mtiles;
+  const int M = cnt ? cnt[g] : mconst;
+  return mt * CF::BM < M;
+}
+
 // The A source row of DMA load i of this lane for tile t: load i of wave wv fills LDS
 // rows (wv*A_INST + i)*8 .. +8, this lane row (lane / 8); rows past M repeat row m0
 // (never stored); with a row map the row is the gathered token (or slot) row.

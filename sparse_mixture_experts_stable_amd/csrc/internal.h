@@ -101,6 +101,7 @@ struct GemmBatch {
   int32_t total;
   int32_t chunk;     // tiles per chunk dealt to one XCD (one group's tiles of problem 0)
   int32_t xcd_max;   // most tiles any XCD receives
+  int32_t list_cap;  // persistent kernel: entries of a block's tile list (LDS)
 };
 
 constexpr int kBf16BM = 128, kBf16BN = 128, kBf16BK = 64;
