@@ -67,8 +67,25 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Standard normal cdf, Phi(z) = erfc(-z / sqrt 2) / 2, with erfc from Abramowitz and
+// Stegun, Handbook of Mathematical Functions, formula 7.1.26: for x >= 0,
+// erfc(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2), t = 1 / (1 + p x),
+// absolute error at most 1.5e-7. Branch-free (one reciprocal, one exponential), so a
+// GEMM epilogue applying it to every output costs a few instructions per value.
+__device__ __forceinline__ float normal_cdf(float z) {
+  const float ax = fabsf(z) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                       -0.284496736f),
+               0.254829592f);
+  const float half_erfc = 0.5f * poly * __expf(-ax * ax);
+  return z >= 0.f ? 1.0f - half_erfc : half_erfc;
+}
+
+// GELU with the exact (erf) form: z Phi(z).
 __device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+  return z * normal_cdf(z);
 }
 
 __device__ __forceinline__ float silu(float z) {

@@ -50,9 +50,8 @@ __device__ __forceinline__ f32x4 ld4v(const float* p) {
 
 // d/dz of z * Phi(z): Phi(z) + z phi(z), with the standard normal cdf / pdf.
 __device__ __forceinline__ float gelu_erf_grad(float z) {
-  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752440f));
   const float pdf = 0.39894228040143267794f * __expf(-0.5f * z * z);
-  return cdf + z * pdf;
+  return normal_cdf(z) + z * pdf;
 }
 }  // namespace
 
