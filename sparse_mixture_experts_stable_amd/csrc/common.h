@@ -88,8 +88,10 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return z * normal_cdf(z);
 }
 
+// z sigma(z), with the hardware reciprocal (1 ulp) in place of a rounded division: a
+// SwiGLU epilogue evaluates it once per output.
 __device__ __forceinline__ float silu(float z) {
-  return z / (1.0f + __expf(-z));
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

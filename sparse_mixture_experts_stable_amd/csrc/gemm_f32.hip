@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float a = v[r];
-            const float sg = 1.0f / (1.0f + __expf(-a));
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
             const float sa = a * sg;
             du[r] = dh[r] * sa;
             da[r] = dh[r] * u[r] * (sg * (1.0f + a * (1.0f - sg)));
