@@ -76,6 +76,14 @@ def _sample_tokens(T, d, n=24, seed=0):
     toks = set(range(8)) | set(range(T - 8, T)) | set(rng.integers(0, T, n).tolist())
     full_drop = np.flatnonzero(d["drops"] == d["slot"].shape[1])
     toks |= set(full_drop[:4].tolist())
+    # experts with fewer kept rows than one 256-row GEMM tile: the tokens in their first
+    # and last slot (these lone, partly filled tiles are what the GEMM schedule has to
+    # spread over the GPU when routing is skewed)
+    k = d["slot"].shape[1]
+    extra = []
+    for e in np.flatnonzero((d["used"] > 0) & (d["used"] < 256)):
+        extra += [int(d["slot_assign"][e, 0]) // k, int(d["slot_assign"][e, d["used"][e] - 1]) // k]
+    toks |= set(extra[:64])
     return np.array(sorted(toks))
 
 
