@@ -74,7 +74,8 @@ typedef enum {
                                NumPy", section 2 forward einsum); W [E, D, D]          */
   MOE_EXPERT_GELU_MLP = 1,  /* o = GELU_erf(x W1 + b1) W2 + b2 (llm-atlas "Mixture of
                                Experts", Expert); W1 [E,D,F], W2 [E,F,D], b1 [E,F],
-                               b2 [E,D]                                                */
+                               b2 [E,D]. GELU_erf(z) = z Phi(z), Phi evaluated with an
+                               absolute error below 1e-7                               */
   MOE_EXPERT_SWIGLU = 2     /* o = (silu(x Wg) * (x Wu)) Wd   ("Module 7",
                                swiglu_expert); Wg, Wu [E,D,F], Wd [E,F,D], no bias     */
 } moe_expert_kind_t;
