@@ -60,6 +60,9 @@ def parse():
                     help="instead of the layer: time the vendor library's bf16 GEMMs (torch "
                          "bmm / mm) on the expert GEMM shapes of the SwiGLU workload, as a "
                          "reference point for the MFMA fraction")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the cold-cache pass (per-kernel timing with a 512 MiB device "
+                         "write before every step)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MiB (a "
                          "known-size reference for hardware byte counters)")
@@ -331,17 +334,48 @@ def main():
     ops.profile_enable(False)
     kern = ops.profile_read()
 
+    # third pass (unless --no-flush): the same per-kernel timing with L2 and the MALL
+    # flushed before every step by a 512 MiB device write outside the library's launches
+    kern_cold = None
+    if not args.no_flush:
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            flush_buf.fill_(1)
+            ops.profile_enable(True)
+            step()
+            ops.profile_enable(False)
+        torch.cuda.synchronize()
+        kern_cold = ops.profile_read()
+        del flush_buf
+
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     flops = gemm_table(w, kept, backward, router_grad)
-    gemms = {}
-    for name, fl in flops.items():
-        if name not in kern or fl <= 0:
-            continue
-        cnt, tot = kern[name]
-        avg = tot / cnt
-        ach = fl / (avg * 1e-3) / 1e12
-        gemms[name] = {"ms_per_step": round(tot / args.steps, 4), "avg_launch_ms": round(avg, 4),
-                       "tflops": round(ach, 2), "frac": round(ach / peak, 4)}
+
+    def gemm_rows(kd):
+        out = {}
+        for name, fl in flops.items():
+            if name not in kd or fl <= 0:
+                continue
+            cnt, tot = kd[name]
+            avg = tot / cnt
+            ach = fl / (avg * 1e-3) / 1e12
+            out[name] = {"ms_per_step": round(tot / args.steps, 4), "avg_launch_ms": round(avg, 4),
+                         "tflops": round(ach, 2), "frac": round(ach / peak, 4)}
+        return out
+
+    def hbm_rows(kd):
+        out = {}
+        for name, by in hbm_table(w, kept, backward).items():
+            if name not in kd:
+                continue
+            cnt, tot = kd[name]
+            gbs = by / (tot / cnt * 1e-3) / 1e9
+            out[name] = {"avg_launch_ms": round(tot / cnt, 4), "bytes_per_launch": by,
+                         "GBs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        return out
+
+    gemms = gemm_rows(kern)
     dom = max(gemms, key=lambda n: gemms[n]["ms_per_step"])
     dom_ms = kern[dom][1] / kern[dom][0]
     achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
@@ -351,14 +385,16 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic_record(dom, w.name, src_hash),
                 "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(dom_ms, 4)}
-    hbm = {}
-    for name, by in hbm_table(w, kept, backward).items():
-        if name not in kern:
-            continue
-        cnt, tot = kern[name]
-        gbs = by / (tot / cnt * 1e-3) / 1e9
-        hbm[name] = {"avg_launch_ms": round(tot / cnt, 4), "bytes_per_launch": by,
-                     "GBs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    hbm = hbm_rows(kern)
+    roofline_cold = hbm_cold = None
+    if kern_cold is not None and dom in kern_cold:
+        cold_ms = kern_cold[dom][1] / kern_cold[dom][0]
+        cold = flops[dom] / (cold_ms * 1e-3) / 1e12
+        roofline_cold = {"bound": "mfma", "kernel": dom, "achieved": round(cold, 2),
+                         "peak": peak, "unit": "TFLOP/s", "frac": round(cold / peak, 4),
+                         "avg_launch_ms": round(cold_ms, 4),
+                         "caches": "L2 and MALL flushed before every step (512 MiB write)"}
+        hbm_cold = hbm_rows(kern_cold)
 
     kernels = {k: {"launches_per_step": round(c / args.steps, 2), "avg_ms": round(t / c, 4)}
                for k, (c, t) in kern.items()}
@@ -407,6 +443,8 @@ def main():
         "roofline": roofline,
         "gemms": gemms,
         "hbm": hbm,
+        "roofline_cold": roofline_cold,
+        "hbm_cold": hbm_cold,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "profiled_ms_per_step": round(prof_ms, 4),
