@@ -66,8 +66,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   constexpr int TM = BM / 32, TN = BN / 32;    // 16 x 16 MFMA tiles per wave
   constexpr int AL = BM / 32, BL = BN / 32;    // float4 loads per thread per k-tile
   static_assert((BM == 64 || BM == 128) && (BN == 64 || BN == 128), "tile size");
-  __shared__ float As[2][A_SZ];
-  __shared__ float Bs[NB][2][B_SZ];
+  // Gathered-K products (weight gradients) keep one LDS buffer and take two barriers per
+  // k-tile: half the LDS lets three blocks share a CU instead of two, which measures
+  // faster for their short K; the others double-buffer with one barrier.
+  constexpr bool SINGLE = AM == A_KROWS;
+  constexpr int NBUF = SINGLE ? 1 : 2;
+  __shared__ float As[NBUF][A_SZ];
+  __shared__ float Bs[NB][NBUF][B_SZ];
   int lid = logical_block_f32(blockIdx.x, gridDim.x);
   const int per_group = P.m_tiles * P.n_tiles;
   // split K: blocks split * tiles .. + tiles - 1 take k rows [split * k_chunk, + k_chunk)
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
     store(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
+      const int cur = SINGLE ? 0 : (kt & 1);
       if (kt + 1 < nk) load(kt + 1, kt + 2 < nk);
 #pragma unroll
       for (int ks = 0; ks < BK / 4; ++ks) {
@@ -267,7 +272,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
               acc[b][i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j], af[i], acc[b][i][j], 0, 0, 0);
         }
       }
-      if (kt + 1 < nk) store(cur ^ 1);
+      if constexpr (SINGLE) {
+        __syncthreads();  // every wave is done with the buffer the next k-tile overwrites
+        if (kt + 1 < nk) store(0);
+      } else {
+        if (kt + 1 < nk) store(cur ^ 1);
+      }
       __syncthreads();
     }
   }
