@@ -55,7 +55,9 @@ __device__ __forceinline__ float gelu_erf_grad(float z) {
 }
 }  // namespace
 
-template <int AM, int BMODE, bool GATED, int BM, int BN>
+// SINGLE: one LDS buffer and two barriers per k-tile (half the LDS, so three blocks
+// share a CU instead of two); else a double buffer and one barrier.
+template <int AM, int BMODE, bool GATED, int BM, int BN, bool SINGLE>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   constexpr int NB = GATED ? 2 : 1;
   constexpr bool AK = AM == A_ROWS;     // A stored [m][k]
@@ -66,10 +68,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Problem P) {
   constexpr int TM = BM / 32, TN = BN / 32;    // 16 x 16 MFMA tiles per wave
   constexpr int AL = BM / 32, BL = BN / 32;    // float4 loads per thread per k-tile
   static_assert((BM == 64 || BM == 128) && (BN == 64 || BN == 128), "tile size");
-  // Gathered-K products (weight gradients) keep one LDS buffer and take two barriers per
-  // k-tile: half the LDS lets three blocks share a CU instead of two, which measures
-  // faster for their short K; the others double-buffer with one barrier.
-  constexpr bool SINGLE = AM == A_KROWS;
   constexpr int NBUF = SINGLE ? 1 : 2;
   __shared__ float As[NBUF][A_SZ];
   __shared__ float Bs[NB][NBUF][B_SZ];
@@ -399,7 +397,15 @@ moe_status_t launch_tile(GemmF32Problem& p, const char* name, hipStream_t s) {
   p.tiles = p.groups * p.m_tiles * p.n_tiles;
   if (p.tiles == 0) return MOE_OK;
   const int blocks = p.tiles * (p.k_splits > 1 ? p.k_splits : 1);
-  MOE_LAUNCH(name, (gemm_f32_kernel<AM, BMODE, GATED, BM, BN>), dim3(blocks), dim3(256), 0, s, p);
+  // Three blocks per CU (single LDS buffer) pay off for the weight gradients (short,
+  // gathered K) and for grids of many blocks; a smaller grid divides better into rounds
+  // of two blocks per CU.
+  if (AM == A_KROWS || blocks >= 4096)
+    MOE_LAUNCH(name, (gemm_f32_kernel<AM, BMODE, GATED, BM, BN, true>), dim3(blocks), dim3(256), 0,
+               s, p);
+  else
+    MOE_LAUNCH(name, (gemm_f32_kernel<AM, BMODE, GATED, BM, BN, false>), dim3(blocks), dim3(256),
+               0, s, p);
   return MOE_OK;
 }
 
