@@ -250,8 +250,8 @@ def main():
         vendor_gemm(args.steps)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "expert-parallel path is not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU "
+              "expert parallelism is not implemented.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
