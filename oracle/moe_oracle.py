@@ -23,7 +23,7 @@ Sources (page titles; sections named as on the pages):
        approach, steps 2-6.
   [P5] "Mixture of Experts" (llm-atlas.app): the Expert and TopKMoE modules.
 
-Readings where the pages are silent or disagree (each one is listed in the design doc):
+Readings where the pages are silent or disagree:
   * the top-k key is the fp32 logit, exact ties to the lower expert index (P2, P3);
   * -0.0 and +0.0 compare equal;
   * gates are renormalised over the k choices before any drop and never after (P1);
