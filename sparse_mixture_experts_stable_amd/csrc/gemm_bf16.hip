@@ -383,7 +383,9 @@ moe_status_t launch_epi(GemmBatch& b, const char* name, hipStream_t s) {
 
 moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStream_t s) {
   // Large tiles (256 x 256, 16 waves, two stages) when every problem has enough rows per
-  // group and the grid still holds at least two tiles per CU; else 128 x 128 tiles. The
+  // group and the grid has at least 128 of them (half the CUs: the large tile's higher
+  // rate per CU outweighs the idle CUs, e.g. 192 tiles with K = 4096 run in 115 us against
+  // 139 us as 640 small tiles); else 128 x 128 tiles. The
   // gated (SwiGLU) GEMM, with long K loops and small output tiles, runs persistent blocks;
   // the others (K as short as d_hidden, 128 KiB output tiles) run one block per tile with
   // the LDS-staged epilogue, whose stores overlap the next block's start.
@@ -396,7 +398,7 @@ moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStr
     const int bnq = gated ? Large::BNQ : 2 * Large::BNQ;
     tiles += long(p.groups) * ((p.m_tiles_rows + 255) / 256) * ((p.N + bnq - 1) / bnq);
   }
-  if (tiles < 512) large = false;
+  if (tiles < 128) large = false;
   if (gated) {
     for (int i = 0; i < b.nprob; ++i)
       if (b.p[i].epi != EPI_SWIGLU || b.p[i].out_f32) return MOE_ERR_UNSUPPORTED;
