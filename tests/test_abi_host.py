@@ -126,3 +126,35 @@ def test_workspace_sizes_positive():
     lib = L.lib()
     assert lib.moe_route_workspace_size(16384, 256) > 16384 // 16 * 256 * 4
     assert lib.moe_dispatch_workspace_size(16384, 8, 256) > 0
+
+
+def test_missing_library_fails_loudly():
+    """With libmoe.so absent, the binding raises ImportError at the first call: there is
+    no fallback (CPU or otherwise) behind the Python names."""
+    import subprocess
+    import sys
+    code = (
+        "import sparse_mixture_experts_stable_amd._lib as L\n"
+        "L.LIB_PATH = '/nonexistent/libmoe.so'\n"
+        "from sparse_mixture_experts_stable_amd import ops\n"
+        "try:\n"
+        "    ops.capacity(16, 2, 4, 1.0)\n"
+        "    print('no error')\n"
+        "except ImportError as e:\n"
+        "    print('ImportError:', e)\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("ImportError:"), r.stdout
+
+
+def test_package_does_not_use_the_oracle():
+    """The product package neither imports nor names the oracle (the oracle is test
+    infrastructure only)."""
+    pkg = os.path.join(ROOT, "sparse_mixture_experts_stable_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", src), os.path.join(dirpath, f)
