@@ -445,11 +445,9 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t
   moe_status_t st = launch_count(topk_idx, T, k, E, w, s);
   if (st != MOE_OK) return st;
   // expert_count is not an output of moe_dispatch; the totals land in fp scratch space
-  st = launch_reduce_scan(T, k, E, C, false, reinterpret_cast<int32_t*>(w.fp), nullptr, nullptr,
-                          expert_used, expert_overflow, slot_assign, nullptr, w, s);
-  if (st != MOE_OK) return st;
-  return launch_assign(topk_idx, T, k, E, C, slot, kept, slot_assign, token_drops, expert_used,
-                       w, s);
+  return launch_dispatch(topk_idx, T, k, E, C, false, reinterpret_cast<int32_t*>(w.fp), nullptr,
+                         nullptr, expert_used, expert_overflow, nullptr, slot, kept, slot_assign,
+                         token_drops, w, s);
 }
 
 size_t moe_expert_mlp_workspace_size(const moe_experts_t* ex, int32_t rows) {
@@ -581,12 +579,9 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
   st = launch_route(a->logits, T, E, k, a->topk_idx, a->topk_gate, route_opts(&a->router), f.rw,
                     s);
   if (st != MOE_OK) return st;
-  st = launch_reduce_scan(T, k, E, C, true, a->expert_count, a->prob_sum, a->aux_loss,
-                          a->expert_used, a->expert_overflow, a->slot_assign, a->router.z_loss,
-                          f.rw, s);
-  if (st != MOE_OK) return st;
-  st = launch_assign(a->topk_idx, T, k, E, C, a->slot, a->kept, a->slot_assign, a->token_drops,
-                     a->expert_used, f.rw, s);
+  st = launch_dispatch(a->topk_idx, T, k, E, C, true, a->expert_count, a->prob_sum, a->aux_loss,
+                       a->expert_used, a->expert_overflow, a->router.z_loss, a->slot, a->kept,
+                       a->slot_assign, a->token_drops, f.rw, s);
   if (st != MOE_OK) return st;
 
   ExpertPlan plans[2];

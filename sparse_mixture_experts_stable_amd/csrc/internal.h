@@ -54,6 +54,15 @@ moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int3
 moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32_t* slot,
                            uint8_t* kept, int32_t* slot_assign, int32_t* drops,
                            const int32_t* used, const RouteWs& w, hipStream_t s);
+// The scan (launch_reduce_scan's outputs) and the slot assignment after routing or
+// counting. With E <= 256 and at most kFusedScanEntries chunk sums the scan runs inside
+// the assignment launch (chunk sums, then one kernel); otherwise as three launches.
+constexpr int64_t kFusedScanEntries = 16384;
+moe_status_t launch_dispatch(const int32_t* idx, int T, int k, int E, int C, bool with_prob,
+                             int32_t* count, float* prob_sum, float* aux, int32_t* used,
+                             int32_t* overflow, float* z_loss, int32_t* slot, uint8_t* kept,
+                             int32_t* slot_assign, int32_t* drops, const RouteWs& w,
+                             hipStream_t s);
 
 // ---- grouped GEMMs ----------------------------------------------------------------
 enum Epi : int32_t {

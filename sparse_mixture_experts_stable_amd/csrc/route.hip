@@ -316,12 +316,16 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 
 // Chunk sums: block c adds the per-block partials of routing blocks c*kScanRows ..
 // (c+1)*kScanRows - 1 (in block order) for every expert.
+// flags_reset != NULL: clear the error word here (the scan that would clear it runs
+// inside the assignment kernel, whose blocks may set it).
 __global__ __launch_bounds__(256) void chunk_sum_kernel(const int32_t* __restrict__ cnt_part,
                                                         const float* __restrict__ prob_part,
                                                         int nb, int E, int with_prob,
                                                         int32_t* __restrict__ chunk_cnt,
-                                                        float* __restrict__ chunk_prob) {
+                                                        float* __restrict__ chunk_prob,
+                                                        int32_t* __restrict__ flags_reset) {
   const int c = blockIdx.x;
+  if (flags_reset && c == 0 && threadIdx.x == 0) flags_reset[0] = 0;
   const int b0 = c * kScanRows;
   const int b1 = min(nb, b0 + kScanRows);
   for (int e = threadIdx.x; e < E; e += 256) {
@@ -420,6 +424,76 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   if (tid == 0) z_out[0] = s_p[0] / float(T);
 }
 
+template <class T>
+struct Vec4;
+template <>
+struct Vec4<int> {
+  typedef int type __attribute__((ext_vector_type(4)));
+};
+template <>
+struct Vec4<float> {
+  typedef float type __attribute__((ext_vector_type(4)));
+};
+
+// Per-expert sums over a chunk table [nchunks][E] with the block's 256 threads: `all`
+// over every chunk, `below` over the chunks c < lim. Thread (g, part) covers column
+// group g (four experts read as one 16-byte load when E % 4 == 0, else one expert) over
+// the chunk range part*seg .. +seg in chunk order; the parts meet in LDS (s_a, s_b:
+// 1024 entries each) and thread e < E adds them in part order, so every sum has a
+// fixed order. Valid in threads e < E (E <= 256); the other threads get zeros.
+template <class T>
+struct ColSum {
+  T all, below;
+};
+template <class T>
+__device__ ColSum<T> chunk_column_sums(const T* __restrict__ tab, int nchunks, int E, int lim,
+                                       T* s_a, T* s_b) {
+  const int tid = threadIdx.x;
+  const bool vec = (E & 3) == 0;
+  const int EG = vec ? E >> 2 : E;
+  const int P = 256 / EG;
+  const int g = tid % EG, part = tid / EG;
+  const int seg = (nchunks + P - 1) / P;
+  const int lo = min(nchunks, part * seg), hi = min(nchunks, lo + seg);
+  T a[4] = {T(0), T(0), T(0), T(0)}, b[4] = {T(0), T(0), T(0), T(0)};
+  if (part < P) {
+    if (vec) {
+#pragma unroll 4
+      for (int c = lo; c < hi; ++c) {
+        const typename Vec4<T>::type v = reinterpret_cast<const typename Vec4<T>::type*>(tab + size_t(c) * E)[g];
+        const bool lt = c < lim;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          a[r] += v[r];
+          if (lt) b[r] += v[r];
+        }
+      }
+    } else {
+      for (int c = lo; c < hi; ++c) {
+        const T v = tab[size_t(c) * E + g];
+        a[0] += v;
+        if (c < lim) b[0] += v;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s_a[tid * 4 + r] = a[r];
+    s_b[tid * 4 + r] = b[r];
+  }
+  __syncthreads();
+  ColSum<T> out{T(0), T(0)};
+  if (tid < E) {
+    const int gg = vec ? tid >> 2 : tid, comp = vec ? (tid & 3) : 0;
+    for (int q = 0; q < P; ++q) {
+      out.all += s_a[(q * EG + gg) * 4 + comp];
+      out.below += s_b[(q * EG + gg) * 4 + comp];
+    }
+  }
+  __syncthreads();
+  return out;
+}
+
 // Slot assignment. Block b covers tokens [b*G*kRouteTokens, ...) (G routing blocks) and
 // walks its assignments in chunks of 256 (a = t*k + j ascending). Within a chunk each
 // wave finds, by ballots on the expert-id bits, the lanes holding the same expert, and
@@ -428,26 +502,102 @@ __global__ __launch_bounds__(1024) void scan_kernel(
 // offset of the block (its chunk's scanned offset plus the counts of the earlier routing
 // blocks of that chunk). The grid then writes -1 into slot_assign[e, c] for
 // c >= used[e] (a grid-stride pass over the E*C table).
+//
+// FUSED (E <= 256 and few chunks): there is no separate scan launch. Every assignment
+// block adds up the chunk sums itself (integer sums, so the order does not matter): those
+// of the chunks before its own give its chunk's offset, all of them the totals behind
+// used[e]. One extra block, the last of the grid, writes the scan's outputs: totals,
+// used/overflow, prob_sum (per expert, the chunk sums of a part of the chunk range in
+// order, then the parts in order), the aux loss and the z-loss (fixed trees).
+struct ScanOut {
+  int32_t* count;
+  float* prob_sum;
+  float* aux;
+  int32_t* used;
+  int32_t* overflow;
+  float* z_loss;     // NULL: no z-loss
+  int with_prob;
+};
+
+template <bool FUSED>
 __global__ __launch_bounds__(256) void assign_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int C, int G,
     const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ cnt_part, int ebits,
     const int32_t* __restrict__ used,
     int32_t* __restrict__ slot, uint8_t* __restrict__ kept, int32_t* __restrict__ slot_assign,
-    int32_t* __restrict__ drops, int32_t* __restrict__ flags) {
+    int32_t* __restrict__ drops, int32_t* __restrict__ flags,
+    const int32_t* __restrict__ chunk_cnt, const float* __restrict__ chunk_prob, int nchunks,
+    const float* __restrict__ zpart, int nb, ScanOut so) {
   extern __shared__ int smem[];
   int* s_run = smem;                // [E]
   int* s_wh = smem + E;             // [4][E]
   int* s_tk = smem + 5 * E;         // [G*kRouteTokens] kept choices per token
+  __shared__ int s_ci[FUSED ? 256 : 1];
+  __shared__ int s_cj[FUSED ? 256 : 1];
+  __shared__ int s_x[FUSED ? 2 : 1][FUSED ? 1024 : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
+  if constexpr (FUSED) {
+    if (blockIdx.x == gridDim.x - 1) {
+      // the scan's outputs
+      const ColSum<int> cnt = chunk_column_sums<int>(chunk_cnt, nchunks, E, 0, s_x[0], s_x[1]);
+      ColSum<float> pr{0.f, 0.f};
+      if (so.with_prob)
+        pr = chunk_column_sums<float>(chunk_prob, nchunks, E, 0, reinterpret_cast<float*>(s_x[0]),
+                                      reinterpret_cast<float*>(s_x[1]));
+      float* s_f = reinterpret_cast<float*>(s_x[0]);
+      float fpv = 0.f;
+      if (tid < E) {
+        const int total = cnt.all;
+        so.count[tid] = total;
+        const int u = min(total, C);
+        so.used[tid] = u;
+        so.overflow[tid] = total - u;
+        if (so.with_prob) {
+          so.prob_sum[tid] = pr.all;
+          fpv = (float(total) / (float(T) * float(k))) * (pr.all / float(T));
+        }
+      }
+      if (!so.with_prob) return;
+      s_f[tid] = fpv;
+      __syncthreads();
+      for (int d = 128; d >= 1; d >>= 1) {
+        if (tid < d) s_f[tid] += s_f[tid + d];
+        __syncthreads();
+      }
+      if (tid == 0) so.aux[0] = float(E) * s_f[0];
+      if (!so.z_loss) return;
+      float z = 0.f;
+      for (int b = tid; b < nb; b += 256) z += zpart[b];
+      __syncthreads();
+      s_f[tid] = z;
+      __syncthreads();
+      for (int d = 128; d >= 1; d >>= 1) {
+        if (tid < d) s_f[tid] += s_f[tid + d];
+        __syncthreads();
+      }
+      if (tid == 0) so.z_loss[0] = s_f[0] / float(T);
+      return;
+    }
+  }
   const int tokens = G * kRouteTokens;
   const int tok0 = blockIdx.x * tokens;
   const int tok1 = min(T, tok0 + tokens);
   const int rb = blockIdx.x * G;    // first routing block of this block
   const int cb = rb / kScanRows;
+  if constexpr (FUSED) {
+    // per expert: the counts of the chunks before chunk cb (the chunk's offset) and
+    // used[e] = min(total, C)
+    const ColSum<int> cs = chunk_column_sums<int>(chunk_cnt, nchunks, E, cb, s_x[0], s_x[1]);
+    if (tid < E) {
+      s_ci[tid] = cs.below;
+      s_cj[tid] = min(cs.all, C);
+    }
+    __syncthreads();
+  }
   for (int e = tid; e < E; e += 256) {
-    int run = chunk_off[size_t(cb) * E + e];
+    int run = FUSED ? s_ci[e] : chunk_off[size_t(cb) * E + e];
     for (int b = cb * kScanRows; b < rb; ++b) run += cnt_part[size_t(b) * E + e];
     s_run[e] = run;
     s_wh[e] = 0;
@@ -506,12 +656,13 @@ __global__ __launch_bounds__(256) void assign_kernel(
     __syncthreads();
   }
   for (int t = tid; t < tok1 - tok0; t += 256) drops[tok0 + t] = k - s_tk[t];
-  // unfilled slots
+  // unfilled slots (FUSED: the last block of the grid is the scan block)
   const int64_t total = int64_t(E) * C;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + tid; i < total; i += int64_t(gridDim.x) * 256) {
-    const int ee = int(i / C);
-    const int c = int(i - int64_t(ee) * C);
-    if (c >= used[ee]) slot_assign[i] = -1;
+  const int nab = FUSED ? gridDim.x - 1 : gridDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + tid; i < total; i += int64_t(nab) * 256) {
+    const int e2 = int(i / C);
+    const int c = int(i - int64_t(e2) * C);
+    if (c >= (FUSED ? s_cj[e2] : used[e2])) slot_assign[i] = -1;
   }
 }
 
@@ -572,7 +723,7 @@ moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int3
   const int nb = route_blocks(T);
   const int nchunks = scan_chunks(T);
   MOE_LAUNCH("chunk_sum", chunk_sum_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt_part,
-             w.prob_part, nb, E, with_prob ? 1 : 0, w.chunk_cnt, w.chunk_prob);
+             w.prob_part, nb, E, with_prob ? 1 : 0, w.chunk_cnt, w.chunk_prob, nullptr);
   int P = 1024 / E;
   if (P < 1) P = 1;
   if (P > nchunks) P = nchunks;
@@ -582,17 +733,51 @@ moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int3
   return MOE_OK;
 }
 
+namespace {
+int assign_ebits(int E) {
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
+  return ebits;
+}
+}  // namespace
+
 moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32_t* slot,
                            uint8_t* kept, int32_t* slot_assign, int32_t* drops,
                            const int32_t* used, const RouteWs& w, hipStream_t s) {
   const int G = assign_group(k);
   const int tokens = G * kRouteTokens;
   const int blocks = (T + tokens - 1) / tokens;
-  int ebits = 0;
-  while ((1 << ebits) < E) ++ebits;
   const size_t shmem = sizeof(int) * (5 * size_t(E) + tokens);
-  MOE_LAUNCH("assign", assign_kernel, dim3(blocks), dim3(256), shmem, s, idx, T, k, E, C, G,
-             w.chunk_off, w.cnt_part, ebits, used, slot, kept, slot_assign, drops, w.flags);
+  MOE_LAUNCH("assign", assign_kernel<false>, dim3(blocks), dim3(256), shmem, s, idx, T, k, E, C,
+             G, w.chunk_off, w.cnt_part, assign_ebits(E), used, slot, kept, slot_assign, drops,
+             w.flags, nullptr, nullptr, 0, nullptr, 0, ScanOut{});
+  return MOE_OK;
+}
+
+moe_status_t launch_dispatch(const int32_t* idx, int T, int k, int E, int C, bool with_prob,
+                             int32_t* count, float* prob_sum, float* aux, int32_t* used,
+                             int32_t* overflow, float* z_loss, int32_t* slot, uint8_t* kept,
+                             int32_t* slot_assign, int32_t* drops, const RouteWs& w,
+                             hipStream_t s) {
+  const int nb = route_blocks(T);
+  const int nchunks = scan_chunks(T);
+  if (E > 256 || int64_t(nchunks) * E > kFusedScanEntries) {
+    moe_status_t st = launch_reduce_scan(T, k, E, C, with_prob, count, prob_sum, aux, used,
+                                         overflow, slot_assign, z_loss, w, s);
+    if (st != MOE_OK) return st;
+    return launch_assign(idx, T, k, E, C, slot, kept, slot_assign, drops, used, w, s);
+  }
+  MOE_LAUNCH("chunk_sum", chunk_sum_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt_part,
+             w.prob_part, nb, E, with_prob ? 1 : 0, w.chunk_cnt, w.chunk_prob, w.flags);
+  const int G = assign_group(k);
+  const int tokens = G * kRouteTokens;
+  const int blocks = (T + tokens - 1) / tokens;
+  const size_t shmem = sizeof(int) * (5 * size_t(E) + tokens);
+  ScanOut so{count, prob_sum, aux, used, overflow, with_prob ? z_loss : nullptr,
+             with_prob ? 1 : 0};
+  MOE_LAUNCH("assign", assign_kernel<true>, dim3(blocks + 1), dim3(256), shmem, s, idx, T, k, E,
+             C, G, nullptr, w.cnt_part, assign_ebits(E), nullptr, slot, kept, slot_assign, drops,
+             w.flags, w.chunk_cnt, w.chunk_prob, nchunks, w.zpart, nb, so);
   return MOE_OK;
 }
 

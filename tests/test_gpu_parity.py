@@ -50,6 +50,19 @@ def test_forward_small(cfg):
     H.check_outputs(w, inp, h, r, d)
 
 
+@pytest.mark.parametrize("case", ["many_experts", "many_chunks"])
+def test_forward_split_scan_path(case):
+    """Shapes past the limits of the scan that runs inside the assignment launch (more than
+    256 experts, or more than 16,384 chunk sums): there the scan is a launch of its own."""
+    w = {"many_experts": SMALL[3].scaled(T=512, E=384, k=4, F=64, shared_F=0),
+         "many_chunks": SMALL[1].scaled(T=70000, D=64, E=256, F=64)}[case]
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp)
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.check_outputs(w, inp, h, r, d)
+
+
 def test_forward_small_zipf_pmf_variant():
     w = SMALL[4].scaled(logits_mode="zipf_pmf_q")
     inp = make_inputs(w)
@@ -264,7 +277,8 @@ def test_route_signed_zero_and_page_examples():
 # ---------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,k,E,C", [(1, 1, 1, 1), (300, 3, 7, 50), (1000, 2, 4, 0), (777, 8, 64, 40),
-                                     (5000, 1, 3, 2000), (257, 5, 1000, 1)])
+                                     (5000, 1, 3, 2000), (257, 5, 1000, 1), (40000, 2, 128, 700),
+                                     (70000, 2, 256, 600)])
 def test_dispatch_random_with_duplicates(T, k, E, C):
     ops = _ops()
     rng = np.random.default_rng(T + k + E + C)
