@@ -98,6 +98,20 @@ __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
 
 }  // namespace
 
+// The 16-wave, 256-row tile with a bf16 output leaves through the LDS-staged epilogue.
+template <class CF, bool OF32>
+constexpr bool staged_epilogue() {
+  return !OF32 && CF::WAVES == 16 && CF::BM == 256;
+}
+// Dynamic LDS of gemm_bf16_kernel: the ring, plus the block's bias columns (fp32) above
+// it when the staged epilogue, which uses the whole ring, needs a bias.
+template <class CF, int EPI, bool OF32>
+constexpr int kernel_lds() {
+  return CF::LDS + (staged_epilogue<CF, OF32>() && (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS)
+                        ? int(sizeof(float)) * CF::BNQ
+                        : 0);
+}
+
 // EPI: EPI_STORE / EPI_BIAS / EPI_GELU_BIAS / EPI_SWIGLU; OF32: store fp32 instead of bf16
 template <class CF, int EPI, bool OF32>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch batch) {
@@ -148,10 +162,10 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
   wait_vmcnt<0>();  // the clamped tail loads still target LDS
   __syncthreads();
 
-  constexpr bool STAGED = !OF32 && CF::WAVES == 16 && CF::BM == 256;
-  // bias of this block's columns, staged once in LDS (free after the main loop; above
-  // the 64 KiB the staged epilogue uses)
-  float* sbias = reinterpret_cast<float*>(smem + (STAGED ? 65536 : 0));
+  constexpr bool STAGED = staged_epilogue<CF, OF32>();
+  // bias of this block's columns, staged once in LDS (in the ring, free after the main
+  // loop; above it when the staged epilogue uses the whole ring)
+  float* sbias = reinterpret_cast<float*>(smem + (STAGED ? CF::LDS : 0));
   if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
     stage_bias<CF>(P, tl, tid, sbias);
     __syncthreads();
@@ -308,14 +322,15 @@ template <class CF, int EPI, bool OF32>
 moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
   plan_tiles<CF>(b);
   if (b.total == 0) return MOE_OK;
+  constexpr int lds = kernel_lds<CF, EPI, OF32>();
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel<CF, EPI, OF32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
       return MOE_ERR_HIP;
     attr_set = true;
   }
-  MOE_LAUNCH(name, (gemm_bf16_kernel<CF, EPI, OF32>), dim3(8 * b.xcd_max), dim3(CF::THREADS), CF::LDS,
+  MOE_LAUNCH(name, (gemm_bf16_kernel<CF, EPI, OF32>), dim3(8 * b.xcd_max), dim3(CF::THREADS), lds,
              s, b);
   return MOE_OK;
 }

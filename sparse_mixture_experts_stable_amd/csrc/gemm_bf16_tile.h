@@ -309,12 +309,13 @@ __device__ __forceinline__ void epi_math(const GemmProblem& P, const TileId& t, 
   }
 }
 
-// bf16 epilogue through LDS: the tile is written to `stage` (64 KiB) in rounds of
-// R = 64 KiB / (2 BNQ) rows, each lane's 8-byte pieces placed with the 16-byte chunk
-// index XORed by (row % 16), then read back as 16 bytes per lane along whole rows and
-// stored (non-temporal), so every store instruction writes complete row segments. All threads of the
-// block take part (it synchronises); `stage` must be free on entry and is free again
-// on return.
+// bf16 epilogue through LDS: the tile is written to `stage` (the whole LDS ring,
+// CF::LDS bytes, free once the K loop is done) in rounds of R = min(BM, CF::LDS / (2 BNQ))
+// rows (one round for the 256-row tiles: every wave writes its accumulators at once), each
+// lane's 8-byte pieces placed with the 16-byte chunk index XORed by (row % 16), then
+// read back as 16 bytes per lane along whole rows and stored (non-temporal), so every
+// store instruction writes complete row segments. All threads of the block take part
+// (it synchronises); `stage` must be free on entry and is free again on return.
 template <class CF, int EPI>
 __device__ __forceinline__ void store_tile_staged(const GemmProblem& P, const TileId& t, int wm,
                                                   int wn, int wv, int lane, const float* sbias,
@@ -322,7 +323,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmProblem& P, const Ti
                                                   const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
   constexpr int RB = CF::BNQ * 2;         // bytes per output row
   constexpr int CPR = RB / 16;            // 16-byte chunks per row
-  constexpr int R = 65536 / RB;           // rows per round
+  constexpr int R = CF::LDS / RB < CF::BM ? CF::LDS / RB : CF::BM;  // rows per round
   constexpr int ROUNDS = CF::BM / R;
   constexpr int LPR = 64 / CPR;           // rows per wave instruction when reading back
   static_assert(CPR >= 16 && R % CF::WROWS == 0 && CF::BM % R == 0 && CF::WAVES == 16,
