@@ -63,6 +63,28 @@ def test_forward_split_scan_path(case):
     H.check_outputs(w, inp, h, r, d)
 
 
+DEGENERATE = {
+    # one token, one choice, a shared expert
+    "one_token": SMALL[3].scaled(T=1, E=4, k=1, F=128, shared_F=128),
+    # every token picks every expert (k = E), no drops, T off every tile size
+    "all_experts": SMALL[2].scaled(T=300, E=4, k=4, cf=2.0),
+    # a single expert: one group of 700 rows, ragged in the last row tile
+    "single_expert": SMALL[3].scaled(T=700, E=1, k=1, cf=1.0, shared_F=0),
+    # bf16 single-linear experts (the output GEMM alone)
+    "bf16_linear": SMALL[5].scaled(dtype="bf16", D=256, backward=False),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DEGENERATE))
+def test_forward_degenerate_shapes(case):
+    w = DEGENERATE[case]
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp)
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.check_outputs(w, inp, h, r, d)
+
+
 def test_forward_small_zipf_pmf_variant():
     w = SMALL[4].scaled(logits_mode="zipf_pmf_q")
     inp = make_inputs(w)
