@@ -60,6 +60,11 @@ def parse():
                     help="instead of the layer: time the vendor library's bf16 GEMMs (torch "
                          "bmm / mm) on the expert GEMM shapes of the SwiGLU workload, as a "
                          "reference point for the MFMA fraction")
+    ap.add_argument("--w-in-layout", choices=["auto", "in_out", "out_in"], default="auto",
+                    help="storage of w_in / w_up handed to the library: [E, D, F] (in_out) or "
+                         "[E, F, D] (out_in, a torch Linear weight per expert; bf16 forward), "
+                         "transposed once before timing. auto: out_in for the bf16 SwiGLU "
+                         "forward, whose persistent gated GEMM runs faster on it; else in_out")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cold-cache pass (per-kernel timing with a 512 MiB device "
                          "write before every step)")
@@ -275,14 +280,26 @@ def main():
     inp = make_inputs(w)
     g = {k: v.to("cuda") for k, v in inp.items()}
     gen_s = time.perf_counter() - t_gen
+    layout = args.w_in_layout
+    if layout == "auto":
+        layout = "out_in" if w.dtype == "bf16" and w.kind == "swiglu" and not backward else "in_out"
+    out_in = layout == "out_in"
     ex = {"kind": w.kind}
     for key in ("w_in", "w_up", "w_out", "b_in", "b_out"):
         if key in g:
-            ex[key] = g[key]
+            ex[key] = g[key].transpose(1, 2).contiguous() if out_in and key in ("w_in", "w_up") else g[key]
     shared = None
     if w.shared_F:
         shared = {"kind": "swiglu", "w_in": g["shared_w_in"][None], "w_up": g["shared_w_up"][None],
                   "w_out": g["shared_w_out"][None]}
+        if out_in:
+            shared["w_in"] = shared["w_in"].transpose(1, 2).contiguous()
+            shared["w_up"] = shared["w_up"].transpose(1, 2).contiguous()
+            shared["w_in_layout"] = "out_in"
+    if out_in:
+        ex["w_in_layout"] = "out_in"
+        for key in ("w_in", "w_up", "shared_w_in", "shared_w_up"):
+            g.pop(key, None)  # the transposed copies replace them in device memory
     C = ops.capacity(w.T, w.k, w.E, w.cf)
     kw = {"logits": g["logits"]} if "logits" in g else {"w_router": g["w_router"]}
     out = ops.forward(g["x"], ex, k=w.k, capacity=C, shared=shared, use_residual=w.residual, **kw)
@@ -383,7 +400,7 @@ def main():
                              else ("gemm_f32.hip",)))
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic_record(dom, w.name, src_hash),
+                "traffic": traffic_record(dom, w.name + ("_w_in_out_in" if out_in else ""), src_hash),
                 "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(dom_ms, 4)}
     hbm = hbm_rows(kern)
     roofline_cold = hbm_cold = None
@@ -439,7 +456,8 @@ def main():
                    "expert": w.kind, "d_hidden": w.F, "shared_hidden": w.shared_F,
                    "capacity": C, "capacity_factor": w.cf, "kept_assignments": kept,
                    "step": "forward + backward" if backward else "forward",
-                   "router_grad": router_grad, "parallelism": "single GPU"},
+                   "router_grad": router_grad, "w_in_layout": layout,
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "gemms": gemms,
         "hbm": hbm,

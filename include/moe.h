@@ -46,7 +46,9 @@
  *   - Index outputs are int32; the kept mask is one byte per assignment. An
  *     assignment a = t*k + j is token t's j-th choice.
  *   - Shape limits: 1 <= E <= 1024, 1 <= k <= min(E, 256). bf16 expert GEMMs need
- *     d_model and d_hidden to be multiples of 64; fp32 ones multiples of 16.
+ *     d_model and d_hidden to be multiples of 64; fp32 ones multiples of 16. The
+ *     OUT_IN weight layout needs bf16 experts, the forward, and (moe_forward) the same
+ *     layout for the routed and the shared experts.
  *     Anything else returns MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H_
@@ -80,6 +82,13 @@ typedef enum {
                                swiglu_expert); Wg, Wu [E,D,F], Wd [E,F,D], no bias     */
 } moe_expert_kind_t;
 
+/* Storage of w_in and w_up (moe_experts_t.w_in_layout). IN_OUT is [E, in, out] as
+   written above (the einsum form of "Sparse MoE Layer in NumPy" and "Module 7");
+   OUT_IN is [E, out, in], each expert's matrix as a torch Linear stores its weight
+   (llm-atlas "Mixture of Experts", Expert): W1/Wg/Wu [E, F, D], LINEAR W [E, D, D]
+   transposed. The product is the same; OUT_IN is taken by the bf16 forward only. */
+typedef enum { MOE_LAYOUT_IN_OUT = 0, MOE_LAYOUT_OUT_IN = 1 } moe_layout_t;
+
 /* A set of experts of one kind and dtype. All pointers are device pointers. */
 typedef struct {
   int32_t kind;         /* moe_expert_kind_t                                        */
@@ -92,6 +101,8 @@ typedef struct {
   const void* w_out;    /* GELU W2, SWIGLU Wd, LINEAR NULL                          */
   const void* b_in;     /* GELU b1 (may be NULL = no bias), else NULL               */
   const void* b_out;    /* GELU b2 (may be NULL = no bias), else NULL               */
+  int32_t w_in_layout;  /* moe_layout_t of w_in and w_up (0, the zero default:
+                           IN_OUT); w_out is always [E, F, D]                       */
 } moe_experts_t;
 
 /*
@@ -282,7 +293,8 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
  *               w_router the logits are an independent input and dx has no router term
  *   dw_router = x^T dlogits
  * The pre-activations are recomputed from x (nothing but expert_out is kept from the
- * forward). fp32 experts only (bf16 returns MOE_ERR_UNSUPPORTED). All reductions run in
+ * forward). fp32 experts in the IN_OUT layout only (bf16 or OUT_IN returns
+ * MOE_ERR_UNSUPPORTED). All reductions run in
  * a fixed order: results are bitwise reproducible.
  */
 typedef struct {

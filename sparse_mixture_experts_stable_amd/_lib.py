@@ -14,6 +14,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_EXPERT_LINEAR, MOE_EXPERT_GELU_MLP, MOE_EXPERT_SWIGLU = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_LAYOUT_IN_OUT, MOE_LAYOUT_OUT_IN = 0, 1
 
 EXPORTED = [
     "moe_version", "moe_status_string", "moe_capacity",
@@ -43,7 +44,7 @@ sz = ctypes.c_size_t
 class Experts(ctypes.Structure):
     _fields_ = [("kind", i32), ("dtype", i32), ("num_experts", i32), ("d_model", i32),
                 ("d_hidden", i32), ("w_in", vp), ("w_up", vp), ("w_out", vp), ("b_in", vp),
-                ("b_out", vp)]
+                ("b_out", vp), ("w_in_layout", i32)]
 
 
 class RouterOpts(ctypes.Structure):

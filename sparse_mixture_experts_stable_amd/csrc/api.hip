@@ -79,8 +79,11 @@ moe_status_t check_experts(const moe_experts_t* ex) {
   if (ex->kind == MOE_EXPERT_LINEAR && ex->d_hidden != ex->d_model) return MOE_ERR_INVALID_ARG;
   if (ex->kind == MOE_EXPERT_SWIGLU && (!ex->w_up || !ex->w_out)) return MOE_ERR_INVALID_ARG;
   if (ex->kind == MOE_EXPERT_GELU_MLP && !ex->w_out) return MOE_ERR_INVALID_ARG;
+  if (ex->w_in_layout != MOE_LAYOUT_IN_OUT && ex->w_in_layout != MOE_LAYOUT_OUT_IN)
+    return MOE_ERR_INVALID_ARG;
   const int q = ex->dtype == MOE_BF16 ? 64 : 16;
   if (ex->d_model % q || ex->d_hidden % q) return MOE_ERR_UNSUPPORTED;
+  if (ex->w_in_layout == MOE_LAYOUT_OUT_IN && ex->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -117,6 +120,7 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
     a.B0 = ex->w_in;
     a.B1 = ex->kind == MOE_EXPERT_SWIGLU ? ex->w_up : nullptr;
     a.b_gstride = int64_t(D) * (pl.two_stage ? F : D);
+    a.b_kmajor = ex->w_in_layout == MOE_LAYOUT_OUT_IN;
     a.bias = ex->kind == MOE_EXPERT_GELU_MLP ? ex->b_in : nullptr;
     a.bias_gstride = F;
     a.K = D;
@@ -549,7 +553,8 @@ moe_status_t check_forward(const moe_forward_args_t* a) {
     st = check_experts(&a->shared);
     if (st != MOE_OK) return st;
     if (a->shared.kind != MOE_EXPERT_SWIGLU || a->shared.num_experts != 1 ||
-        a->shared.dtype != a->experts.dtype || a->shared.d_model != D)
+        a->shared.dtype != a->experts.dtype || a->shared.d_model != D ||
+        a->shared.w_in_layout != a->experts.w_in_layout)
       return MOE_ERR_UNSUPPORTED;
   }
   const int V = a->experts.dtype == MOE_BF16 ? 8 : 4;

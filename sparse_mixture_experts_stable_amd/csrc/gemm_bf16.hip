@@ -49,7 +49,8 @@ using namespace tile;
 // One K step: request step `nxt` into slot `nxt_slot`, then multiply the tiles in slot
 // `cur`. The two slots are distinct, which the restrict qualifiers state; that lets the
 // compiler order the LDS reads of `cur` freely against the DMA writes still in flight.
-template <class CF>
+// BKM: B is staged [n][k] like A, and its fragments are read like A's.
+template <class CF, bool BKM>
 __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
                                                    char* __restrict__ nxt_slot,
                                                    const DmaSrc<CF>& S, int nxt, int N,
@@ -57,7 +58,7 @@ __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
                                                    f32x4 (&acc)[CF::NB][CF::TM][CF::TN],
                                                    bool issue = true) {
   constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
-  if (issue) issue_stage<CF>(nxt_slot, S, nxt, N, wv);
+  if (issue) issue_stage<CF, BKM>(nxt_slot, S, nxt, N, wv);
   const int fr = lane & 15, fc = lane >> 4;
   const int arow = wm * CF::WROWS + fr;
   // B transpose-read coordinates of this lane: k row within the 32-wide k step and the
@@ -73,14 +74,20 @@ __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
     for (int q = 0; q < NB; ++q) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = wn * CF::WCOLS + j * 16 + bcol;
-        const int k0 = ks * 32 + bk;
-        const int k1 = k0 + 4;
-        const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k0 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k0)) + 2 * (col & 7)));
-        const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k1 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k1)) + 2 * (col & 7)));
-        bfr[q][j] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (BKM) {
+          const int n = wn * CF::WCOLS + j * 16 + fr;
+          bfr[q][j] = *reinterpret_cast<const bf16x8*>(Bs + q * CF::BQ_BYTES + n * (BK * 2) +
+                                                      16 * ((ks * 4 + fc) ^ fswz(n)));
+        } else {
+          const int col = wn * CF::WCOLS + j * 16 + bcol;
+          const int k0 = ks * 32 + bk;
+          const int k1 = k0 + 4;
+          const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k0 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k0)) + 2 * (col & 7)));
+          const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k1 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k1)) + 2 * (col & 7)));
+          bfr[q][j] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
       }
     }
 #pragma unroll
@@ -112,8 +119,9 @@ constexpr int kernel_lds() {
                         : 0);
 }
 
-// EPI: EPI_STORE / EPI_BIAS / EPI_GELU_BIAS / EPI_SWIGLU; OF32: store fp32 instead of bf16
-template <class CF, int EPI, bool OF32>
+// EPI: EPI_STORE / EPI_BIAS / EPI_GELU_BIAS / EPI_SWIGLU; OF32: store fp32 instead of bf16;
+// BKM: B stored [N][K]
+template <class CF, int EPI, bool OF32, bool BKM>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch batch) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
   const int wm = wv % CF::WGM, wn = wv / CF::WGM;
 
   DmaSrc<CF> S;
-  tile_sources<CF>(P, tl, wv, lane, S);
+  tile_sources<CF, BKM>(P, tl, wv, lane, S);
 
   f32x4 acc[NB][TM][TN];
 #pragma unroll
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
   constexpr int NS = CF::STAGES;
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
-    issue_stage<CF>(smem + st * CF::STAGE, S, st <= last ? st : last, N, wv);
+    issue_stage<CF, BKM>(smem + st * CF::STAGE, S, st <= last ? st : last, N, wv);
   for (int kt = 0; kt < nk; ++kt) {
     // this thread's loads for step kt have landed (S-2 later steps may still be in
     // flight); after the barrier everyone's have, and every wave is done with step kt-1,
@@ -156,8 +164,9 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const int nxt = kt + NS - 1 <= last ? kt + NS - 1 : last;
-    step_compute_issue<CF>(smem + (kt % NS) * CF::STAGE, smem + ((kt + NS - 1) % NS) * CF::STAGE,
-                           S, nxt, N, wv, wm, wn, lane, acc);
+    step_compute_issue<CF, BKM>(smem + (kt % NS) * CF::STAGE,
+                                smem + ((kt + NS - 1) % NS) * CF::STAGE, S, nxt, N, wv, wm, wn,
+                                lane, acc);
   }
   wait_vmcnt<0>();  // the clamped tail loads still target LDS
   __syncthreads();
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
 // the block's next tile, so that tile's first stage streams in while the epilogue of the
 // current one runs; the next tile's gathered row indices are read at the start of the
 // current tile.
-template <class CF, int EPI, bool OF32>
+template <class CF, int EPI, bool OF32, bool BKM>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(GemmBatch batch) {
   static_assert(CF::STAGES == 2, "two-stage ring");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
   const int wm = wv % CF::WGM, wn = wv / CF::WGM;
 
   DmaSrc<CF> S;
-  tile_sources<CF>(batch.p[tl.pi], tl, wv, lane, S);
+  tile_sources<CF, BKM>(batch.p[tl.pi], tl, wv, lane, S);
   f32x4 acc[NB][TM][TN];
 #pragma unroll
   for (int q = 0; q < NB; ++q)
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue_stage<CF>(smem, S, 0, batch.p[tl.pi].N, wv);
+  issue_stage<CF, BKM>(smem, S, 0, batch.p[tl.pi].N, wv);
   int g = 0;  // steps done by this block: stage g & 1 holds the current one
   while (true) {
     const GemmProblem& P = batch.p[tl.pi];
@@ -269,15 +278,15 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
       bool issue = true;
       if (knext == nk) {
         if (more) {
-          tile_sources_from_rows<CF>(batch.p[tl2.pi], tl2, wv, lane, rows2, S);
+          tile_sources_from_rows<CF, BKM>(batch.p[tl2.pi], tl2, wv, lane, rows2, S);
           knext = 0;
           nN = batch.p[tl2.pi].N;
         } else {
           issue = false;
         }
       }
-      step_compute_issue<CF>(smem + (g & 1) * CF::STAGE, smem + ((g + 1) & 1) * CF::STAGE, S,
-                             knext, nN, wv, wm, wn, lane, acc, issue);
+      step_compute_issue<CF, BKM>(smem + (g & 1) * CF::STAGE, smem + ((g + 1) & 1) * CF::STAGE,
+                                  S, knext, nN, wv, wm, wn, lane, acc, issue);
     }
     store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, nullptr, acc);
     if (!more) break;
@@ -318,20 +327,20 @@ void plan_tiles(GemmBatch& b) {
   }
 }
 
-template <class CF, int EPI, bool OF32>
+template <class CF, int EPI, bool OF32, bool BKM>
 moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
   plan_tiles<CF>(b);
   if (b.total == 0) return MOE_OK;
   constexpr int lds = kernel_lds<CF, EPI, OF32>();
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel<CF, EPI, OF32>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel<CF, EPI, OF32, BKM>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
       return MOE_ERR_HIP;
     attr_set = true;
   }
-  MOE_LAUNCH(name, (gemm_bf16_kernel<CF, EPI, OF32>), dim3(8 * b.xcd_max), dim3(CF::THREADS), lds,
-             s, b);
+  MOE_LAUNCH(name, (gemm_bf16_kernel<CF, EPI, OF32, BKM>), dim3(8 * b.xcd_max), dim3(CF::THREADS),
+             lds, s, b);
   return MOE_OK;
 }
 
@@ -349,14 +358,15 @@ int cu_count() {
   return n;
 }
 
-template <class CF, int EPI, bool OF32>
+template <class CF, int EPI, bool OF32, bool BKM>
 moe_status_t launch_persistent(GemmBatch& b, const char* name, hipStream_t s) {
   plan_tiles<CF>(b);
   if (b.total == 0) return MOE_OK;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_persistent_kernel<CF, EPI, OF32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kPersistentLdsMax) != hipSuccess)
+    if (hipFuncSetAttribute(
+            reinterpret_cast<const void*>(gemm_bf16_persistent_kernel<CF, EPI, OF32, BKM>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, kPersistentLdsMax) != hipSuccess)
       return MOE_ERR_HIP;
     attr_set = true;
   }
@@ -364,35 +374,40 @@ moe_status_t launch_persistent(GemmBatch& b, const char* name, hipStream_t s) {
   const int nb_min = grid / 8 > 0 ? grid / 8 : 1;  // blocks of the XCD with the fewest
   b.list_cap = (b.xcd_max + nb_min - 1) / nb_min;
   const size_t lds = CF::LDS + sizeof(int) * (size_t(b.list_cap) + CF::WAVES);
-  if (lds > size_t(kPersistentLdsMax)) return launch_cfg<CF, EPI, OF32>(b, name, s);
-  MOE_LAUNCH(name, (gemm_bf16_persistent_kernel<CF, EPI, OF32>), dim3(grid), dim3(CF::THREADS),
-             lds, s, b);
+  if (lds > size_t(kPersistentLdsMax)) return launch_cfg<CF, EPI, OF32, BKM>(b, name, s);
+  MOE_LAUNCH(name, (gemm_bf16_persistent_kernel<CF, EPI, OF32, BKM>), dim3(grid),
+             dim3(CF::THREADS), lds, s, b);
   return MOE_OK;
 }
 
-template <class CF, int EPI, bool OF32, bool PERSISTENT>
-moe_status_t launch_one(GemmBatch& b, const char* name, hipStream_t s) {
-  if constexpr (PERSISTENT)
-    return launch_persistent<CF, EPI, OF32>(b, name, s);
-  else
-    return launch_cfg<CF, EPI, OF32>(b, name, s);
-}
-
-template <class CF, bool PERSISTENT>
+template <class CF, bool BKM>
 moe_status_t launch_epi(GemmBatch& b, const char* name, hipStream_t s) {
   const int epi = b.p[0].epi;
   for (int i = 1; i < b.nprob; ++i)
     if (b.p[i].epi != epi || b.p[i].out_f32 != b.p[0].out_f32) return MOE_ERR_UNSUPPORTED;
   if (b.p[0].out_f32) {
-    if (epi != EPI_STORE) return MOE_ERR_UNSUPPORTED;
-    return launch_one<CF, EPI_STORE, true, PERSISTENT>(b, name, s);
+    if (epi != EPI_STORE || BKM) return MOE_ERR_UNSUPPORTED;
+    return launch_cfg<CF, EPI_STORE, true, false>(b, name, s);
   }
   switch (epi) {
-    case EPI_STORE: return launch_one<CF, EPI_STORE, false, PERSISTENT>(b, name, s);
-    case EPI_BIAS: return launch_one<CF, EPI_BIAS, false, PERSISTENT>(b, name, s);
-    case EPI_GELU_BIAS: return launch_one<CF, EPI_GELU_BIAS, false, PERSISTENT>(b, name, s);
+    case EPI_STORE: return launch_cfg<CF, EPI_STORE, false, BKM>(b, name, s);
+    case EPI_BIAS: return launch_cfg<CF, EPI_BIAS, false, BKM>(b, name, s);
+    case EPI_GELU_BIAS: return launch_cfg<CF, EPI_GELU_BIAS, false, BKM>(b, name, s);
     default: return MOE_ERR_UNSUPPORTED;
   }
+}
+
+template <bool BKM>
+moe_status_t launch_layout(GemmBatch& b, bool gated, bool large, const char* name,
+                           hipStream_t s) {
+  if (gated) {
+    for (int i = 0; i < b.nprob; ++i)
+      if (b.p[i].epi != EPI_SWIGLU || b.p[i].out_f32) return MOE_ERR_UNSUPPORTED;
+    return large ? launch_persistent<TileCfg<256, 256, true, 4, 4, 2>, EPI_SWIGLU, false, BKM>(b, name, s)
+                 : launch_cfg<TileCfg<128, 128, true, 2, 2, 3>, EPI_SWIGLU, false, BKM>(b, name, s);
+  }
+  return large ? launch_epi<TileCfg<256, 256, false, 4, 4, 2>, BKM>(b, name, s)
+               : launch_epi<TileCfg<128, 128, false, 2, 2, 3>, BKM>(b, name, s);
 }
 }  // namespace
 
@@ -414,14 +429,11 @@ moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStr
     tiles += long(p.groups) * ((p.m_tiles_rows + 255) / 256) * ((p.N + bnq - 1) / bnq);
   }
   if (tiles < 128) large = false;
-  if (gated) {
-    for (int i = 0; i < b.nprob; ++i)
-      if (b.p[i].epi != EPI_SWIGLU || b.p[i].out_f32) return MOE_ERR_UNSUPPORTED;
-    return large ? launch_persistent<TileCfg<256, 256, true, 4, 4, 2>, EPI_SWIGLU, false>(b, name, s)
-                 : launch_cfg<TileCfg<128, 128, true, 2, 2, 3>, EPI_SWIGLU, false>(b, name, s);
-  }
-  return large ? launch_epi<TileCfg<256, 256, false, 4, 4, 2>, false>(b, name, s)
-               : launch_epi<TileCfg<128, 128, false, 2, 2, 3>, false>(b, name, s);
+  // B layout: every problem of a batch stores B the same way
+  for (int i = 1; i < b.nprob; ++i)
+    if (b.p[i].b_kmajor != b.p[0].b_kmajor) return MOE_ERR_UNSUPPORTED;
+  return b.p[0].b_kmajor ? launch_layout<true>(b, gated, large, name, s)
+                         : launch_layout<false>(b, gated, large, name, s);
 }
 
 }  // namespace moe

@@ -103,12 +103,12 @@ struct DmaSrc {
 };
 
 // Requests the tiles of step kt into the LDS stage `dst` (one 1 KiB DMA per instruction).
-// `wv` is the wave index (uniform).
-template <class CF>
+// `wv` is the wave index (uniform). BKM: B is stored [N][K] (k contiguous, like A).
+template <class CF, bool BKM = false>
 __device__ __forceinline__ void issue_stage(char* __restrict__ dst, const DmaSrc<CF>& S, int kt,
                                             int N, int wv) {
   const size_t ka = size_t(kt) * BK * 2;
-  const size_t kb = size_t(kt) * BK * size_t(N) * 2;
+  const size_t kb = BKM ? ka : size_t(kt) * BK * size_t(N) * 2;
 #pragma unroll
   for (int t = 0; t < CF::A_INST; ++t) {
     const char* g = S.a + ka + S.ao[t];
@@ -182,8 +182,10 @@ __device__ __forceinline__ int tile_a_row(const GemmProblem& P, const TileId& t,
 // DMA sources of tile t from the A rows of tile_a_row. A: this lane's physical chunk
 // p = lane % 8 holds source chunk p ^ f(row). B: load i of wave wv is load
 // u = wv*B_INST + i overall: matrix u / B_IPQ, rows (u % B_IPQ) * B_RPI .. +B_RPI;
-// columns past N read column 0 (never stored).
-template <class CF>
+// columns past N read column 0 (never stored). BKM (B stored [N][K]): B is staged like
+// A, [n][k] with 128-byte rows and the same chunk swizzle; load u covers the 8 rows
+// (u % B_IPQ) * 8 .. +8 of its matrix, and rows past N read row 0.
+template <class CF, bool BKM = false>
 __device__ __forceinline__ void tile_sources_from_rows(const GemmProblem& P, const TileId& t,
                                                        int wv, int lane, const int* rows,
                                                        DmaSrc<CF>& S) {
@@ -195,25 +197,37 @@ __device__ __forceinline__ void tile_sources_from_rows(const GemmProblem& P, con
     const int row = (wv * CF::A_INST + i) * 8 + (lane >> 3);
     S.ao[i] = uint32_t((size_t(rows[i]) * P.lda + 8 * ((lane & 7) ^ fswz(row))) * 2);
   }
-  constexpr int CPR = CF::B_RB / 16;  // chunks per row
+  if constexpr (BKM) {
+    static_assert(CF::B_IPQ * 8 == CF::BNQ, "one 1 KiB load per 8 rows of 128 bytes");
 #pragma unroll
-  for (int i = 0; i < CF::B_INST; ++i) {
-    const int u = wv * CF::B_INST + i;
-    const int k = (u % CF::B_IPQ) * CF::B_RPI + lane / CPR;
-    const int c = (lane % CPR) ^ hswz<CF::B_RB>(k);
-    int col = t.n0 + 8 * c;
-    if (col >= P.N) col = 0;
-    S.bo[i] = uint32_t((size_t(k) * P.N + col) * 2);
+    for (int i = 0; i < CF::B_INST; ++i) {
+      const int u = wv * CF::B_INST + i;
+      const int nl = (u % CF::B_IPQ) * 8 + (lane >> 3);
+      int n = t.n0 + nl;
+      if (n >= P.N) n = 0;
+      S.bo[i] = uint32_t((size_t(n) * P.K + 8 * ((lane & 7) ^ fswz(nl))) * 2);
+    }
+  } else {
+    constexpr int CPR = CF::B_RB / 16;  // chunks per row
+#pragma unroll
+    for (int i = 0; i < CF::B_INST; ++i) {
+      const int u = wv * CF::B_INST + i;
+      const int k = (u % CF::B_IPQ) * CF::B_RPI + lane / CPR;
+      const int c = (lane % CPR) ^ hswz<CF::B_RB>(k);
+      int col = t.n0 + 8 * c;
+      if (col >= P.N) col = 0;
+      S.bo[i] = uint32_t((size_t(k) * P.N + col) * 2);
+    }
   }
 }
 
-template <class CF>
+template <class CF, bool BKM = false>
 __device__ __forceinline__ void tile_sources(const GemmProblem& P, const TileId& t, int wv,
                                              int lane, DmaSrc<CF>& S) {
   int rows[CF::A_INST];
 #pragma unroll
   for (int i = 0; i < CF::A_INST; ++i) rows[i] = tile_a_row<CF>(P, t, wv, lane, i);
-  tile_sources_from_rows<CF>(P, t, wv, lane, rows, S);
+  tile_sources_from_rows<CF, BKM>(P, t, wv, lane, rows, S);
 }
 
 // Epilogue: lane holds C[m][n..n+3] of every MFMA tile (the MFMA ran with B as its first

@@ -102,6 +102,7 @@ struct GemmProblem {
   int32_t epi;
   int32_t out_f32;  // bf16 kernel: 1 = store fp32 (router logits)
   int32_t tiles;    // groups * m_tiles * n_tiles (filled by the launcher)
+  int32_t b_kmajor; // bf16 kernel: B stored [N][K] per group (k contiguous), else [K][N]
 };
 
 struct GemmBatch {

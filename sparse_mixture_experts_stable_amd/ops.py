@@ -7,7 +7,8 @@ layer runs in the HIP kernels; nothing here computes.
 
 Experts are passed as a dict: {"kind": "linear"|"gelu"|"swiglu", "w_in": [E,D,F],
 "w_up": [E,D,F], "w_out": [E,F,D], "b_in": [E,F], "b_out": [E,D]} (absent keys = None),
-all of one dtype (float32 or bfloat16) on the GPU.
+all of one dtype (float32 or bfloat16) on the GPU. With "w_in_layout": "out_in", w_in and
+w_up are given as [E,F,D] instead (bf16 forward only).
 """
 
 from __future__ import annotations
@@ -68,14 +69,23 @@ def capacity(T, k, E, capacity_factor):
     return int(c)
 
 
+_LAYOUT = {"in_out": L.MOE_LAYOUT_IN_OUT, "out_in": L.MOE_LAYOUT_OUT_IN}
+
+
 def _experts_struct(ex):
+    """moe_experts_t of an expert dict. ``ex["w_in_layout"]``: "in_out" (the default:
+    w_in and w_up are [E, D, F]) or "out_in" ([E, F, D], a torch Linear weight per
+    expert)."""
     w_in = _c(ex["w_in"])
-    E, D = w_in.shape[0], w_in.shape[1]
-    F = w_in.shape[2]
+    layout = ex.get("w_in_layout", "in_out")
+    if layout not in _LAYOUT:
+        raise ValueError(f"w_in_layout must be one of {sorted(_LAYOUT)}")
+    E = w_in.shape[0]
+    D, F = (w_in.shape[2], w_in.shape[1]) if layout == "out_in" else (w_in.shape[1], w_in.shape[2])
     keep = {k: _c(ex.get(k)) for k in ("w_in", "w_up", "w_out", "b_in", "b_out")}
     s = L.Experts(kind=_KIND[ex["kind"]], dtype=_dt(w_in), num_experts=E, d_model=D, d_hidden=F,
                   w_in=_p(keep["w_in"]), w_up=_p(keep["w_up"]), w_out=_p(keep["w_out"]),
-                  b_in=_p(keep["b_in"]), b_out=_p(keep["b_out"]))
+                  b_in=_p(keep["b_in"]), b_out=_p(keep["b_out"]), w_in_layout=_LAYOUT[layout])
     return s, keep
 
 

@@ -158,3 +158,26 @@ def test_package_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", src), os.path.join(dirpath, f)
+
+
+def test_weight_layout_validation():
+    """w_in_layout: values other than IN_OUT / OUT_IN are invalid; OUT_IN is taken by
+    bf16 experts in the forward only, with the shared expert in the same layout."""
+    lib = L.lib()
+    p = ctypes.c_void_p(1 << 21)
+    mk = lambda dt, lay, kind=L.MOE_EXPERT_SWIGLU, E=4: L.Experts(
+        kind=kind, dtype=dt, num_experts=E, d_model=128, d_hidden=128, w_in=p, w_up=p, w_out=p,
+        w_in_layout=lay)
+    outs = {f: p for f in ("topk_idx", "topk_gate", "expert_count", "prob_sum", "aux_loss", "slot",
+                           "kept", "slot_assign", "expert_used", "expert_overflow", "token_drops",
+                           "expert_out", "y")}
+    fwd = lambda ex, sh=L.Experts(): L.ForwardArgs(x=p, ldx=128, T=8, logits=p, experts=ex,
+                                                   shared=sh, k=2, capacity=4, **outs)
+    assert lib.moe_forward(ctypes.byref(fwd(mk(L.MOE_BF16, 7))), p, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(ctypes.byref(fwd(mk(L.MOE_F32, L.MOE_LAYOUT_OUT_IN))), p, 1 << 30,
+                           None) == L.MOE_ERR_UNSUPPORTED
+    mixed = fwd(mk(L.MOE_BF16, L.MOE_LAYOUT_OUT_IN), mk(L.MOE_BF16, L.MOE_LAYOUT_IN_OUT, E=1))
+    assert lib.moe_forward(ctypes.byref(mixed), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    b = L.BackwardArgs(dy=p, x=p, ld=128, T=8, logits=p, experts=mk(L.MOE_F32, L.MOE_LAYOUT_OUT_IN),
+                       k=2, capacity=4)
+    assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED

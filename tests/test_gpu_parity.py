@@ -132,6 +132,52 @@ def test_forward_full_size(cfg):
     H.check_outputs(w, inp, h, r, d, tokens=_sample_tokens(w.T, d))
 
 
+# ---------------------------------------------------------------------------------
+# w_in / w_up stored [E, F, D] (the OUT_IN layout): same products, k-contiguous B tiles
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["swiglu_shared", "gelu_bias", "bf16_linear", "one_token"])
+def test_forward_out_in_layout_small(case):
+    w = {"swiglu_shared": SMALL[3], "gelu_bias": SMALL[2],
+         "bf16_linear": DEGENERATE["bf16_linear"], "one_token": DEGENERATE["one_token"]}[case]
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp, layout="out_in")
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.check_outputs(w, inp, h, r, d)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_forward_out_in_layout_full_size(cfg):
+    w = WORKLOADS[cfg]
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp, layout="out_in")
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.check_outputs(w, inp, h, r, d, tokens=_sample_tokens(w.T, d))
+
+
+def test_out_in_layout_rejections():
+    """OUT_IN is bf16-forward only, and the routed and shared experts must agree."""
+    ops = _ops()
+    from sparse_mixture_experts_stable_amd import _lib as L
+    w = SMALL[3]
+    inp = make_inputs(w)
+    g = H.gpu_inputs(inp)
+    C = ops.capacity(w.T, w.k, w.E, w.cf)
+    with pytest.raises(L.MoeError) as e:
+        ops.forward(g["x"], H.experts_dict(w, g, "out_in"), k=w.k, capacity=C,
+                    shared=H.shared_dict(w, g, "in_out"), w_router=g["w_router"])
+    assert e.value.status == L.MOE_ERR_UNSUPPORTED
+    w32 = SMALL[5]
+    inp32 = make_inputs(w32)
+    g32 = H.gpu_inputs(inp32)
+    with pytest.raises(L.MoeError) as e:
+        ops.forward(g32["x"], H.experts_dict(w32, g32, "out_in"), k=w32.k,
+                    capacity=ops.capacity(w32.T, w32.k, w32.E, w32.cf), w_router=g32["w_router"])
+    assert e.value.status == L.MOE_ERR_UNSUPPORTED
+
+
 def _backward_case(w, aux_scale, tokens=None):
     ops = _ops()
     inp = make_inputs(w)
