@@ -20,6 +20,8 @@
 //   16-lane group that instruction hands lane l element l % 4 of the 8-byte pieces
 //   addressed by lanes l/4 + 4v (v = 0..3), so lane s of group g points at row
 //   8g + (s%16)/4 (+4 for the second read) and column 4 (s % 4) of its 16-column slice.
+//   B stored [n][k] per expert instead (the OUT_IN weight layout, BKM) is staged and
+//   read exactly like A: one ds_read_b128 per fragment.
 //
 // Tiles: the large tile is 256 rows x 256 staged B columns (SwiGLU: 128 gate + 128 up
 // columns of the same outputs) on 16 waves (4 x 4, four per SIMD, each 64 rows x 64

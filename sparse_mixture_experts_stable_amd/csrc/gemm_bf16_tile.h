@@ -12,6 +12,7 @@
 //   group that instruction hands lane l element l % 4 of the 8-byte pieces addressed by
 //   lanes l/4 + 4v (v = 0..3), so lane s of group g points at row 8g + (s%16)/4 (+4 for
 //   the second read) and column 4 (s % 4) of its 16-column slice.
+//   B stored [n][k] (k contiguous, BKM) is laid out and read like A instead.
 // Both operands move HBM -> LDS with global_load_lds_dwordx4: one instruction moves
 // 1 KiB (64 lanes x 16 bytes) to a contiguous LDS range.
 #pragma once
