@@ -6,8 +6,9 @@ HIP path is checked against. Only the test suite, the smoke check in
 product path never calls it, and it imports nothing from the HIP package.
 
 Everything is NumPy float64. Loops follow the pages where the pages loop (the
-position-priority dispatch is the serial token-then-choice loop). Library primitives
-(a sort, a matmul, ``exp``) are used as single steps; nothing is blocked, fused or
+position-priority dispatch walks the assignments serially in token-then-choice
+order). Library primitives (a sort, a matmul, ``exp``) are used as single steps;
+nothing is blocked, fused or
 reordered beyond what the definitions state.
 
 Sources (page titles; sections named as on the pages):
@@ -265,16 +266,20 @@ def capacity(T, k, E, cf):
 
 
 def dispatch(idx, E, C):
-    """Position-priority slot assignment (P1 position_priority_dispatch; P3
-    dispatch_with_capacity without survivor renormalisation).
+    """Position-priority slot assignment (P1 trap 3 and section 2; P3
+    dispatch_with_capacity without survivor renormalisation; P4 steps 2-4).
 
-    Tokens are visited in order and, within a token, choices in order j = 0..k-1.
-    Each expert keeps a running count of accepted rows; an assignment is kept iff that
-    count is below C, and its slot is the count before the increment.
+    Definition: the assignments are ordered by their flat index a = t*k + j (earlier
+    tokens first, then a token's choices in order). The slot of a is the number of
+    earlier assignments to the same expert; a is kept iff that number is below C.
+
+    Here the assignments are walked once in that order with one arrival counter per
+    expert; the counter's value on arrival is the rank above. Every earlier arrival with
+    a rank below C was itself kept, so the kept slots of an expert are 0..used-1.
 
     Returns slot [T,k] (-1 when dropped), kept [T,k] bool, slot_assign [E,C] holding
-    the flat assignment a = t*k + j of each filled slot (-1 when empty), used [E],
-    overflow [E] = attempts - used, drops [T] = k - number kept.
+    the flat assignment a of each filled slot (-1 when empty), used [E],
+    overflow [E] = arrivals - used, drops [T] = k - number kept.
     """
     idx = np.asarray(idx)
     T, k = idx.shape
@@ -282,29 +287,27 @@ def dispatch(idx, E, C):
         raise ValueError("expert index out of range")
     if C < 0:
         raise ValueError("capacity must be >= 0")
-    used = np.zeros(E, dtype=np.int64)
-    attempts = np.zeros(E, dtype=np.int64)
-    slot = np.full((T, k), -1, dtype=np.int64)
-    kept = np.zeros((T, k), dtype=bool)
+    flat = idx.reshape(-1)
+    arrivals = np.zeros(E, dtype=np.int64)
+    rank = np.empty(T * k, dtype=np.int64)
     slot_assign = np.full((E, C), -1, dtype=np.int64)
-    for t in range(T):
-        for j in range(k):
-            e = int(idx[t, j])
-            attempts[e] += 1
-            if used[e] < C:
-                slot[t, j] = used[e]
-                slot_assign[e, used[e]] = t * k + j
-                kept[t, j] = True
-                used[e] += 1
-    overflow = attempts - used
-    drops = k - kept.sum(axis=1)
+    for a in range(T * k):
+        e = int(flat[a])
+        rank[a] = arrivals[e]
+        arrivals[e] += 1
+        if rank[a] < C:
+            slot_assign[e, rank[a]] = a
+    keep = rank < C
+    slot = np.where(keep, rank, -1).reshape(T, k)
+    kept = keep.reshape(T, k)
+    used = np.minimum(arrivals, C)
     return {
         "slot": slot,
         "kept": kept,
         "slot_assign": slot_assign,
         "used": used,
-        "overflow": overflow,
-        "drops": drops.astype(np.int64),
+        "overflow": arrivals - used,
+        "drops": (k - kept.sum(axis=1)).astype(np.int64),
     }
 
 

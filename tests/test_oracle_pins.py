@@ -731,19 +731,22 @@ def _tie_to_higher(s, k):
 
 
 def _dispatch_choice_major(idx, E, C):
+    """Planted mistake: every token's first choice is served before any second choice
+    (choice-major order instead of the flat token-then-choice order)."""
     T, k = idx.shape
-    used = np.zeros(E, dtype=np.int64)
+    arrivals = np.zeros(E, dtype=np.int64)
     slot = np.full((T, k), -1, dtype=np.int64)
-    kept = np.zeros((T, k), dtype=bool)
     for j in range(k):
         for t in range(T):
             e = idx[t, j]
-            if used[e] < C:
-                slot[t, j] = used[e]; used[e] += 1; kept[t, j] = True
-    att = np.bincount(idx.ravel(), minlength=E)
+            if arrivals[e] < C:
+                slot[t, j] = arrivals[e]
+            arrivals[e] += 1
+    kept = slot >= 0
+    used = np.minimum(arrivals, C)
     sa = np.full((E, C), -1, dtype=np.int64)
     return {"slot": slot, "kept": kept, "slot_assign": sa, "used": used,
-            "overflow": att - used, "drops": k - kept.sum(1)}
+            "overflow": arrivals - used, "drops": k - kept.sum(1)}
 
 
 def _route_aux_over_T(logits, k):
