@@ -92,6 +92,23 @@ size_t hidden_bytes(const moe_experts_t* ex, int rows) {
   return size_t(ex->num_experts) * rows * ex->d_hidden * elem_size(ex->dtype);
 }
 
+// The bf16 tile loader forms each lane's A and B byte offsets from a group's base in 32
+// bits (the base itself is 64-bit), so every row of a bf16 operand it reads must start
+// below 4 GiB from its group's base: rows * leading dimension * 2 bytes < 2^32.
+bool bf16_rows_fit(int64_t rows, int64_t ld) {
+  return rows >= 0 && ld >= 0 && rows * ld * 2 < (int64_t(1) << 32);
+}
+
+// The bf16 operands of one expert set run through that loader: x (rows of T, leading
+// dimension ldx), the hidden activation of each group (C rows routed, T dense, of F),
+// and each expert's weight matrices (D x F either way round).
+bool bf16_expert_offsets_fit(const moe_experts_t* ex, int64_t T, int64_t ldx, int64_t rows) {
+  if (ex->dtype != MOE_BF16) return true;
+  const int64_t D = ex->d_model, F = ex->d_hidden;
+  return bf16_rows_fit(T, ldx) && bf16_rows_fit(rows, F) && bf16_rows_fit(D, F) &&
+         bf16_rows_fit(F, D);
+}
+
 // The expert GEMM problems for one expert set. dense: slot_assign == NULL (all T rows).
 struct ExpertPlan {
   GemmProblem g1, g2;       // bf16
@@ -413,6 +430,7 @@ moe_status_t moe_route(const void* x, int32_t x_dtype, int64_t ldx, const void* 
     return MOE_ERR_INVALID_ARG;
   if (w_router) {
     if (!x || !valid_dtype(x_dtype) || D < 1 || ldx < D) return MOE_ERR_INVALID_ARG;
+    if (x_dtype == MOE_BF16 && !bf16_rows_fit(T, ldx)) return MOE_ERR_UNSUPPORTED;
   }
   if (!opts_ok(opts)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe_route_workspace_size(T, E)) return MOE_ERR_WORKSPACE;
@@ -425,8 +443,10 @@ moe_status_t moe_route(const void* x, int32_t x_dtype, int64_t ldx, const void* 
   }
   st = launch_route(logits, T, E, k, topk_idx, topk_gate, route_opts(opts), w, s);
   if (st != MOE_OK) return st;
+  const LoadStats ls{opts ? opts->token_fraction : nullptr,
+                     opts ? opts->probability_mass : nullptr};
   return launch_reduce_scan(T, k, E, -1, true, expert_count, prob_sum, aux_loss, nullptr, nullptr,
-                            nullptr, opts ? opts->z_loss : nullptr, w, s);
+                            nullptr, opts ? opts->z_loss : nullptr, ls, w, s);
 }
 
 size_t moe_dispatch_workspace_size(int32_t T, int32_t k, int32_t E) {
@@ -450,8 +470,8 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t
   if (st != MOE_OK) return st;
   // expert_count is not an output of moe_dispatch; the totals land in fp scratch space
   return launch_dispatch(topk_idx, T, k, E, C, false, reinterpret_cast<int32_t*>(w.fp), nullptr,
-                         nullptr, expert_used, expert_overflow, nullptr, slot, kept, slot_assign,
-                         token_drops, w, s);
+                         nullptr, expert_used, expert_overflow, nullptr, LoadStats{}, slot, kept,
+                         slot_assign, token_drops, w, s);
 }
 
 size_t moe_expert_mlp_workspace_size(const moe_experts_t* ex, int32_t rows) {
@@ -471,6 +491,7 @@ moe_status_t moe_expert_mlp(const moe_experts_t* ex, const void* x, int64_t ldx,
   if (!dense && (k < 1 || C < 0 || !expert_used)) return MOE_ERR_INVALID_ARG;
   if (ldx % (ex->dtype == MOE_BF16 ? 8 : 4)) return MOE_ERR_UNSUPPORTED;
   const int rows = dense ? T : C;
+  if (!bf16_expert_offsets_fit(ex, T, ldx, rows)) return MOE_ERR_UNSUPPORTED;
   void* hidden = hidden_cache;
   if (!hidden && hidden_bytes(ex, rows)) {
     if (!ws || ws_bytes < moe_expert_mlp_workspace_size(ex, rows)) return MOE_ERR_WORKSPACE;
@@ -487,14 +508,13 @@ moe_status_t moe_combine(int32_t dt, const void* residual, const void* shared_ou
                          const void* expert_out, const int32_t* topk_idx, const int32_t* slot,
                          const float* topk_gate, int32_t T, int32_t k, int32_t E, int32_t C,
                          int32_t D, int32_t renormalize_kept, void* y, void* stream) {
-  if (!valid_dtype(dt) || T < 1 || k < 1 || E < 1 || C < 0 || D < 1) return MOE_ERR_INVALID_ARG;
-  if (!topk_idx || !slot || !topk_gate || !y || (C > 0 && !expert_out)) return MOE_ERR_INVALID_ARG;
-  const int V = dt == MOE_BF16 ? 8 : 4;
-  const int per_row = D / V;
-  if (D % V || (per_row > 256 && per_row % 256) || (per_row < 256 && 256 % per_row))
-    return MOE_ERR_UNSUPPORTED;
+  if (!valid_dtype(dt) || T < 1 || k < 1 || E < 1 || D < 1) return MOE_ERR_INVALID_ARG;
+  if (!topk_idx || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  const bool dense = slot == nullptr;
+  if (dense ? !expert_out : (C < 0 || (C > 0 && !expert_out))) return MOE_ERR_INVALID_ARG;
+  if (dense && int64_t(T) * E >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   return launch_combine(dt, residual, D, shared_out, expert_out, topk_idx, slot, topk_gate, T, k,
-                        E, C, D, renormalize_kept ? 1 : 0, y, S(stream));
+                        E, dense ? 1 : C, D, renormalize_kept ? 1 : 0, y, S(stream));
 }
 
 // ---- forward ------------------------------------------------------------------------
@@ -549,6 +569,9 @@ moe_status_t check_forward(const moe_forward_args_t* a) {
       (C > 0 && (!a->slot_assign || !a->expert_out)))
     return MOE_ERR_INVALID_ARG;
   if (a->ldx % (a->experts.dtype == MOE_BF16 ? 8 : 4)) return MOE_ERR_UNSUPPORTED;
+  if (!bf16_expert_offsets_fit(&a->experts, T, a->ldx, C)) return MOE_ERR_UNSUPPORTED;
+  if (a->shared.w_in && !bf16_expert_offsets_fit(&a->shared, T, a->ldx, T))
+    return MOE_ERR_UNSUPPORTED;
   if (a->shared.w_in) {
     st = check_experts(&a->shared);
     if (st != MOE_OK) return st;
@@ -557,9 +580,6 @@ moe_status_t check_forward(const moe_forward_args_t* a) {
         a->shared.w_in_layout != a->experts.w_in_layout)
       return MOE_ERR_UNSUPPORTED;
   }
-  const int V = a->experts.dtype == MOE_BF16 ? 8 : 4;
-  const int per_row = D / V;
-  if ((per_row > 256 && per_row % 256) || (per_row < 256 && 256 % per_row)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 }  // namespace
@@ -585,8 +605,9 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
                     s);
   if (st != MOE_OK) return st;
   st = launch_dispatch(a->topk_idx, T, k, E, C, true, a->expert_count, a->prob_sum, a->aux_loss,
-                       a->expert_used, a->expert_overflow, a->router.z_loss, a->slot, a->kept,
-                       a->slot_assign, a->token_drops, f.rw, s);
+                       a->expert_used, a->expert_overflow, a->router.z_loss,
+                       LoadStats{a->router.token_fraction, a->router.probability_mass}, a->slot,
+                       a->kept, a->slot_assign, a->token_drops, f.rw, s);
   if (st != MOE_OK) return st;
 
   ExpertPlan plans[2];

@@ -181,3 +181,40 @@ def test_weight_layout_validation():
     b = L.BackwardArgs(dy=p, x=p, ld=128, T=8, logits=p, experts=mk(L.MOE_F32, L.MOE_LAYOUT_OUT_IN),
                        k=2, capacity=4)
     assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_bf16_shapes_past_32bit_row_offsets_are_rejected():
+    """The bf16 tile loader addresses rows with 32-bit byte offsets from each group's
+    base; shapes whose rows start 4 GiB or more from it (x of 2^20 tokens at d_model
+    2048, a dense shared hidden of 2^22 rows at width 512) are refused before any launch,
+    and the largest shapes below the limit pass validation (the workspace check that
+    follows fails instead, so nothing runs)."""
+    lib = L.lib()
+    p = ctypes.c_void_p(1 << 21)
+    outs = {f: p for f in ("topk_idx", "topk_gate", "expert_count", "prob_sum", "aux_loss", "slot",
+                           "kept", "slot_assign", "expert_used", "expert_overflow", "token_drops",
+                           "expert_out", "y")}
+    ex = L.Experts(kind=L.MOE_EXPERT_SWIGLU, dtype=L.MOE_BF16, num_experts=8, d_model=2048,
+                   d_hidden=512, w_in=p, w_up=p, w_out=p)
+    big = L.ForwardArgs(x=p, ldx=2048, T=1 << 20, w_router=p, logits=p, experts=ex, k=1,
+                        capacity=1024, **outs)
+    assert lib.moe_forward(ctypes.byref(big), p, 1 << 62, None) == L.MOE_ERR_UNSUPPORTED
+    ok = L.ForwardArgs(x=p, ldx=2048, T=(1 << 20) - 1, w_router=p, logits=p, experts=ex, k=1,
+                       capacity=1024, **outs)
+    assert lib.moe_forward(ctypes.byref(ok), p, 1, None) == L.MOE_ERR_WORKSPACE
+    # the shared expert's hidden activation, [T, 512] bf16, over 2^22 rows
+    sh = L.Experts(kind=L.MOE_EXPERT_SWIGLU, dtype=L.MOE_BF16, num_experts=1, d_model=64,
+                   d_hidden=512, w_in=p, w_up=p, w_out=p)
+    ex64 = L.Experts(kind=L.MOE_EXPERT_SWIGLU, dtype=L.MOE_BF16, num_experts=8, d_model=64,
+                     d_hidden=64, w_in=p, w_up=p, w_out=p)
+    a = L.ForwardArgs(x=p, ldx=64, T=1 << 22, w_router=p, logits=p, experts=ex64, shared=sh, k=1,
+                      capacity=1024, **outs)
+    assert lib.moe_forward(ctypes.byref(a), p, 1 << 62, None) == L.MOE_ERR_UNSUPPORTED
+    # moe_route's router GEMM on bf16 x
+    assert lib.moe_route(p, L.MOE_BF16, 2048, p, p, 1 << 20, 2048, 8, 1, p, p, p, p, p, None, p,
+                         1 << 62, None) == L.MOE_ERR_UNSUPPORTED
+    # moe_expert_mlp, routed and dense
+    assert lib.moe_expert_mlp(ctypes.byref(ex), p, 2048, 1 << 20, 1, 1024, p, p, p, p, p, 1 << 62,
+                              None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_mlp(ctypes.byref(sh), p, 64, 1 << 22, 1, 0, None, None, p, p, p, 1 << 62,
+                              None) == L.MOE_ERR_UNSUPPORTED
