@@ -45,10 +45,13 @@
  *     readable with moe_read_error.
  *   - Index outputs are int32; the kept mask is one byte per assignment. An
  *     assignment a = t*k + j is token t's j-th choice.
- *   - Shape limits: 1 <= E <= 1024, 1 <= k <= min(E, 256). bf16 expert GEMMs need
- *     d_model and d_hidden to be multiples of 64; fp32 ones multiples of 16. The
- *     OUT_IN weight layout needs bf16 experts, the forward, and (moe_forward) the same
- *     layout for the routed and the shared experts.
+ *   - Shape limits: 1 <= E <= 1024, 1 <= k <= min(E, 256), T * k < 2^31. bf16 expert
+ *     GEMMs need d_model and d_hidden to be multiples of 64; fp32 ones multiples of 16.
+ *     bf16 operands are addressed with 32-bit byte offsets from each expert's base, so
+ *     x (T rows of ldx), a hidden activation (C rows routed, T rows for the shared
+ *     expert, of d_hidden) and one expert's weight matrix must each stay below 4 GiB.
+ *     The OUT_IN weight layout needs bf16 experts, the forward, and (moe_forward) the
+ *     same layout for the routed and the shared experts. The combine takes any d_model.
  *     Anything else returns MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H_
@@ -121,6 +124,11 @@ typedef struct {
  *                    by their sum (a token with nothing kept gets no expert term).
  *                    Used by moe_forward's combine and by moe_backward.
  *   z_loss           device [1] fp32 or NULL: mean over tokens of (log sum_e exp s)^2.
+ *   token_fraction   device [E] fp32 or NULL: f_e = count_e / T, the fraction of tokens
+ *                    that chose expert e ("Top-k MoE Router with Load Statistics", f_e
+ *                    equation; counts before any drop).
+ *   probability_mass device [E] fp32 or NULL: m_e = prob_sum_e / T, the mean softmax
+ *                    probability of expert e over the tokens (same page, m_e equation).
  * The aux loss keeps P_e = mean softmax probability and the counts of the selection
  * actually made under every variant.
  */
@@ -130,6 +138,8 @@ typedef struct {
   const float* selection_bias;
   int32_t renormalize_kept;
   float* z_loss;
+  float* token_fraction;
+  float* probability_mass;
 } moe_router_opts_t;
 
 /* Library version string, e.g. "moe-gfx950 0.1". */
@@ -218,7 +228,15 @@ moe_status_t moe_expert_mlp(const moe_experts_t* ex, const void* x, int64_t ldx,
  * renormalize_kept = 1 each kept gate is first divided by the token's kept gate sum
  * ("Module 7. Mixture of Experts", dispatch_with_capacity, renormalize_kept_gates).
  *   residual, shared_out  device, [T, D] of dt, each may be NULL (term omitted).
- *   expert_out            device, [E, C, D] of dt.
+ *   expert_out            device, [E, C, D] of dt (the slot buffers).
+ *   slot                  device, [T, k] int32, or NULL: then every choice is kept and
+ *                         expert_out holds one output per token and expert, [T, E, D],
+ *                         row (t, topk_idx[t, j]) -- the precomputed expert outputs of
+ *                         "Top-k MoE Router with Load Statistics" (C is then ignored;
+ *                         T * E must be below 2^31).
+ * Any D >= 1: rows that split into 16-byte pieces tiling 256 threads (D / 8 for bf16,
+ * D / 4 for fp32, dividing 256 or a multiple of it) take the vector kernel, other D a
+ * one-element-per-thread kernel with the same summation order.
  * Precondition: 0 <= topk_idx < E and slot < C (violations are skipped).
  */
 moe_status_t moe_combine(int32_t dt, const void* residual, const void* shared_out,
@@ -227,8 +245,13 @@ moe_status_t moe_combine(int32_t dt, const void* residual, const void* shared_ou
                          int32_t k, int32_t E, int32_t C, int32_t D,
                          int32_t renormalize_kept, void* y, void* stream);
 
-/* The whole forward pass in one call: routing, dispatch, experts, shared expert,
- * combine and aux loss, all enqueued on one stream with no host synchronisation. */
+/* The whole forward pass in one call ("Sparse MoE Layer in NumPy", section 2 forward and
+ * section 4 usage; "Module 7. Mixture of Experts", EducationalMoE.forward; llm-atlas
+ * "Mixture of Experts", TopKMoE.forward): router scores, routing, capacity dispatch,
+ * the routed experts on their slot buffers, the shared expert, the gate-weighted
+ * combine onto the residual and the pre-drop aux loss, all enqueued on one stream with
+ * no host synchronisation. Each step is the one of the entry point above that names
+ * it (moe_route, moe_dispatch, moe_expert_mlp, moe_combine); the outputs are theirs. */
 typedef struct {
   const void* x;            /* device [T, ldx], experts.dtype                          */
   int64_t ldx;

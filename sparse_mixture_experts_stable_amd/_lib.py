@@ -49,7 +49,7 @@ class Experts(ctypes.Structure):
 
 class RouterOpts(ctypes.Structure):
     _fields_ = [("scoring", i32), ("selection_bias", vp), ("renormalize_kept", i32),
-                ("z_loss", vp)]
+                ("z_loss", vp), ("token_fraction", vp), ("probability_mass", vp)]
 
 
 class ForwardArgs(ctypes.Structure):

@@ -104,6 +104,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
                                                       int k, int E, int C, int D, int64_t ldr,
                                                       int renorm, T* __restrict__ y) {
   constexpr int V = Vec<T>::N;
+  const bool dense = slot == nullptr;
   const int per_row = D / V;
   int t, col;
   if (per_row >= 256) {
@@ -136,12 +137,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
     K = 0.f;
     for (int j = 0; j < k; ++j) {
       const int e = idx[size_t(t) * k + j];
-      const int sl = slot[size_t(t) * k + j];
+      const int sl = dense ? 0 : slot[size_t(t) * k + j];
       if (sl >= 0 && sl < C && e >= 0 && e < E) K += gate[size_t(t) * k + j];
     }
   }
   for (int j0 = 0; j0 < k; j0 += KB) {
-    int off[KB];
+    int64_t off[KB];
     float g[KB];
 #pragma unroll
     for (int b = 0; b < KB; ++b) {
@@ -150,9 +151,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
       const int j = j0 + b;
       if (j < k) {
         const int e = idx[size_t(t) * k + j];
-        const int sl = slot[size_t(t) * k + j];
+        const int sl = dense ? 0 : slot[size_t(t) * k + j];
         if (sl >= 0 && sl < C && e >= 0 && e < E) {
-          off[b] = e * C + sl;
+          off[b] = dense ? int64_t(t) * E + e : int64_t(e) * C + sl;
           g[b] = gate ? gate[size_t(t) * k + j] : 1.0f;
           if (renorm) g[b] = g[b] / K;
         }
@@ -169,10 +170,76 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
   Vec<T>::store(y + size_t(t) * D + col, acc);
 }
 
+__device__ __forceinline__ float load_f32(const float* p) { return *p; }
+__device__ __forceinline__ float load_f32(const bf16_t* p) { return bf16_to_f32(*p); }
+
+// The same sum for any d_model: one output element per thread, the token's choices
+// read by every thread of its row. Used where a row cannot be split into 16-byte
+// pieces that tile the 256-thread block evenly.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_generic_kernel(
+    const T* __restrict__ residual, const T* __restrict__ shared_out,
+    const T* __restrict__ expert_out, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ slot, const float* __restrict__ gate, int T_, int k, int E,
+    int C, int D, int64_t ldr, int renorm, T* __restrict__ y) {
+  const int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (g >= int64_t(T_) * D) return;
+  const int t = int(g / D), c = int(g - int64_t(t) * D);
+  const bool dense = slot == nullptr;
+  float acc = residual ? load_f32(residual + size_t(t) * ldr + c) : 0.f;
+  if (shared_out) acc += load_f32(shared_out + size_t(t) * D + c);
+  float K = 1.0f;
+  if (renorm) {
+    K = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[size_t(t) * k + j];
+      const int sl = dense ? 0 : slot[size_t(t) * k + j];
+      if (sl >= 0 && sl < C && e >= 0 && e < E) K += gate[size_t(t) * k + j];
+    }
+  }
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[size_t(t) * k + j];
+    const int sl = dense ? 0 : slot[size_t(t) * k + j];
+    if (sl < 0 || sl >= C || e < 0 || e >= E) continue;
+    float gj = gate ? gate[size_t(t) * k + j] : 1.0f;
+    if (renorm) gj = gj / K;
+    const int64_t row = dense ? int64_t(t) * E + e : int64_t(e) * C + sl;
+    acc = fmaf(gj, load_f32(expert_out + size_t(row) * D + c), acc);
+  }
+  if constexpr (sizeof(T) == 2) reinterpret_cast<bf16_t*>(y)[size_t(t) * D + c] = f32_to_bf16(acc);
+  else y[size_t(t) * D + c] = acc;
+}
+
+// Whether the 16-byte combine tiles rows of d_model D: D a multiple of the vector width
+// and D / width dividing 256 or a multiple of 256. Otherwise the generic kernel runs.
+bool combine_vector_shape(int dt, int D) {
+  const int V = dt == MOE_BF16 ? 8 : 4;
+  const int per_row = D / V;
+  return D % V == 0 && ((per_row >= 256 && per_row % 256 == 0) || (per_row < 256 && 256 % per_row == 0));
+}
+
 moe_status_t launch_combine(int dt, const void* residual, int64_t ldr, const void* shared_out,
                             const void* expert_out, const int32_t* idx, const int32_t* slot,
                             const float* gate, int T, int k, int E, int C, int D, int renorm,
                             void* y, hipStream_t s) {
+  const int rn = renorm && gate ? 1 : 0;
+  // vector loads also need 16-byte aligned rows of the residual
+  if (!combine_vector_shape(dt, D) || (residual && ldr % (dt == MOE_BF16 ? 8 : 4))) {
+    const int64_t n = int64_t(T) * D;
+    const dim3 grid(unsigned((n + 255) / 256));
+    if (dt == MOE_BF16) {
+      MOE_LAUNCH("combine", combine_generic_kernel<bf16_t>, grid, dim3(256), 0, s,
+                 static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(shared_out),
+                 static_cast<const bf16_t*>(expert_out), idx, slot, gate, T, k, E, C, D, ldr, rn,
+                 static_cast<bf16_t*>(y));
+    } else {
+      MOE_LAUNCH("combine", combine_generic_kernel<float>, grid, dim3(256), 0, s,
+                 static_cast<const float*>(residual), static_cast<const float*>(shared_out),
+                 static_cast<const float*>(expert_out), idx, slot, gate, T, k, E, C, D, ldr, rn,
+                 static_cast<float*>(y));
+    }
+    return MOE_OK;
+  }
   const int V = dt == MOE_BF16 ? 8 : 4;
   const int per_row = D / V;
   int blocks;
@@ -186,12 +253,12 @@ moe_status_t launch_combine(int dt, const void* residual, int64_t ldr, const voi
     MOE_LAUNCH("combine", (combine_kernel<bf16_t, 4>), dim3(blocks), dim3(256), 0, s,
                static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(shared_out),
                static_cast<const bf16_t*>(expert_out), idx, slot, gate, T, k, E, C, D,
-               ldr, renorm && gate ? 1 : 0, static_cast<bf16_t*>(y));
+               ldr, rn, static_cast<bf16_t*>(y));
   } else {
     MOE_LAUNCH("combine", (combine_kernel<float, 4>), dim3(blocks), dim3(256), 0, s,
                static_cast<const float*>(residual), static_cast<const float*>(shared_out),
                static_cast<const float*>(expert_out), idx, slot, gate, T, k, E, C, D,
-               ldr, renorm && gate ? 1 : 0, static_cast<float*>(y));
+               ldr, rn, static_cast<float*>(y));
   }
   return MOE_OK;
 }

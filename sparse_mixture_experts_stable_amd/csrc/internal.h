@@ -44,12 +44,18 @@ moe_status_t launch_route(const float* logits, int T, int E, int k, int32_t* idx
                           const RouteOpts& o, const RouteWs& w, hipStream_t s);
 moe_status_t launch_count(const int32_t* idx, int T, int k, int E, const RouteWs& w,
                           hipStream_t s);
+// Optional per-expert load statistics written by the scan: token_fraction = count / T,
+// probability_mass = prob_sum / T (each may be NULL).
+struct LoadStats {
+  float* token_fraction;
+  float* probability_mass;
+};
 // with_prob: prob_part is valid (computes prob_sum and aux); C < 0: routing only;
 // z_loss != NULL: zpart is valid, z_loss = sum of zpart / T.
 moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int32_t* count,
                                 float* prob_sum, float* aux, int32_t* used, int32_t* overflow,
-                                int32_t* slot_assign, float* z_loss, const RouteWs& w,
-                                hipStream_t s);
+                                int32_t* slot_assign, float* z_loss, const LoadStats& ls,
+                                const RouteWs& w, hipStream_t s);
 // `used` (from launch_reduce_scan) also drives the -1 fill of unfilled slots.
 moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32_t* slot,
                            uint8_t* kept, int32_t* slot_assign, int32_t* drops,
@@ -60,9 +66,9 @@ moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32
 constexpr int64_t kFusedScanEntries = 16384;
 moe_status_t launch_dispatch(const int32_t* idx, int T, int k, int E, int C, bool with_prob,
                              int32_t* count, float* prob_sum, float* aux, int32_t* used,
-                             int32_t* overflow, float* z_loss, int32_t* slot, uint8_t* kept,
-                             int32_t* slot_assign, int32_t* drops, const RouteWs& w,
-                             hipStream_t s);
+                             int32_t* overflow, float* z_loss, const LoadStats& ls,
+                             int32_t* slot, uint8_t* kept, int32_t* slot_assign, int32_t* drops,
+                             const RouteWs& w, hipStream_t s);
 
 // ---- grouped GEMMs ----------------------------------------------------------------
 enum Epi : int32_t {

@@ -351,7 +351,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     int with_prob, int32_t* __restrict__ count_out, float* __restrict__ prob_out,
     float* __restrict__ aux_out, int32_t* __restrict__ used_out,
     int32_t* __restrict__ overflow_out, int32_t* __restrict__ flags,
-    const float* __restrict__ zpart, int nb, float* __restrict__ z_out) {
+    const float* __restrict__ zpart, int nb, float* __restrict__ z_out, LoadStats ls) {
   __shared__ int s_c[1024];
   __shared__ float s_p[1024];
   const int tid = threadIdx.x;
@@ -389,8 +389,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(
       P_e += s_p[q * E + e];
     }
     count_out[e] = total;
+    if (ls.token_fraction) ls.token_fraction[e] = float(total) / float(T);
     if (with_prob) {
       prob_out[e] = P_e;
+      if (ls.probability_mass) ls.probability_mass[e] = P_e / float(T);
       fpv = (float(total) / (float(T) * float(k))) * (P_e / float(T));
     }
     if (C >= 0) {
@@ -517,6 +519,7 @@ struct ScanOut {
   int32_t* overflow;
   float* z_loss;     // NULL: no z-loss
   int with_prob;
+  LoadStats ls;      // optional count / T and prob_sum / T
 };
 
 template <bool FUSED>
@@ -554,8 +557,10 @@ __global__ __launch_bounds__(256) void assign_kernel(
         const int u = min(total, C);
         so.used[tid] = u;
         so.overflow[tid] = total - u;
+        if (so.ls.token_fraction) so.ls.token_fraction[tid] = float(total) / float(T);
         if (so.with_prob) {
           so.prob_sum[tid] = pr.all;
+          if (so.ls.probability_mass) so.ls.probability_mass[tid] = pr.all / float(T);
           fpv = (float(total) / (float(T) * float(k))) * (pr.all / float(T));
         }
       }
@@ -717,8 +722,8 @@ moe_status_t launch_count(const int32_t* idx, int T, int k, int E, const RouteWs
 
 moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int32_t* count,
                                 float* prob_sum, float* aux, int32_t* used, int32_t* overflow,
-                                int32_t* slot_assign, float* z_loss, const RouteWs& w,
-                                hipStream_t s) {
+                                int32_t* slot_assign, float* z_loss, const LoadStats& ls,
+                                const RouteWs& w, hipStream_t s) {
   (void)slot_assign;
   const int nb = route_blocks(T);
   const int nchunks = scan_chunks(T);
@@ -729,7 +734,8 @@ moe_status_t launch_reduce_scan(int T, int k, int E, int C, bool with_prob, int3
   if (P > nchunks) P = nchunks;
   MOE_LAUNCH("scan", scan_kernel, dim3(1), dim3(1024), 0, s, w.chunk_cnt, w.chunk_prob,
              C >= 0 ? w.chunk_off : nullptr, nchunks, P, T, k, E, C, with_prob ? 1 : 0, count,
-             prob_sum, aux, used, overflow, w.flags, w.zpart, nb, with_prob ? z_loss : nullptr);
+             prob_sum, aux, used, overflow, w.flags, w.zpart, nb, with_prob ? z_loss : nullptr,
+             LoadStats{ls.token_fraction, with_prob ? ls.probability_mass : nullptr});
   return MOE_OK;
 }
 
@@ -756,14 +762,14 @@ moe_status_t launch_assign(const int32_t* idx, int T, int k, int E, int C, int32
 
 moe_status_t launch_dispatch(const int32_t* idx, int T, int k, int E, int C, bool with_prob,
                              int32_t* count, float* prob_sum, float* aux, int32_t* used,
-                             int32_t* overflow, float* z_loss, int32_t* slot, uint8_t* kept,
-                             int32_t* slot_assign, int32_t* drops, const RouteWs& w,
-                             hipStream_t s) {
+                             int32_t* overflow, float* z_loss, const LoadStats& ls,
+                             int32_t* slot, uint8_t* kept, int32_t* slot_assign, int32_t* drops,
+                             const RouteWs& w, hipStream_t s) {
   const int nb = route_blocks(T);
   const int nchunks = scan_chunks(T);
   if (E > 256 || int64_t(nchunks) * E > kFusedScanEntries) {
     moe_status_t st = launch_reduce_scan(T, k, E, C, with_prob, count, prob_sum, aux, used,
-                                         overflow, slot_assign, z_loss, w, s);
+                                         overflow, slot_assign, z_loss, ls, w, s);
     if (st != MOE_OK) return st;
     return launch_assign(idx, T, k, E, C, slot, kept, slot_assign, drops, used, w, s);
   }
@@ -774,7 +780,8 @@ moe_status_t launch_dispatch(const int32_t* idx, int T, int k, int E, int C, boo
   const int blocks = (T + tokens - 1) / tokens;
   const size_t shmem = sizeof(int) * (5 * size_t(E) + tokens);
   ScanOut so{count, prob_sum, aux, used, overflow, with_prob ? z_loss : nullptr,
-             with_prob ? 1 : 0};
+             with_prob ? 1 : 0,
+             LoadStats{ls.token_fraction, with_prob ? ls.probability_mass : nullptr}};
   MOE_LAUNCH("assign", assign_kernel<true>, dim3(blocks + 1), dim3(256), shmem, s, idx, T, k, E,
              C, G, nullptr, w.cnt_part, assign_ebits(E), nullptr, slot, kept, slot_assign, drops,
              w.flags, w.chunk_cnt, w.chunk_prob, nchunks, w.zpart, nb, so);

@@ -24,13 +24,16 @@ _KIND = {"linear": L.MOE_EXPERT_LINEAR, "gelu": L.MOE_EXPERT_GELU_MLP,
 _SCORING = {"softmax": L.MOE_SCORE_SOFTMAX, "sigmoid": L.MOE_SCORE_SIGMOID}
 
 
-def _router_opts(scoring, selection_bias, renormalize_kept, z_loss_out):
-    """moe_router_opts_t for the router variants; returns (struct, tensors to keep)."""
+def _router_opts(scoring, selection_bias, renormalize_kept, z_loss_out, token_fraction=None,
+                 probability_mass=None):
+    """moe_router_opts_t for the router variants and the optional load statistics;
+    returns (struct, tensors to keep)."""
     bias = None
     if selection_bias is not None:
         bias = selection_bias.to(torch.float32).contiguous()
     o = L.RouterOpts(scoring=_SCORING[scoring], selection_bias=_p(bias),
-                     renormalize_kept=1 if renormalize_kept else 0, z_loss=_p(z_loss_out))
+                     renormalize_kept=1 if renormalize_kept else 0, z_loss=_p(z_loss_out),
+                     token_fraction=_p(token_fraction), probability_mass=_p(probability_mass))
     return o, bias
 
 
@@ -92,7 +95,9 @@ def _experts_struct(ex):
 def route(*, k, logits=None, x=None, w_router=None, scoring="softmax", selection_bias=None,
           z_loss=False):
     """moe_route. Either logits [T,E] fp32, or x [T,D] and w_router [D,E]. ``scoring``,
-    ``selection_bias`` ([E]) and ``z_loss`` select the router variants."""
+    ``selection_bias`` ([E]) and ``z_loss`` select the router variants. Besides the
+    routing outputs, returns the router page's load statistics token_fraction
+    (count / T) and probability_mass (prob_sum / T), both [E] fp32."""
     if w_router is not None:
         x = _c(x)
         w_router = _c(w_router)
@@ -113,7 +118,9 @@ def route(*, k, logits=None, x=None, w_router=None, scoring="softmax", selection
     prob = torch.empty(E, dtype=torch.float32, device=dev)
     aux = torch.empty(1, dtype=torch.float32, device=dev)
     zl = torch.empty(1, dtype=torch.float32, device=dev) if z_loss else None
-    opts, bias = _router_opts(scoring, selection_bias, False, zl)
+    tf = torch.empty(E, dtype=torch.float32, device=dev)
+    pm = torch.empty(E, dtype=torch.float32, device=dev)
+    opts, bias = _router_opts(scoring, selection_bias, False, zl, tf, pm)
     ws = _ws(L.lib().moe_route_workspace_size(T, E), dev)
     st = L.lib().moe_route(_p(x) if w_router is not None else None, xdt, D, _p(w_router), _p(logits),
                            T, D, E, k, _p(idx), _p(gate), _p(count), _p(prob), _p(aux),
@@ -121,7 +128,7 @@ def route(*, k, logits=None, x=None, w_router=None, scoring="softmax", selection
     L.check("moe_route", st)
     del bias
     out = {"logits": logits, "topk_idx": idx, "topk_gate": gate, "expert_count": count,
-           "prob_sum": prob, "aux_loss": aux}
+           "prob_sum": prob, "aux_loss": aux, "token_fraction": tf, "probability_mass": pm}
     if z_loss:
         out["z_loss"] = zl
     return out
@@ -181,10 +188,15 @@ def expert_mlp(experts, x, *, k=1, C=0, slot_assign=None, expert_used=None, keep
 def combine(expert_out, topk_idx, slot, topk_gate, *, residual=None, shared_out=None,
             renormalize_kept=False):
     """moe_combine: y = residual + shared + sum_kept gate * expert_out[idx, slot] (gates
-    renormalised over the survivors with ``renormalize_kept``)."""
+    renormalised over the survivors with ``renormalize_kept``). With ``slot`` None,
+    expert_out is [T, E, D], one output per token and expert, and every choice counts."""
     eo = _c(expert_out)
-    E, C, D = eo.shape
     T, k = topk_idx.shape
+    if slot is None:
+        _, E, D = eo.shape
+        C = 0
+    else:
+        E, C, D = eo.shape
     ref = residual if residual is not None else eo
     y = torch.empty(T, D, dtype=eo.dtype, device=eo.device)
     st = L.lib().moe_combine(_dt(eo), _p(_c(residual)), _p(_c(shared_out)), _p(eo),
@@ -193,6 +205,26 @@ def combine(expert_out, topk_idx, slot, topk_gate, *, residual=None, shared_out=
     L.check("moe_combine", st)
     del ref
     return y
+
+
+def topk_router(x, w_router, expert_outputs, shared_output, k):
+    """The result contract of "Top-k MoE Router with Load Statistics": router scores
+    x w_router, top-k by score (ties to the lower index) with softmax weights over the k
+    chosen, y = shared_output + sum_j weight_j * expert_outputs[t, e_j], and the load
+    statistics f (token_fraction) and m (probability_mass). The routing math is fp32 in
+    moe_route; y is the fp32 combine of moe_combine in its dense mode. Returns the
+    page's dictionary: selected_experts int64, every other result in x's dtype, all on
+    x's device (dtype casts only; every value comes from the library)."""
+    r = route(k=k, x=x, w_router=w_router)
+    eo = _c(expert_outputs).to(x.dtype)
+    y = combine(eo, r["topk_idx"], None, r["topk_gate"], shared_out=_c(shared_output).to(x.dtype))
+    return {
+        "output": y,
+        "selected_experts": r["topk_idx"].to(torch.int64),
+        "selected_weights": r["topk_gate"].to(x.dtype),
+        "token_fraction": r["token_fraction"].to(x.dtype),
+        "probability_mass": r["probability_mass"].to(x.dtype),
+    }
 
 
 def forward(x, experts, *, k, capacity, w_router=None, logits=None, shared=None,
@@ -234,9 +266,12 @@ def forward(x, experts, *, k, capacity, w_router=None, logits=None, shared=None,
                        if keep_shared_out and shared is not None else None),
         "capacity": C,
         "z_loss": torch.empty(1, dtype=torch.float32, device=dev) if z_loss else None,
+        "token_fraction": torch.empty(E, dtype=torch.float32, device=dev),
+        "probability_mass": torch.empty(E, dtype=torch.float32, device=dev),
         "router": {"scoring": scoring, "renormalize_kept": bool(renormalize_kept)},
     }
-    ropts, bias = _router_opts(scoring, selection_bias, renormalize_kept, o["z_loss"])
+    ropts, bias = _router_opts(scoring, selection_bias, renormalize_kept, o["z_loss"],
+                               o["token_fraction"], o["probability_mass"])
     a = L.ForwardArgs(
         x=_p(x), ldx=x.stride(0), T=T, w_router=_p(w_router), logits=_p(logits), experts=es,
         shared=shs, k=k, capacity=C, use_residual=1 if use_residual else 0,
