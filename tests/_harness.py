@@ -137,29 +137,82 @@ def check_routing_dispatch(w, inp, h):
     return r, d
 
 
-def check_outputs(w, inp, h, r, d, tokens=None):
-    """Expert outputs (kept slots) and y for the given tokens against the oracle."""
+def ulp(v, dtype):
+    """Spacing of the floating-point grid of ``dtype`` ("bf16" or "f32") at the values v:
+    2^(floor(log2|v|) - mantissa bits), and the smallest normal spacing at zero."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    mant = 7 if dtype == "bf16" else 23
+    e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    e = np.maximum(e, -126.0)
+    return np.where(v > 0, np.exp2(e - mant), np.exp2(-126.0 - mant))
+
+
+def assert_routed_close(y_got, x, sh_got, routed_want, residual, dtype, what="routed"):
+    """The routed part of y, y - r x - Sh, against the oracle's sum over kept choices of
+    gate * o. y is rounded once to ``dtype`` after an fp32 sum (x, then Sh, then the
+    gated rows), so y - r x - Sh recovers the GPU's routed sum up to half a unit in the
+    last place of y plus the fp32 rounding of that sum; the bound is the usual relative
+    bound on the routed term plus those two. This keeps the residual's magnitude out of
+    the tolerance on the expert outputs."""
+    y_got = np.asarray(y_got, dtype=np.float64)
+    base = np.zeros_like(y_got)
+    if residual:
+        base = base + np.asarray(x, dtype=np.float64)
+    if sh_got is not None:
+        base = base + np.asarray(sh_got, dtype=np.float64)
+    routed_got = y_got - base
+    want = np.asarray(routed_want, dtype=np.float64)
+    rtol = RTOL[dtype]
+    rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
+    slack = 0.5 * ulp(y_got, dtype) + 8.0 * 2.0 ** -24 * (np.abs(base) + np.abs(want))
+    err = np.abs(routed_got - want)
+    bound = rtol * (np.abs(want) + rms) + slack
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), want.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())}/{want.size} outside tolerance; worst at {i}: got "
+            f"{routed_got[i]!r} want {want[i]!r} (rtol {rtol}, rms {rms:.3e}, slack {slack[i]:.3e})")
+
+
+def gather_kept_rows(h, idx, slot, kept):
+    """The GPU's expert_out rows of the kept choices, as [n_tokens, k, D] (zeros where
+    dropped), read through the same (expert, slot) pairs the oracle's dispatch gives."""
+    eo = h["expert_out"]
+    n, k = idx.shape
+    got = np.zeros((n, k, eo.shape[-1]), dtype=np.float64)
+    tt, jj = np.nonzero(kept)
+    got[tt, jj] = eo[idx[tt, jj], slot[tt, jj]]
+    return got
+
+
+def check_outputs(w, inp, h, r, d, tokens=None, idx=None, gate=None, renormalize=False):
+    """Every kept expert output row, the shared expert's output, y and the routed part
+    of y for the given tokens (all tokens by default), against the oracle. ``idx`` and
+    ``gate`` default to the oracle's routing (equal to the GPU's where these are
+    called)."""
     T = w.T
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     bf16 = w.dtype == "bf16"
     rtol = RTOL[w.dtype]
+    idx = r["idx"] if idx is None else idx
+    gate = r["gate"] if gate is None else gate
     x = to_numpy_f32(inp["x"])
     wts = oracle_weights(inp)
-    o = om.expert_outputs(w.kind, wts, x, r["idx"], d["kept"], tokens=tokens, bf16=bf16)
-    # GPU expert_out rows of the kept choices of these tokens
-    k = w.k
-    got_o = np.zeros_like(o)
-    for i, t in enumerate(tokens):
-        for j in range(k):
-            if d["kept"][t, j]:
-                got_o[i, j] = h["expert_out"][r["idx"][t, j], d["slot"][t, j]]
-    assert_close(got_o, o, rtol, "expert_out")
+    kept = d["kept"][tokens]
+    o = om.expert_outputs(w.kind, wts, x, idx, d["kept"], tokens=tokens, bf16=bf16)
+    got_o = gather_kept_rows(h, idx[tokens], d["slot"][tokens], kept)
+    assert_close(got_o[kept], o[kept], rtol, "expert_out")
     sh = None
+    sh_got = None
     shared = oracle_shared(inp)
     if shared is not None:
         sh = om.shared_apply(shared, x[tokens], bf16=bf16)
-        assert_close(h["shared_out"][tokens], sh, rtol, "shared_out")
-    y = om.combine(x[tokens], sh, o, r["gate"][tokens], d["kept"][tokens], w.residual)
+        sh_got = h["shared_out"][tokens]
+        assert_close(sh_got, sh, rtol, "shared_out")
+    y = om.combine(x[tokens], sh, o, gate[tokens], kept, w.residual, renormalize=renormalize)
     if bf16:
         y = om.bf16_round(y)
     assert_close(h["y"][tokens], y, rtol, "y")
+    routed = om.combine(x[tokens], None, o, gate[tokens], kept, False, renormalize=renormalize)
+    assert_routed_close(h["y"][tokens], x[tokens], sh_got, routed, w.residual, w.dtype)

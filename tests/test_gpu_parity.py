@@ -6,8 +6,12 @@ aux loss within 1e-4 relative; fp32 outputs and gradients within 1e-4 and bf16 o
 within 2e-2 (metric in tests/_harness.py).
 
 Sizes: each workload at a reduced size the oracle finishes in seconds (several GEMM
-tiles and a ragged tail per expert) with every output compared, and at its full size
-with routing/dispatch compared everywhere and the floating outputs on sampled tokens.
+tiles and a ragged tail per expert); mid-size cases whose GEMMs take the 256 x 256 tiles
+the full-size workloads run on (the persistent gated kernel, the staged-epilogue kernel,
+in both weight layouts, routed loads even and skewed); and every workload at its full
+size. Every element is compared in each case: all kept expert output rows, the shared
+expert's output, y, and the routed part of y (y minus the residual and the shared term,
+so that the residual's magnitude does not set the bound on the experts' contribution).
 """
 
 import numpy as np
@@ -106,20 +110,57 @@ def test_forward_small_f32_mlp(kind):
     H.check_outputs(w, inp, h, r, d)
 
 
-def _sample_tokens(T, d, n=24, seed=0):
-    rng = np.random.default_rng(seed)
-    toks = set(range(8)) | set(range(T - 8, T)) | set(rng.integers(0, T, n).tolist())
-    full_drop = np.flatnonzero(d["drops"] == d["slot"].shape[1])
-    toks |= set(full_drop[:4].tolist())
-    # experts with fewer kept rows than one 256-row GEMM tile: the tokens in their first
-    # and last slot (these lone, partly filled tiles are what the GEMM schedule has to
-    # spread over the GPU when routing is skewed)
-    k = d["slot"].shape[1]
-    extra = []
-    for e in np.flatnonzero((d["used"] > 0) & (d["used"] < 256)):
-        extra += [int(d["slot_assign"][e, 0]) // k, int(d["slot_assign"][e, d["used"][e] - 1]) // k]
-    toks |= set(extra[:64])
-    return np.array(sorted(toks))
+def _gemm_large_tiles(w):
+    """Whether each grouped bf16 GEMM launch of the forward (GEMM-1 with the shared expert
+    in the same launch, then GEMM-2) runs on the 256 x 256 tiles. Restates the selection
+    rule of the bf16 GEMM launcher: every problem of the launch has at least 192 rows
+    per group (C for the routed experts, T for the shared one) and the launch has at
+    least 128 tiles of 256 rows by 128 (gated) or 256 output columns."""
+    if w.dtype != "bf16":
+        return None
+    from sparse_mixture_experts_stable_amd import ops
+    C = ops.capacity(w.T, w.k, w.E, w.cf)
+    cdiv = lambda a, b: -(-a // b)
+    gated = w.kind == "swiglu"
+    n1 = w.F if w.kind != "linear" else w.D
+    probs1 = [(C, w.E, n1)] + ([(w.T, 1, w.shared_F)] if w.shared_F else [])
+    bnq1 = 128 if gated else 256
+    t1 = sum(g * cdiv(r, 256) * cdiv(n, bnq1) for r, g, n in probs1)
+    large1 = all(r >= 192 for r, _, _ in probs1) and t1 >= 128
+    if w.kind == "linear":
+        return large1, None
+    probs2 = [(C, w.E, w.D)] + ([(w.T, 1, w.D)] if w.shared_F else [])
+    t2 = sum(g * cdiv(r, 256) * cdiv(n, 256) for r, g, n in probs2)
+    large2 = all(r >= 192 for r, _, _ in probs2) and t2 >= 128
+    return large1, large2
+
+
+# Mid-size bf16 cases whose expert GEMMs take the 256 x 256 tiles (the kernels the
+# full-size workloads and the benchmark run), small enough for the oracle to check every
+# element in seconds.
+MID = {
+    # SwiGLU + shared expert, k = 8: C = 1024, 576 gated GEMM-1 tiles, 288 GEMM-2 tiles
+    "swiglu_shared_k8": WORKLOADS[3].scaled(T=4096, D=512, E=32, F=512, shared_F=512),
+    # few experts, long row groups: C = 2048, 640 gated tiles, 192 GEMM-2 tiles
+    "swiglu_shared_k2": WORKLOADS[3].scaled(T=8192, D=512, E=8, k=2, F=1024, shared_F=512),
+    # GELU with biases (bias + GELU epilogues of the large tiles): C = 2560
+    "gelu_bias": WORKLOADS[2].scaled(T=8192, D=512, E=8, F=1024),
+    # skewed routing (Zipf bias, quarter-grid ties): most experts far below one row tile,
+    # a few full; C = 2048
+    "swiglu_zipf": WORKLOADS[4].scaled(T=16384, D=512, E=16, F=512),
+}
+
+
+@pytest.mark.parametrize("layout", ["in_out", "out_in"])
+@pytest.mark.parametrize("case", sorted(MID))
+def test_forward_mid_size_large_tiles(case, layout):
+    w = MID[case]
+    assert _gemm_large_tiles(w) == (True, True), "case must select the 256 x 256 tiles"
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp, layout=layout)
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.check_outputs(w, inp, h, r, d)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
@@ -129,7 +170,17 @@ def test_forward_full_size(cfg):
     out, _ = H.run_forward(w, inp)
     h = H.host(out)
     r, d = H.check_routing_dispatch(w, inp, h)
-    H.check_outputs(w, inp, h, r, d, tokens=_sample_tokens(w.T, d))
+    H.check_outputs(w, inp, h, r, d)
+
+
+def test_forward_full_size_zipf_pmf_variant():
+    """The drop/tie stress workload with the pmf-as-bias reading of its Zipf bias."""
+    w = WORKLOADS[4].scaled(logits_mode="zipf_pmf_q")
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp)
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.check_outputs(w, inp, h, r, d)
 
 
 # ---------------------------------------------------------------------------------
@@ -154,7 +205,7 @@ def test_forward_out_in_layout_full_size(cfg):
     out, _ = H.run_forward(w, inp, layout="out_in")
     h = H.host(out)
     r, d = H.check_routing_dispatch(w, inp, h)
-    H.check_outputs(w, inp, h, r, d, tokens=_sample_tokens(w.T, d))
+    H.check_outputs(w, inp, h, r, d)
 
 
 def test_out_in_layout_rejections():
@@ -409,6 +460,105 @@ def test_combine_standalone_matches_oracle():
                 o[tt, j] = eo[idx[tt, j], d["slot"][tt, j]]
     want = om.combine(x, sh, o, gate.astype(np.float32), d["kept"], True)
     H.assert_close(y.cpu().numpy(), want, 1e-5, "combine")
+
+
+@pytest.mark.parametrize("residual,shared", [(False, False), (True, True)])
+def test_combine_standalone_bf16(residual, shared):
+    """The bf16 combine on its own: y is the fp32 sum (x, shared, then the gated kept rows
+    in choice order) rounded once to bf16, so it must lie within half a bf16 unit in the
+    last place of the float64 sum, plus the fp32 rounding of that sum."""
+    ops = _ops()
+    rng = np.random.default_rng(7)
+    T, k, E, C, D = 300, 8, 64, 30, 2048
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int64)
+    d = om.dispatch(idx, E, C)
+    gate = rng.random((T, k)).astype(np.float32)
+    gate /= gate.sum(1, keepdims=True)
+    bf = lambda a: om.bf16_round(a).astype(np.float32)
+    eo = bf(rng.standard_normal((E, C, D)) * 0.1)
+    x = bf(rng.standard_normal((T, D)))
+    sh = bf(rng.standard_normal((T, D)) * 0.1)
+    t = lambda a, dt=torch.bfloat16: torch.tensor(a, device="cuda").to(dt)
+    y = ops.combine(t(eo), t(idx, torch.int32), t(d["slot"], torch.int32), t(gate, torch.float32),
+                    residual=t(x) if residual else None, shared_out=t(sh) if shared else None)
+    got = y.float().cpu().numpy().astype(np.float64)
+    o = np.zeros((T, k, D))
+    tt, jj = np.nonzero(d["kept"])
+    o[tt, jj] = eo[idx[tt, jj], d["slot"][tt, jj]]
+    want = om.combine(x, sh if shared else None, o, gate.astype(np.float64), d["kept"], residual)
+    terms = np.abs(o * np.where(d["kept"], gate, 0.0)[:, :, None]).sum(1)
+    terms = terms + (np.abs(x) if residual else 0.0) + (np.abs(sh) if shared else 0.0)
+    bound = 0.5 * H.ulp(got, "bf16") + 16.0 * 2.0 ** -24 * terms
+    err = np.abs(got - want)
+    assert np.all(err <= bound), (float(np.max(err - bound)), int(np.sum(err > bound)))
+    # fully dropped tokens with no other term: exactly zero
+    if not residual and not shared:
+        assert np.all(got[d["drops"] == k] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_router_page_result_contract(dtype):
+    """"Top-k MoE Router with Load Statistics", Examples 1-3, through ops.topk_router
+    (moe_route with its load statistics, then moe_combine on the per-token expert
+    outputs): the page's printed values, selected_experts as int64, every other result
+    in x's dtype on x's device."""
+    import json
+    import os
+    ops = _ops()
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                     "p2_router_examples.json")))["examples"]
+    tol = 1e-6 if dtype == torch.float32 else 4e-3
+    for e in ex:
+        t = lambda a: torch.tensor(a, dtype=torch.float32, device="cuda").to(dtype)
+        got = ops.topk_router(t(e["x"]), t(e["w_router"]), t(e["expert_outputs"]),
+                              t(e["shared_output"]), e["k"])
+        torch.cuda.synchronize()
+        assert got["selected_experts"].dtype == torch.int64
+        assert got["selected_experts"].cpu().tolist() == e["selected_experts"]
+        for key in ("output", "selected_weights", "token_fraction", "probability_mass"):
+            v = got[key]
+            assert v.dtype == dtype and v.device.type == "cuda", key
+            np.testing.assert_allclose(v.float().cpu().numpy(), np.array(e[key], dtype=np.float64),
+                                       rtol=tol, atol=1e-6 if key == "probability_mass" else tol,
+                                       err_msg=key)
+
+
+def test_forward_load_statistics():
+    """moe_forward's token_fraction and probability_mass are count / T and prob_sum / T
+    of the same call."""
+    w = SMALL[3]
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp)
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.assert_close(h["token_fraction"], r["count"] / w.T, 1e-6, "token_fraction")
+    H.assert_close(h["probability_mass"], r["prob_sum"] / w.T, 1e-4, "probability_mass")
+
+
+@pytest.mark.parametrize("D,dt", [(2, torch.float32), (7, torch.bfloat16), (1536, torch.bfloat16),
+                                  (100, torch.float32)])
+def test_combine_any_width(D, dt):
+    """d_model that does not split into 16-byte pieces tiling the block (odd widths,
+    1536 in bf16) runs the one-element-per-thread combine, same order, same result."""
+    ops = _ops()
+    rng = np.random.default_rng(D)
+    T, k, E, C = 130, 3, 5, 60
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int64)
+    d = om.dispatch(idx, E, C)
+    gate = rng.random((T, k)).astype(np.float32)
+    bf = (lambda a: om.bf16_round(a).astype(np.float32)) if dt == torch.bfloat16 else (lambda a: a.astype(np.float32))
+    eo = bf(rng.standard_normal((E, C, D)))
+    x = bf(rng.standard_normal((T, D)))
+    t = lambda a, ty=dt: torch.tensor(a, device="cuda").to(ty)
+    y = ops.combine(t(eo), t(idx, torch.int32), t(d["slot"], torch.int32), t(gate, torch.float32),
+                    residual=t(x))
+    o = np.zeros((T, k, D))
+    tt, jj = np.nonzero(d["kept"])
+    o[tt, jj] = eo[idx[tt, jj], d["slot"][tt, jj]]
+    want = om.combine(x, None, o, gate.astype(np.float64), d["kept"], True)
+    if dt == torch.bfloat16:
+        want = om.bf16_round(want)
+    H.assert_close(y.float().cpu().numpy(), want, 1e-2 if dt == torch.bfloat16 else 1e-5, "y")
 
 
 def test_shared_expert_dense_entry_point():
