@@ -12,11 +12,21 @@ moe_forward followed by moe_backward. The default workload is T=16384 tokens, d_
 2048, 256 SwiGLU experts (intermediate 512) at top-8 plus one shared SwiGLU expert,
 bf16 data with fp32 routing, capacity factor 1.0, forward.
 
-Prints one JSON line: throughput (tokens/s), a roofline entry for the dominant kernel
-(the GEMM launch with the largest time per step), whose duration comes from HIP events
-recorded around that kernel on its own stream over a second timed pass, per-GEMM MFMA
-and per-kernel HBM fractions, and the CPU oracle timed on a bounded token sample of the
-same workload.
+Passes, after W warm-up steps: (1) exactly K steps between two HIP events on the
+launch stream, which give ms_per_step and value (inputs resident in HBM, the same batch
+every step); (2) K steps with an event pair each (the per-step median); (3) K steps with
+HIP events around every kernel on the stream it is launched on (warm per-kernel times);
+(4) K steps, each after a 512 MiB device write that flushes L2 and the MALL, with the
+per-kernel events again (cold per-kernel times). The roofline entry for the dominant
+kernel (the GEMM with the largest time per step), the per-GEMM MFMA fractions and the
+per-kernel HBM fractions come from pass 4; the warm figures of pass 3 sit beside them.
+The CPU oracle is timed last, median of three runs on a bounded token sample.
+
+--cold-only flushes before every step (warm-up included) and runs only pass 4 (and the
+flushed per-step times), so that a profiler's per-kernel averages over the whole
+process are flushed launches; value is then the mean flushed step time.
+
+Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -67,7 +77,12 @@ def parse():
                          "forward, whose persistent gated GEMM runs faster on it; else in_out")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cold-cache pass (per-kernel timing with a 512 MiB device "
-                         "write before every step)")
+                         "write before every step); the warm per-kernel pass then gives the "
+                         "roofline")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="flush before every step, warm-up included, and run only the cold "
+                         "passes (for profiler runs, whose per-kernel averages then cover "
+                         "flushed steps only); value is then the mean flushed step time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MiB (a "
                          "known-size reference for hardware byte counters)")
@@ -126,17 +141,29 @@ def gemm_table(w, kept, backward, router_grad):
     return f
 
 
-def hbm_table(w, kept, backward):
-    """Algorithmic HBM bytes of one launch of the memory-bound kernels: each operand
-    read once and each result written once (kept rows only)."""
+def hbm_table(w, kept, backward, C=0):
+    """Algorithmic HBM bytes of one launch of the memory- and latency-bound kernels: each
+    operand read once and each result written once (kept rows only)."""
     T, D, E, k = w.T, w.D, w.E, w.k
     es = 2 if w.dtype == "bf16" else 4
+    nb = -(-T // 32)            # routing blocks (32 tokens each): per-block partials
+    nc = -(-nb // 16)           # scan chunks (16 routing blocks each)
     b = {}
     # y = r x + Sh + sum_kept g o: kept expert rows, x, Sh, idx/slot/gate; y written
     b["combine"] = es * D * (kept + (T if w.residual else 0) + (T if w.shared_F else 0) + T) \
         + T * k * 12
-    # logits read; idx, gate and the per-block expert partials written
-    b["route"] = T * E * 4 + T * k * 8
+    # logits read; idx and gate written; per-block expert counts and probability sums
+    b["route"] = T * E * 4 + T * k * 8 + nb * E * 8
+    if w.logits_mode == "router":
+        # x and W_r read, fp32 logits written
+        b["router_gemm" if w.dtype == "bf16" else "router_gemm_f32"] = \
+            T * D * es + D * E * es + T * E * 4
+    # per-block partials read, chunk sums written
+    b["chunk_sum"] = nb * E * 8 + nc * E * 8
+    # idx, the block partials before each block and the chunk sums read; slot, kept,
+    # slot_assign, drops and the per-expert totals (count, used, overflow, prob_sum,
+    # aux) written
+    b["assign"] = T * k * 4 + nb * E * 4 + nc * E * 8 + T * k * 5 + E * C * 4 + T * 4 + E * 16
     if backward:
         # dy, kept expert rows, logits, idx/gate/slot read; dgate, dlogits written
         b["dgate_router_bwd"] = 4 * D * (T + kept) + T * E * 4 * 2 + T * k * 16
@@ -168,9 +195,10 @@ def traffic_record(kernel, workload_name, src_hash):
 
 
 def cpu_baseline(w, inp, n_tokens, backward=False, router_grad=False):
-    """The oracle (float64 NumPy) on the first n_tokens tokens of the workload, as a batch
-    of its own (its capacity recomputed for that batch size): the forward, and with
-    ``backward`` the backward after it."""
+    """A callable running the oracle (float64 NumPy) once on the first n_tokens tokens of
+    the workload, as a batch of their own (capacity recomputed for that batch size): the
+    forward, and with ``backward`` the backward after it; it returns the seconds taken
+    (input conversion excluded)."""
     import numpy as np
     import oracle.moe_oracle as om
     from workloads import to_numpy_f32
@@ -187,21 +215,26 @@ def cpu_baseline(w, inp, n_tokens, backward=False, router_grad=False):
     else:
         kw["w_router"] = to_numpy_f32(inp["w_router"])
     dy = to_numpy_f32(inp["dy"][:n_tokens]) if backward else None
-    t0 = time.perf_counter()
-    f = om.forward(x, w.k, w.kind, wts, cf=w.cf, residual=w.residual, shared=shared,
-                   bf16=(w.dtype == "bf16"), **kw)
-    if backward:
-        om.backward(dy, x, w.kind, wts, f["logits"], f["idx"], f["gate"], f["kept"], f["count"],
-                    residual=w.residual, shared=shared,
-                    w_router=kw.get("w_router") if router_grad else None)
-    dt = time.perf_counter() - t0
-    threads = None
+
+    def once():
+        t0 = time.perf_counter()
+        f = om.forward(x, w.k, w.kind, wts, cf=w.cf, residual=w.residual, shared=shared,
+                       bf16=(w.dtype == "bf16"), **kw)
+        if backward:
+            om.backward(dy, x, w.kind, wts, f["logits"], f["idx"], f["gate"], f["kept"],
+                        f["count"], residual=w.residual, shared=shared,
+                        w_router=kw.get("w_router") if router_grad else None)
+        return time.perf_counter() - t0
+
+    return once
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
     except Exception:
-        pass
-    return n_tokens / dt, dt, threads
+        return None
 
 
 def vendor_gemm(steps):
@@ -316,6 +349,12 @@ def main():
     torch.cuda.synchronize()
     kept = int(out["kept"].sum().item())
     stream = torch.cuda.current_stream()
+    # L2 (4 MiB per XCD) and the 256 MiB MALL are flushed by a 512 MiB device write
+    # before every step of the cold passes; the write is outside the library's launches
+    flush_buf = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        flush_buf.fill_(1)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -327,47 +366,69 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
+        if args.cold_only:
+            flush()
         step()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
 
-    # second timed pass: HIP events around every kernel, recorded by the library on the
-    # stream each kernel is launched on
-    ops.profile_enable(True)
-    torch.cuda.synchronize()
-    p0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    prof_ms = (time.perf_counter() - p0) * 1e3 / args.steps
-    ops.profile_enable(False)
-    kern = ops.profile_read()
-
-    # third pass (unless --no-flush): the same per-kernel timing with L2 and the MALL
-    # flushed before every step by a 512 MiB device write outside the library's launches
-    kern_cold = None
-    if not args.no_flush:
-        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        torch.cuda.synchronize()
+    def timed_steps(cold):
+        """Per-step times from HIP events on the launch stream (a flush, if any, runs
+        before the step's first event)."""
+        evs = []
         for _ in range(args.steps):
-            flush_buf.fill_(1)
+            if cold:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    kern_warm = kern_cold = None
+    step_ms_warm = step_ms_cold = None
+    prof_ms = None
+    if not args.cold_only:
+        # the timed pass: exactly K steps between two events, synchronised on both sides
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        step_ms_warm = timed_steps(False)
+        # per-kernel pass: HIP events around every kernel, recorded by the library on
+        # the stream each kernel is launched on
+        ops.profile_enable(True)
+        torch.cuda.synchronize()
+        p0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        prof_ms = (time.perf_counter() - p0) * 1e3 / args.steps
+        ops.profile_enable(False)
+        kern_warm = ops.profile_read()
+    if flush_buf is not None:
+        step_ms_cold = timed_steps(True)
+        for _ in range(args.steps):
+            flush()
             ops.profile_enable(True)
             step()
             ops.profile_enable(False)
         torch.cuda.synchronize()
         kern_cold = ops.profile_read()
         del flush_buf
+    if args.cold_only:
+        ms = sum(step_ms_cold) / len(step_ms_cold)
 
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     flops = gemm_table(w, kept, backward, router_grad)
+    C_ = ops.capacity(w.T, w.k, w.E, w.cf)
 
     def gemm_rows(kd):
         out = {}
@@ -383,7 +444,7 @@ def main():
 
     def hbm_rows(kd):
         out = {}
-        for name, by in hbm_table(w, kept, backward).items():
+        for name, by in hbm_table(w, kept, backward, C_).items():
             if name not in kd:
                 continue
             cnt, tot = kd[name]
@@ -392,50 +453,73 @@ def main():
                          "GBs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
         return out
 
-    gemms = gemm_rows(kern)
-    dom = max(gemms, key=lambda n: gemms[n]["ms_per_step"])
-    dom_ms = kern[dom][1] / kern[dom][0]
-    achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
     src_hash = source_hash(*(("gemm_bf16.hip", "gemm_bf16_tile.h") if w.dtype == "bf16"
                              else ("gemm_f32.hip",)))
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic_record(dom, w.name + ("_w_in_out_in" if out_in else ""), src_hash),
-                "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(dom_ms, 4)}
-    hbm = hbm_rows(kern)
-    roofline_cold = hbm_cold = None
-    if kern_cold is not None and dom in kern_cold:
-        cold_ms = kern_cold[dom][1] / kern_cold[dom][0]
-        cold = flops[dom] / (cold_ms * 1e-3) / 1e12
-        roofline_cold = {"bound": "mfma", "kernel": dom, "achieved": round(cold, 2),
-                         "peak": peak, "unit": "TFLOP/s", "frac": round(cold / peak, 4),
-                         "avg_launch_ms": round(cold_ms, 4),
-                         "caches": "L2 and MALL flushed before every step (512 MiB write)"}
-        hbm_cold = hbm_rows(kern_cold)
 
+    def roofline_of(kd, caches, with_traffic):
+        gemms = gemm_rows(kd)
+        dom = max(gemms, key=lambda n: gemms[n]["ms_per_step"])
+        dom_ms = kd[dom][1] / kd[dom][0]
+        ach = flops[dom] / (dom_ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
+             "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+             "traffic": (traffic_record(dom, w.name + ("_w_in_out_in" if out_in else ""), src_hash)
+                         if with_traffic else None),
+             "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(dom_ms, 4),
+             "launches": kd[dom][0], "caches": caches}
+        return r, gemms
+
+    cold_note = "L2 and MALL flushed before every step (512 MiB device write)"
+    roofline = roofline_warm = None
+    gemms = gemms_warm = hbm = hbm_warm = None
+    if kern_cold is not None:
+        roofline, gemms = roofline_of(kern_cold, cold_note, True)
+        hbm = hbm_rows(kern_cold)
+    if kern_warm is not None:
+        roofline_warm, gemms_warm = roofline_of(kern_warm, "warm: the same input on every step",
+                                                kern_cold is None)
+        hbm_warm = hbm_rows(kern_warm)
+    if roofline is None:
+        roofline, gemms, hbm = roofline_warm, gemms_warm, hbm_warm
+        roofline_warm = gemms_warm = hbm_warm = None
+    kern = kern_cold if kern_cold is not None else kern_warm
     kernels = {k: {"launches_per_step": round(c / args.steps, 2), "avg_ms": round(t / c, 4)}
                for k, (c, t) in kern.items()}
+
+    def med(v):
+        return None if not v else round(float(np.median(v)), 4)
 
     cpu = None
     if not args.no_cpu_baseline:
         if args.cpu_tokens:
             n = min(args.cpu_tokens, w.T)
-            v, dt, threads = cpu_baseline(w, inp, n, backward, router_grad)
+            run = cpu_baseline(w, inp, n, backward, router_grad)
+            dt = run()
         else:
             # grow the sample until one run takes at least half of --cpu-seconds (the
             # oracle's per-token rate rises with batch size, so a single probe misjudges)
             n = min(w.T, 512)
             while True:
-                v, dt, threads = cpu_baseline(w, inp, n, backward, router_grad)
+                run = cpu_baseline(w, inp, n, backward, router_grad)
+                dt = run()
                 if n >= w.T or dt >= 0.5 * args.cpu_seconds:
                     break
                 grow = max(2.0, min(8.0, args.cpu_seconds / max(dt, 1e-3)))
                 n = min(w.T, int(n * grow) // 256 * 256)
+        # median of three runs at the final sample size (one if a run exceeds 30 s)
+        runs = [dt]
+        if dt <= 30.0:
+            runs += [run(), run()]
+        dt = float(np.median(runs))
         what = "forward + backward" if backward else "forward"
-        cpu = {"value": round(v, 2), "unit": "tokens/s", "cores": threads or os.cpu_count(),
-               "kind": "oracle", "seconds": round(dt, 2),
-               "sample": f"oracle {what} (float64 NumPy) on the first {n} tokens of the "
-                         f"workload as a batch of their own"}
+        nblas = blas_threads()
+        affinity = len(os.sched_getaffinity(0))
+        cpu = {"value": round(n / dt, 2), "unit": "tokens/s", "cores": nblas or affinity,
+               "kind": "oracle", "seconds": round(dt, 2), "runs_s": [round(r, 2) for r in runs],
+               "affinity_cores": affinity, "blas_threads": nblas,
+               "sample": f"oracle {what} (float64 NumPy, its matrix products on "
+                         f"{nblas or affinity} BLAS threads) on the first {n} tokens of the "
+                         f"workload as a batch of their own; median of {len(runs)} runs"}
 
     rec = {
         "metric": ("MoE layer fwd tokens/s (E=256,k=8,D=2048) + MFMA % / HBM GB/s of peak"
@@ -461,11 +545,13 @@ def main():
         "roofline": roofline,
         "gemms": gemms,
         "hbm": hbm,
-        "roofline_cold": roofline_cold,
-        "hbm_cold": hbm_cold,
+        "roofline_warm": roofline_warm,
+        "gemms_warm": gemms_warm,
+        "hbm_warm": hbm_warm,
+        "step_ms_median": {"warm": med(step_ms_warm), "cold": med(step_ms_cold)},
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "profiled_ms_per_step": round(prof_ms, 4),
+        "profiled_ms_per_step": None if prof_ms is None else round(prof_ms, 4),
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(rec), flush=True)
