@@ -287,6 +287,23 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
                          void* stream);
 
 /*
+ * moe_forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same launches, same results as moe_forward. The workspace is a 32 MiB
+ * device array inside the library: each GPU the library runs on holds its own copy
+ * until the process ends. Requirements beyond moe_forward's: hidden_cache must be
+ * given when the experts have a hidden layer and C > 0, shared_out when there is a
+ * shared expert (both are then outputs), and moe_forward_workspace_size(a) must not
+ * exceed 32 MiB (the routing partials, about T * E / 4 bytes, plus the shared expert's
+ * hidden activation, T * d_hidden elements); otherwise MOE_ERR_INVALID_ARG or
+ * MOE_ERR_WORKSPACE and nothing is launched. Every call on one GPU uses that GPU's
+ * array: calls that are not ordered on one stream race with each other. No contents
+ * carry over from one call to the next. Allocates nothing, and makes no allocating
+ * library call.
+ */
+moe_status_t moe_forward_noalloc(const moe_forward_args_t* a, void* stream);
+
+/*
  * Backward of the whole layer ("Sparse MoE Layer in NumPy", section 2 moe_backward and
  * trap 7, for single-linear experts; extended by the chain rule through the GELU and
  * SwiGLU expert MLPs of "Module 7" / llm-atlas "Mixture of Experts", Expert), with the

@@ -22,7 +22,7 @@ EXPORTED = [
     "moe_dispatch_workspace_size", "moe_dispatch",
     "moe_expert_mlp_workspace_size", "moe_expert_mlp",
     "moe_combine",
-    "moe_forward_workspace_size", "moe_forward",
+    "moe_forward_workspace_size", "moe_forward", "moe_forward_noalloc",
     "moe_backward_workspace_size", "moe_backward",
     "moe_read_error", "moe_profile_enable", "moe_profile_read",
 ]
@@ -103,6 +103,8 @@ def _declare(L):
     L.moe_forward_workspace_size.argtypes = [P(ForwardArgs)]
     L.moe_forward.restype = i32
     L.moe_forward.argtypes = [P(ForwardArgs), vp, sz, vp]
+    L.moe_forward_noalloc.restype = i32
+    L.moe_forward_noalloc.argtypes = [P(ForwardArgs), vp]
     L.moe_backward_workspace_size.restype = sz
     L.moe_backward_workspace_size.argtypes = [P(BackwardArgs)]
     L.moe_backward.restype = i32

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "gemm_bf16.hip", "gemm_f32.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "gemm_bf16.hip", "gemm_f32.hip", "combine.hip", "noalloc.hip"]
 # MFMA accumulators in arch VGPRs: avoids AGPR copy chains around the MFMA loops
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 NO_VGPR_FORM: set = set()
