@@ -70,7 +70,7 @@ __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
   const char* As = cur;
   const char* Bs = cur + CF::A_BYTES;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < CF::BK / 32; ++ks) {
     bf16x8 bfr[NB][TN];
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
@@ -78,8 +78,8 @@ __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
       for (int j = 0; j < TN; ++j) {
         if constexpr (BKM) {
           const int n = wn * CF::WCOLS + j * 16 + fr;
-          bfr[q][j] = *reinterpret_cast<const bf16x8*>(Bs + q * CF::BQ_BYTES + n * (BK * 2) +
-                                                      16 * ((ks * 4 + fc) ^ fswz(n)));
+          bfr[q][j] = *reinterpret_cast<const bf16x8*>(Bs + q * CF::BQ_BYTES + n * CF::K_RB +
+                                                      16 * ((ks * 4 + fc) ^ fswz<CF::K_RB>(n)));
         } else {
           const int col = wn * CF::WCOLS + j * 16 + bcol;
           const int k0 = ks * 32 + bk;
@@ -95,7 +95,8 @@ __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = arow + i * 16;
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(As + m * (BK * 2) + 16 * ((ks * 4 + fc) ^ fswz(m)));
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(As + m * CF::K_RB +
+                                                         16 * ((ks * 4 + fc) ^ fswz<CF::K_RB>(m)));
 #pragma unroll
       for (int q = 0; q < NB; ++q)
 #pragma unroll
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
+  const int nk = K / CF::BK;
   const int last = nk - 1;
   constexpr int NS = CF::STAGES;
 #pragma unroll
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
 #pragma unroll
       for (int i = 0; i < CF::A_INST; ++i) rows2[i] = tile_a_row<CF>(batch.p[tl2.pi], tl2, wv, lane, i);
     }
-    const int nk = P.K / BK;
+    const int nk = P.K / CF::BK;
     for (int kt = 0; kt < nk; ++kt, ++g) {
       // this thread's loads for step kt have landed; after the barrier everyone's have,
       // and every wave is done with the previous step, whose stage the next request uses

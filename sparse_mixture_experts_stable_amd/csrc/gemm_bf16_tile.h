@@ -2,10 +2,11 @@
 // layouts and their swizzles, the DMA requests that fill one LDS stage, the decoding of
 // a block's tile, and the epilogue.
 //
-// LDS stage layout (one K step of BK = 64):
-//   A (expert rows, k contiguous) is stored [m][k], 128 bytes per row, and read as one
-//   16-byte fragment per lane. Each lane fetches source chunk c ^ f(m), f(m) = m % 8,
-//   so that the lanes of a fragment read hit distinct bank groups.
+// LDS stage layout (one K step of BK = 64 or 32):
+//   A (expert rows, k contiguous) is stored [m][k], 2 BK bytes per row (128 or 64), and
+//   read as one 16-byte fragment per lane. Each lane fetches source chunk c ^ f(m), with
+//   f(m) = m % 8 for 128-byte rows and (m / 4) % 4 for 64-byte rows, so that the lanes
+//   of a fragment read hit distinct bank groups.
 //   B (weights, n contiguous: [k][n] per expert, as stored) is copied unchanged apart
 //   from a per-row XOR of the 16-byte chunk index (hswz); the k-major fragment each MFMA
 //   needs is assembled with two ds_read_b64_tr_b16 transpose reads. Within a 16-lane
@@ -22,17 +23,23 @@
 namespace moe {
 namespace tile {
 
-constexpr int BK = kBf16BK;  // 64
-
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// A rows: chunk c of row m sits at c ^ (m % 8). (Measured on gfx950 with the LDS
-// bank-conflict counter: this pattern reads conflict-free for the 16-row fragment
-// reads, where c ^ ((m ^ m/8) % 8) does not.)
-__device__ __forceinline__ int fswz(int m) { return m & 7; }
+// k-contiguous rows of RB bytes (A, and B in the OUT_IN layout): chunk c of row m sits at
+// c ^ fswz(m). 128-byte rows: m % 8 (measured on gfx950 with the LDS bank-conflict
+// counter: conflict-free for the 16-row fragment reads, where c ^ ((m ^ m/8) % 8) is
+// not). 64-byte rows: (m / 4) % 4, which gives the 16 rows of a fragment read 16
+// distinct 16-byte bank groups (rows m and m + 4 share the byte offset m % 4 * 64 of a
+// 256-byte bank line, and the swizzle separates them).
+template <int RB>
+__device__ __forceinline__ int fswz(int m) {
+  static_assert(RB == 128 || RB == 64, "k-contiguous row of 64 or 32 bf16");
+  if constexpr (RB == 128) return m & 7;
+  return (m >> 2) & 3;
+}
 // B rows: the 16-byte chunk index is XORed with an even value that differs for the four
 // rows one 16-lane group reads together and, in addition, between groups 0 and 1 (rows
 // k and k + 8), so that both 16 and 32 lanes per LDS cycle are conflict free.
@@ -64,9 +71,14 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
 }
 
-template <int BM_, int BNE_, bool GATED_, int WGM_ = 2, int WGN_ = 2, int STAGES_ = 3>
+template <int BM_, int BNE_, bool GATED_, int WGM_ = 2, int WGN_ = 2, int STAGES_ = 3,
+          int BK_ = 64>
 struct TileCfg {
   static constexpr int STAGES = STAGES_;           // LDS ring depth
+  static constexpr int BK = BK_;                   // K per step (64 or 32)
+  static constexpr int K_RB = BK * 2;              // bytes per k-contiguous LDS row
+  static constexpr int K_RPI = 1024 / K_RB;        // such rows per 1 KiB DMA load
+  static constexpr int K_CPR = K_RB / 16;          // 16-byte chunks per such row
   static constexpr int BM = BM_;                 // rows per block
   static constexpr int BNE = BNE_;               // B columns staged per step (all matrices)
   static constexpr bool GATED = GATED_;
@@ -83,13 +95,13 @@ struct TileCfg {
   static constexpr int BQ_BYTES = BK * BNQ * 2;  // one B matrix
   static constexpr int STAGE = A_BYTES + NB * BQ_BYTES;
   static constexpr int LDS = STAGES * STAGE;
-  static constexpr int A_INST = BM / 8 / WAVES;  // 1 KiB DMA loads of A per wave per step
+  static constexpr int A_INST = BM / K_RPI / WAVES;  // 1 KiB DMA loads of A per wave per step
   static constexpr int B_RB = BNQ * 2;           // bytes per B row
   static constexpr int B_RPI = 1024 / B_RB;      // B rows per 1 KiB load
   static constexpr int B_IPQ = BK / B_RPI;       // loads per B matrix per step
   static constexpr int B_INST = NB * B_IPQ / WAVES;  // per wave per step
   static constexpr int LOADS = A_INST + B_INST;  // vector-memory ops per thread per step
-  static_assert(BM % (8 * WAVES) == 0, "A loads split evenly over the waves");
+  static_assert(BM % (K_RPI * WAVES) == 0, "A loads split evenly over the waves");
   static_assert(NB * B_IPQ % WAVES == 0, "B loads split evenly over the waves");
 };
 
@@ -108,8 +120,8 @@ struct DmaSrc {
 template <class CF, bool BKM = false>
 __device__ __forceinline__ void issue_stage(char* __restrict__ dst, const DmaSrc<CF>& S, int kt,
                                             int N, int wv) {
-  const size_t ka = size_t(kt) * BK * 2;
-  const size_t kb = BKM ? ka : size_t(kt) * BK * size_t(N) * 2;
+  const size_t ka = size_t(kt) * CF::BK * 2;
+  const size_t kb = BKM ? ka : size_t(kt) * CF::BK * size_t(N) * 2;
 #pragma unroll
   for (int t = 0; t < CF::A_INST; ++t) {
     const char* g = S.a + ka + S.ao[t];
@@ -169,23 +181,24 @@ __device__ __forceinline__ bool tile_nonempty(const GemmBatch& batch, int lid) {
 }
 
 // The A source row of DMA load i of this lane for tile t: load i of wave wv fills LDS
-// rows (wv*A_INST + i)*8 .. +8, this lane row (lane / 8); rows past M repeat row m0
+// rows (wv*A_INST + i)*K_RPI .. +K_RPI, this lane row (lane / K_CPR); rows past M repeat
+// row m0
 // (never stored); with a row map the row is the gathered token (or slot) row.
 template <class CF>
 __device__ __forceinline__ int tile_a_row(const GemmProblem& P, const TileId& t, int wv, int lane,
                                           int i) {
-  const int row = (wv * CF::A_INST + i) * 8 + (lane >> 3);
+  const int row = (wv * CF::A_INST + i) * CF::K_RPI + lane / CF::K_CPR;
   int r = t.m0 + row;
   if (r >= t.M) r = t.m0;
   return P.row_map ? P.row_map[size_t(t.g) * P.row_map_ld + r] / P.row_div : r;
 }
 
 // DMA sources of tile t from the A rows of tile_a_row. A: this lane's physical chunk
-// p = lane % 8 holds source chunk p ^ f(row). B: load i of wave wv is load
+// p = lane % K_CPR holds source chunk p ^ f(row). B: load i of wave wv is load
 // u = wv*B_INST + i overall: matrix u / B_IPQ, rows (u % B_IPQ) * B_RPI .. +B_RPI;
 // columns past N read column 0 (never stored). BKM (B stored [N][K]): B is staged like
-// A, [n][k] with 128-byte rows and the same chunk swizzle; load u covers the 8 rows
-// (u % B_IPQ) * 8 .. +8 of its matrix, and rows past N read row 0.
+// A, [n][k] with K_RB-byte rows and the same chunk swizzle; load u covers the K_RPI rows
+// (u % B_IPQ) * K_RPI .. +K_RPI of its matrix, and rows past N read row 0.
 template <class CF, bool BKM = false>
 __device__ __forceinline__ void tile_sources_from_rows(const GemmProblem& P, const TileId& t,
                                                        int wv, int lane, const int* rows,
@@ -195,18 +208,18 @@ __device__ __forceinline__ void tile_sources_from_rows(const GemmProblem& P, con
   if constexpr (CF::NB > 1) S.b[CF::NB - 1] = static_cast<const char*>(P.B1) + size_t(t.g) * P.b_gstride * 2;
 #pragma unroll
   for (int i = 0; i < CF::A_INST; ++i) {
-    const int row = (wv * CF::A_INST + i) * 8 + (lane >> 3);
-    S.ao[i] = uint32_t((size_t(rows[i]) * P.lda + 8 * ((lane & 7) ^ fswz(row))) * 2);
+    const int row = (wv * CF::A_INST + i) * CF::K_RPI + lane / CF::K_CPR;
+    S.ao[i] = uint32_t((size_t(rows[i]) * P.lda + 8 * ((lane % CF::K_CPR) ^ fswz<CF::K_RB>(row))) * 2);
   }
   if constexpr (BKM) {
-    static_assert(CF::B_IPQ * 8 == CF::BNQ, "one 1 KiB load per 8 rows of 128 bytes");
+    static_assert(CF::B_IPQ * CF::K_RPI == CF::BNQ, "one 1 KiB load per K_RPI rows");
 #pragma unroll
     for (int i = 0; i < CF::B_INST; ++i) {
       const int u = wv * CF::B_INST + i;
-      const int nl = (u % CF::B_IPQ) * 8 + (lane >> 3);
+      const int nl = (u % CF::B_IPQ) * CF::K_RPI + lane / CF::K_CPR;
       int n = t.n0 + nl;
       if (n >= P.N) n = 0;
-      S.bo[i] = uint32_t((size_t(n) * P.K + 8 * ((lane & 7) ^ fswz(nl))) * 2);
+      S.bo[i] = uint32_t((size_t(n) * P.K + 8 * ((lane % CF::K_CPR) ^ fswz<CF::K_RB>(nl))) * 2);
     }
   } else {
     constexpr int CPR = CF::B_RB / 16;  // chunks per row
