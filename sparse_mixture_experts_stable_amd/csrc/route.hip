@@ -151,6 +151,8 @@ __global__ __launch_bounds__(NT) void route_kernel(const float* __restrict__ log
   __shared__ int s_hist[L * V];
   __shared__ float s_prob[TPR][L * V];
   __shared__ float s_z[TPR];
+  // rows of E fp32 logits start 16-byte aligned when E % 4 == 0 (logits is)
+  const bool vec_rows = V % 4 == 0 && (E & 3) == 0;
   const bool sig = VAR && o.scoring == MOE_SCORE_SIGMOID;
   const bool with_z = VAR && o.with_z;
   const float* bias = VAR ? o.bias : nullptr;
@@ -171,8 +173,20 @@ __global__ __launch_bounds__(NT) void route_kernel(const float* __restrict__ log
     if (t >= T) break;  // uniform across the group
     const float* row = logits + size_t(t) * E + li * V;
     float s[V];
+    if (vec_rows && li * V + V <= E) {
+      // the lane's V logits are in range and 16-byte aligned: V / 4 vector loads
 #pragma unroll
-    for (int i = 0; i < V; ++i) s[i] = (li * V + i < E) ? row[i] : -INFINITY;
+      for (int i = 0; i < V; i += 4) {
+        const f32x4 q = *reinterpret_cast<const f32x4*>(row + i);
+        s[i] = q[0];
+        s[i + 1] = q[1];
+        s[i + 2] = q[2];
+        s[i + 3] = q[3];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) s[i] = (li * V + i < E) ? row[i] : -INFINITY;
+    }
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < V; ++i) mx = fmaxf(mx, s[i]);
