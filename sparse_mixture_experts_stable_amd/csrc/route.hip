@@ -343,11 +343,21 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const int32_t* __restric
   const int b0 = c * kScanRows;
   const int b1 = min(nb, b0 + kScanRows);
   for (int e = threadIdx.x; e < E; e += 256) {
+    // all kScanRows loads of the column in flight at once, then added in block order
+    int cv[kScanRows];
+    float pv[kScanRows];
+#pragma unroll
+    for (int i = 0; i < kScanRows; ++i) {
+      const bool in = b0 + i < b1;
+      cv[i] = in ? cnt_part[size_t(b0 + i) * E + e] : 0;
+      pv[i] = (in && with_prob) ? prob_part[size_t(b0 + i) * E + e] : 0.f;
+    }
     int cs = 0;
     float ps = 0.f;
-    for (int b = b0; b < b1; ++b) {
-      cs += cnt_part[size_t(b) * E + e];
-      if (with_prob) ps += prob_part[size_t(b) * E + e];
+#pragma unroll
+    for (int i = 0; i < kScanRows; ++i) {
+      cs += cv[i];
+      ps += pv[i];
     }
     chunk_cnt[size_t(c) * E + e] = cs;
     if (with_prob) chunk_prob[size_t(c) * E + e] = ps;
