@@ -12,7 +12,8 @@ moe_forward followed by moe_backward. The default workload is T=16384 tokens, d_
 2048, 256 SwiGLU experts (intermediate 512) at top-8 plus one shared SwiGLU expert,
 bf16 data with fp32 routing, capacity factor 1.0, forward.
 
-Passes, after W warm-up steps: (1) exactly K steps between two HIP events on the
+Passes, after a settle phase (untimed steps for at least --settle-s seconds, while the
+GPU's clocks ramp up) and W warm-up steps: (1) exactly K steps between two HIP events on the
 launch stream, which give ms_per_step and value (inputs resident in HBM, the same batch
 every step); (2) K steps with an event pair each (the per-step median); (3) K steps with
 HIP events around every kernel on the stream it is launched on (warm per-kernel times);
@@ -83,6 +84,15 @@ def parse():
                     help="flush before every step, warm-up included, and run only the cold "
                          "passes (for profiler runs, whose per-kernel averages then cover "
                          "flushed steps only); value is then the mean flushed step time")
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="before the warm-up steps, run the step untimed for at least this many "
+                         "seconds: the first ~20 launches of a process run 10-40%% slower while "
+                         "the GPU's clocks ramp up")
+    ap.add_argument("--summarize-trace", default=None, metavar="CSV",
+                    help="instead of running: print per-kernel durations from a rocprofv3 "
+                         "--kernel-trace CSV (kernel_trace.csv), over the last --last dispatches "
+                         "of each kernel name")
+    ap.add_argument("--last", type=int, default=40)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MiB (a "
                          "known-size reference for hardware byte counters)")
@@ -282,8 +292,30 @@ def vendor_gemm(steps):
                       "results": res}), flush=True)
 
 
+def summarize_trace(path, last):
+    """Per-kernel dispatch durations (microseconds) from a rocprofv3 kernel trace: count,
+    average, minimum and maximum over the last `last` dispatches of each kernel name, as a
+    markdown table, with the whole-trace average beside it."""
+    import csv
+    import statistics
+    runs = {}
+    for r in csv.DictReader(open(path)):
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        runs.setdefault(r["Kernel_Name"], []).append(d)
+    print(f"| kernel | dispatches | last {last}: avg us | min us | max us | all: avg us |")
+    print("|---|---|---|---|---|---|")
+    for name, ds in sorted(runs.items(), key=lambda kv: -sum(kv[1][-last:])):
+        tail = ds[-last:]
+        short = name.replace("void ", "").split("(")[0]
+        print(f"| `{short}` | {len(ds)} | {statistics.mean(tail):.1f} | {min(tail):.1f} | "
+              f"{max(tail):.1f} | {statistics.mean(ds):.1f} |")
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.last)
+        return
     if args.vendor_gemm:
         vendor_gemm(args.steps)
         return
@@ -365,6 +397,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # settle: untimed steps until the clocks have ramped up (then the W warm-up steps)
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        if args.cold_only:
+            flush()
+        step()
+        torch.cuda.synchronize()
+        settle_steps += 1
     for _ in range(args.warmup):
         if args.cold_only:
             flush()
@@ -552,6 +593,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "profiled_ms_per_step": None if prof_ms is None else round(prof_ms, 4),
+        "settle_steps": settle_steps,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(rec), flush=True)
