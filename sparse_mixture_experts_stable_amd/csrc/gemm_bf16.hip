@@ -7,10 +7,11 @@
 // LDS tiles from x without a separate gather pass.
 //
 // Data movement. Both operands go from HBM straight into LDS with
-// global_load_lds_dwordx4 (no register staging), through a three-stage ring: the tile
-// for step k+2 is requested while step k is multiplied (ring depth S: step k+S-1), so
-// S-1 steps of MFMA cover the memory latency and one barrier per step publishes the
-// next tile.
+// global_load_lds_dwordx4 (no register staging), through a ring of stages: with S
+// stages the tiles of step k+S-1 are requested while step k is multiplied, so S-1 steps
+// of MFMA cover the memory latency and one barrier per step publishes the next tiles.
+// The persistent kernel splits its ring into per-operand slots so that the weights can
+// be requested two steps ahead (see there).
 //   A (expert rows, k contiguous) is stored [m][k], 128 bytes per row (BK = 64), and
 //   read as one 16-byte fragment per lane. Each lane fetches the source chunk
 //   c ^ (m % 8), so that the lanes of a fragment read hit distinct bank groups.
@@ -25,8 +26,8 @@
 //
 // Tiles: the large tile is 256 rows x 256 staged B columns (SwiGLU: 128 gate + 128 up
 // columns of the same outputs) on 16 waves (4 x 4, four per SIMD, each 64 rows x 64
-// staged columns) with a two-stage ring (128 KiB of LDS): large enough that each byte
-// staged feeds 128 FLOPs. The small tile (128 x 128, 4 waves, three stages) serves
+// staged columns) with a two-stage ring (128 KiB of LDS; 160 KiB in five slots for the
+// persistent form): large enough that each byte staged feeds 128 FLOPs. The small tile (128 x 128, 4 waves, three stages) serves
 // narrow problems. The gated variant holds gate and up accumulators of the same outputs
 // in one lane, so silu(x Wg) * (x Wu) is formed in the epilogue and only the product is
 // written.
@@ -48,62 +49,111 @@ namespace {
 
 using namespace tile;
 
+// B fragment (matrix q, column fragment j, 32-wide k slice ks) of this lane from the B
+// tiles at `Bs` (matrix q at q * BQ_BYTES). BKM: B is staged [n][k] like A, and its
+// fragments are read like A's; otherwise [k][n], read with two transpose reads: within a
+// 16-lane group lane s points at k row 8 (s / 16) + (s % 16) / 4 (+4 for the second read)
+// and column 4 (s % 4) of its 16-column slice.
+template <class CF, bool BKM>
+__device__ __forceinline__ bf16x8 b_frag(const char* Bs, int q, int j, int ks, int wn, int lane) {
+  const int fr = lane & 15, fc = lane >> 4;
+  if constexpr (BKM) {
+    const int n = wn * CF::WCOLS + j * 16 + fr;
+    return *reinterpret_cast<const bf16x8*>(Bs + q * CF::BQ_BYTES + n * CF::K_RB +
+                                            16 * ((ks * 4 + fc) ^ fswz<CF::K_RB>(n)));
+  } else {
+    const int col = wn * CF::WCOLS + j * 16 + 4 * (fr & 3);
+    const int k0 = ks * 32 + 8 * fc + (fr >> 2);
+    const int k1 = k0 + 4;
+    const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k0 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k0)) + 2 * (col & 7)));
+    const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k1 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k1)) + 2 * (col & 7)));
+    return __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// A fragment (row fragment i, k slice ks) of this lane from the A tile at `As`.
+template <class CF>
+__device__ __forceinline__ bf16x8 a_frag(const char* As, int i, int ks, int wm, int lane) {
+  const int m = wm * CF::WROWS + i * 16 + (lane & 15);
+  return *reinterpret_cast<const bf16x8*>(As + m * CF::K_RB + 16 * ((ks * 4 + (lane >> 4)) ^ fswz<CF::K_RB>(m)));
+}
+
+// The MFMAs of one K step on the A tile at `As` and the B tiles at `Bs`. Per 32-wide k
+// slice: AFIRST = false reads the wave's NB x TN B fragments, then per row fragment one A
+// fragment and its NB x TN MFMAs; AFIRST = true reads the TM A fragments, then per B
+// fragment its TM MFMAs, which holds fewer fragment registers (the same reads and MFMAs).
+template <class CF, bool BKM, bool AFIRST = false>
+__device__ __forceinline__ void mma_step(const char* As, const char* Bs, int wm, int wn, int lane,
+                                         f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
+#pragma unroll
+  for (int ks = 0; ks < CF::BK / 32; ++ks) {
+    if constexpr (AFIRST) {
+      bf16x8 af[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = a_frag<CF>(As, i, ks, wm, lane);
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const bf16x8 bf = b_frag<CF, BKM>(Bs, q, j, ks, wn, lane);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            acc[q][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[i], acc[q][i][j], 0, 0, 0);
+        }
+    } else {
+      bf16x8 bfr[NB][TN];
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[q][j] = b_frag<CF, BKM>(Bs, q, j, ks, wn, lane);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const bf16x8 af = a_frag<CF>(As, i, ks, wm, lane);
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[q][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[q][j], af, acc[q][i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // One K step: request step `nxt` into slot `nxt_slot`, then multiply the tiles in slot
 // `cur`. The two slots are distinct, which the restrict qualifiers state; that lets the
 // compiler order the LDS reads of `cur` freely against the DMA writes still in flight.
-// BKM: B is staged [n][k] like A, and its fragments are read like A's.
+
 template <class CF, bool BKM>
 __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
                                                    char* __restrict__ nxt_slot,
                                                    const DmaSrc<CF>& S, int nxt, int N,
                                                    int wv, int wm, int wn, int lane,
-                                                   f32x4 (&acc)[CF::NB][CF::TM][CF::TN],
-                                                   bool issue = true) {
-  constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
-  if (issue) issue_stage<CF, BKM>(nxt_slot, S, nxt, N, wv);
-  const int fr = lane & 15, fc = lane >> 4;
-  const int arow = wm * CF::WROWS + fr;
-  // B transpose-read coordinates of this lane: k row within the 32-wide k step and the
-  // column offset inside a 16-column fragment
-  const int bk = 8 * fc + (fr >> 2);
-  const int bcol = 4 * (fr & 3);
-  const char* As = cur;
-  const char* Bs = cur + CF::A_BYTES;
-#pragma unroll
-  for (int ks = 0; ks < CF::BK / 32; ++ks) {
-    bf16x8 bfr[NB][TN];
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if constexpr (BKM) {
-          const int n = wn * CF::WCOLS + j * 16 + fr;
-          bfr[q][j] = *reinterpret_cast<const bf16x8*>(Bs + q * CF::BQ_BYTES + n * CF::K_RB +
-                                                      16 * ((ks * 4 + fc) ^ fswz<CF::K_RB>(n)));
-        } else {
-          const int col = wn * CF::WCOLS + j * 16 + bcol;
-          const int k0 = ks * 32 + bk;
-          const int k1 = k0 + 4;
-          const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k0 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k0)) + 2 * (col & 7)));
-          const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(Bs + q * CF::BQ_BYTES + k1 * CF::B_RB + 16 * ((col >> 3) ^ hswz<CF::B_RB>(k1)) + 2 * (col & 7)));
-          bfr[q][j] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = arow + i * 16;
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(As + m * CF::K_RB +
-                                                         16 * ((ks * 4 + fc) ^ fswz<CF::K_RB>(m)));
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[q][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[q][j], af, acc[q][i][j], 0, 0, 0);
-    }
-  }
+                                                   f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  issue_stage<CF, BKM>(nxt_slot, S, nxt, N, wv);
+  mma_step<CF, BKM>(cur, cur + CF::A_BYTES, wm, wn, lane, acc);
+}
+
+// The same for the slot ring of the persistent kernel: request the A tile of step `ka`
+// into `dA` (if `ia`) and the B tiles of step `kb` into `dB` (if `ib`), then multiply the
+// A tile at `As` with the B tiles at `Bs`. The four slots are distinct.
+template <class CF, bool BKM>
+__device__ __forceinline__ void step_compute_issue_split(
+    const char* __restrict__ As, const char* __restrict__ Bs, char* __restrict__ dA,
+    char* __restrict__ dB, const DmaSrc<CF>& SA, const DmaSrc<CF>& SB, int ka, int kb, int N,
+    bool ia, bool ib, int wv, int wm, int wn, int lane, f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  if (ia) issue_a<CF>(dA, SA, ka, wv);
+  if (ib) issue_b<CF, BKM>(dB, SB, kb, N, wv);
+  mma_step<CF, BKM, false>(As, Bs, wm, wn, lane, acc);
+}
+
+// Entry q of a block's tile list held in a register: lane j holds entries j (low 16 bits)
+// and 64 + j (high 16 bits).
+__device__ __forceinline__ int list_entry(int l, int q) {
+  const int v = __builtin_amdgcn_readlane(l, q & 63);
+  return q < 64 ? (v & 0xffff) : int(uint32_t(v) >> 16);
 }
 
 }  // namespace
@@ -188,30 +238,45 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
     store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, sbias, acc);
 }
 
-// Persistent form of the two-stage kernel: one block per CU works through a list of
+// LDS of the persistent kernel: five slots of 32 KiB, the whole 160 KiB of a CU.
+constexpr int kSlotBytes = 32768;
+constexpr int kSlots = 5;
+constexpr int kPersistentLds = kSlots * kSlotBytes;
+// Longest tile list a persistent block holds (one register per lane, 16-bit tile ids).
+constexpr int kPersistentListMax = 128;
+
+// Persistent form of the large gated tile: one block per CU works through a list of
 // tiles. XCD x (hardware blocks x, x+8, ...) owns a contiguous range of logical tiles, so
 // the blocks running together on one XCD work on neighbouring tiles, which share weight
 // panels in that XCD's L2. At the start the block ranks the non-empty tiles of its XCD's
-// range in order (a block-wide prefix count) and keeps those of rank bi, bi + nb_x, ...
-// in LDS, so skewed groups (many nearly empty experts) still spread evenly over the
-// XCD's blocks. On the last K step of a tile the DMA request already targets step 0 of
-// the block's next tile, so that tile's first stage streams in while the epilogue of the
-// current one runs; the next tile's gathered row indices are read at the start of the
-// current tile.
+// range in order (a block-wide prefix count) and keeps those of rank bi, bi + nb_x, ...;
+// so skewed groups (many nearly empty experts) still spread evenly over the XCD's blocks.
+// The list then moves to registers, since the operand ring takes the whole LDS.
+//
+// The ring: the A tile (256 gathered rows x 64 k) and the B tiles (gate and up, 64 k x
+// 128 columns each) of one K step take one 32 KiB slot each. The block's steps run on
+// as one stream across its tiles, and the slots are requested in the order B(0), A(0),
+// B(1), A(1), ..., so step s reads slots 2s % 5 (B) and (2s + 1) % 5 (A). While step s
+// is multiplied, A(s + 1) and B(s + 2) are in flight: the weights, which come from HBM,
+// are requested two steps ahead and the gathered x rows, which the router GEMM has just
+// read, one step ahead (three whole 64 KiB stages would not fit). Requests cross into
+// the block's next tile the same way, so its first steps stream in while the epilogue of
+// the current one runs. Every tile has at least two K steps (the host checks).
 template <class CF, int EPI, bool OF32, bool BKM>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(GemmBatch batch) {
-  static_assert(CF::STAGES == 2, "two-stage ring");
+  static_assert(CF::A_BYTES == kSlotBytes && CF::NB * CF::BQ_BYTES == kSlotBytes,
+                "one slot per operand tile");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   constexpr int NB = CF::NB, TM = CF::TM, TN = CF::TN;
   const int nblk = gridDim.x;
   const int x = blockIdx.x & 7, bi = blockIdx.x >> 3;
   const int nb_x = (nblk >> 3) + ((nblk & 7) > x ? 1 : 0);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   int ranked = 0;  // non-empty tiles in XCD x's range
   {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int wv = tid >> 6;
-    int* s_list = reinterpret_cast<int*>(smem + CF::LDS);
+    int* s_list = reinterpret_cast<int*>(smem);
     int* s_wsum = s_list + batch.list_cap;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int j0 = 0;; j0 += CF::THREADS) {
@@ -236,19 +301,26 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
       if (xcd_tile(batch.total, batch.chunk, x, j0 + CF::THREADS) < 0) break;
     }
   }
-  const int* s_list = reinterpret_cast<const int*>(smem + CF::LDS);
   const int nmine = ranked > bi ? (ranked - bi + nb_x - 1) / nb_x : 0;
   if (nmine == 0) return;
-  int qi = 0;  // position in the block's tile list
-  TileId tl = decode_tile<CF>(batch, __builtin_amdgcn_readfirstlane(s_list[0]));
+  int lst;  // entries lane (low half) and 64 + lane (high half); ids below 2^16
+  {
+    const int* s_list = reinterpret_cast<const int*>(smem);
+    const int e0 = lane < nmine ? s_list[lane] : 0;
+    const int e1 = 64 + lane < nmine ? s_list[64 + lane] : 0;
+    lst = e0 | (e1 << 16);
+  }
+  __syncthreads();  // the ring below overwrites the list
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv % CF::WGM, wn = wv / CF::WGM;
+  int qi = 0;  // position in the block's tile list
+  TileId tl = decode_tile<CF>(batch, list_entry(lst, 0));
 
-  DmaSrc<CF> S;
-  tile_sources<CF, BKM>(batch.p[tl.pi], tl, wv, lane, S);
+  DmaSrc<CF> SA, SB;  // sources of the A requests and of the B requests
+  tile_sources<CF, BKM>(batch.p[tl.pi], tl, wv, lane, SA);
+  SB = SA;
+  int nb = batch.p[tl.pi].N;  // N of the problem the B requests read
   f32x4 acc[NB][TM][TN];
 #pragma unroll
   for (int q = 0; q < NB; ++q)
@@ -257,39 +329,71 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue_stage<CF, BKM>(smem, S, 0, batch.p[tl.pi].N, wv);
-  int g = 0;  // steps done by this block: stage g & 1 holds the current one
+  issue_b<CF, BKM>(smem + 0 * kSlotBytes, SB, 0, nb, wv);
+  issue_a<CF>(smem + 1 * kSlotBytes, SA, 0, wv);
+  issue_b<CF, BKM>(smem + 2 * kSlotBytes, SB, 1, nb, wv);
+  int sb = 0, sa = 1;  // slots of the current step's B and A tiles
   while (true) {
     const GemmProblem& P = batch.p[tl.pi];
-    // the block's next tile, and its gathered A rows
     const bool more = qi + 1 < nmine;
+    // The next tile: its decode, and scalar loads of its row count and of the row map
+    // entries of this wave's A rows (its A rows are formed when its first A request is
+    // made). No vector load is outstanding in the loop apart from the DMA: the compiler,
+    // which does not count DMA requests, would wait for all of them before using a loaded
+    // register.
     TileId tl2 = tl;
-    if (more) tl2 = decode_tile<CF>(batch, __builtin_amdgcn_readfirstlane(s_list[qi + 1]));
-    int rows2[CF::A_INST];
+    int m2 = 0;
+    WaveRows<CF> wr2;
     if (more) {
-#pragma unroll
-      for (int i = 0; i < CF::A_INST; ++i) rows2[i] = tile_a_row<CF>(batch.p[tl2.pi], tl2, wv, lane, i);
+      tl2 = decode_tile_id<CF>(batch, list_entry(lst, qi + 1));
+      m2 = group_rows_scalar(batch.p[tl2.pi], tl2);
+      wave_row_entries<CF>(batch.p[tl2.pi], tl2, wv, wr2);
     }
     const int nk = P.K / CF::BK;
-    for (int kt = 0; kt < nk; ++kt, ++g) {
-      // this thread's loads for step kt have landed; after the barrier everyone's have,
-      // and every wave is done with the previous step, whose stage the next request uses
-      wait_vmcnt<0>();
+    for (int kt = 0; kt < nk; ++kt) {
+      // the current step's loads have landed once at most the B loads of the next step
+      // (the newest requests) are outstanding; after the barrier everyone's have, and
+      // every wave is done with the previous step, whose two slots are reused. One wait
+      // count on every step: past the block's last step the B requests repeat that step
+      // (into a free slot, never read), so the count stays exact.
+      wait_vmcnt<CF::B_INST>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      int knext = kt + 1, nN = P.N;
-      bool issue = true;
-      if (knext == nk) {
+      // A one step ahead: the next step of this tile, or the first of the next tile
+      int ka = kt + 1;
+      bool ia = true;
+      if (ka == nk) {
         if (more) {
-          tile_sources_from_rows<CF, BKM>(batch.p[tl2.pi], tl2, wv, lane, rows2, S);
-          knext = 0;
-          nN = batch.p[tl2.pi].N;
+          tl2.M = m2;
+          int rows2[CF::A_INST];
+#pragma unroll
+          for (int i = 0; i < CF::A_INST; ++i) rows2[i] = a_row_from_entries<CF>(batch.p[tl2.pi], tl2, wv, lane, i, wr2);
+          tile_a_sources<CF>(batch.p[tl2.pi], tl2, wv, lane, rows2, SA);
+          ka = 0;
         } else {
-          issue = false;
+          ia = false;
         }
       }
-      step_compute_issue<CF, BKM>(smem + (g & 1) * CF::STAGE, smem + ((g + 1) & 1) * CF::STAGE,
-                                  S, knext, nN, wv, wm, wn, lane, acc, issue);
+      // B two steps ahead (clamped to the last step at the end of the block's tiles)
+      int kb = kt + 2;
+      if (kb >= nk) {
+        if (more) {
+          if (kb == nk) {
+            tile_b_sources<CF, BKM>(batch.p[tl2.pi], tl2, wv, lane, SB);
+            nb = batch.p[tl2.pi].N;
+          }
+          kb -= nk;
+        } else {
+          kb = nk - 1;
+        }
+      }
+      const int da = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;  // (2s + 3) % 5
+      const int db = sb + 4 < kSlots ? sb + 4 : sb + 4 - kSlots;  // (2s + 4) % 5
+      step_compute_issue_split<CF, BKM>(smem + sa * kSlotBytes, smem + sb * kSlotBytes,
+                                        smem + da * kSlotBytes, smem + db * kSlotBytes, SA, SB,
+                                        ka, kb, nb, ia, true, wv, wm, wn, lane, acc);
+      sa = da;
+      sb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;
     }
     store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, nullptr, acc);
     if (!more) break;
@@ -302,6 +406,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
     ++qi;
     tl = tl2;
   }
+  wait_vmcnt<0>();  // the repeated tail requests still target LDS
 }
 
 namespace {
@@ -347,9 +452,6 @@ moe_status_t launch_cfg(GemmBatch& b, const char* name, hipStream_t s) {
   return MOE_OK;
 }
 
-// LDS of a persistent block: the ring plus its tile list (at most 24 KiB of entries)
-constexpr int kPersistentLdsMax = 2 * 65536 + 24576;
-
 int cu_count() {
   static int n = 0;
   if (n == 0) {
@@ -365,21 +467,27 @@ template <class CF, int EPI, bool OF32, bool BKM>
 moe_status_t launch_persistent(GemmBatch& b, const char* name, hipStream_t s) {
   plan_tiles<CF>(b);
   if (b.total == 0) return MOE_OK;
+  const int grid = b.total < cu_count() ? int(b.total) : cu_count();
+  const int nb_min = grid / 8 > 0 ? grid / 8 : 1;  // blocks of the XCD with the fewest
+  b.list_cap = (b.xcd_max + nb_min - 1) / nb_min;
+  // the slot ring needs two K steps per tile; the list lives in two registers per lane
+  bool fits = b.list_cap <= kPersistentListMax && b.total <= 65536 &&
+              sizeof(int) * (size_t(b.list_cap) + CF::WAVES) <= size_t(kPersistentLds);
+  for (int i = 0; i < b.nprob; ++i) {
+    if (b.p[i].K < 2 * CF::BK) fits = false;
+    if (b.p[i].row_map && b.p[i].row_map_ld < CF::A_INST * CF::K_RPI) fits = false;
+  }
+  if (!fits) return launch_cfg<CF, EPI, OF32, BKM>(b, name, s);
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(
             reinterpret_cast<const void*>(gemm_bf16_persistent_kernel<CF, EPI, OF32, BKM>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, kPersistentLdsMax) != hipSuccess)
+            hipFuncAttributeMaxDynamicSharedMemorySize, kPersistentLds) != hipSuccess)
       return MOE_ERR_HIP;
     attr_set = true;
   }
-  const int grid = b.total < cu_count() ? int(b.total) : cu_count();
-  const int nb_min = grid / 8 > 0 ? grid / 8 : 1;  // blocks of the XCD with the fewest
-  b.list_cap = (b.xcd_max + nb_min - 1) / nb_min;
-  const size_t lds = CF::LDS + sizeof(int) * (size_t(b.list_cap) + CF::WAVES);
-  if (lds > size_t(kPersistentLdsMax)) return launch_cfg<CF, EPI, OF32, BKM>(b, name, s);
   MOE_LAUNCH(name, (gemm_bf16_persistent_kernel<CF, EPI, OF32, BKM>), dim3(grid),
-             dim3(CF::THREADS), lds, s, b);
+             dim3(CF::THREADS), kPersistentLds, s, b);
   return MOE_OK;
 }
 

@@ -115,27 +115,40 @@ struct DmaSrc {
   uint32_t bo[CF::B_INST];    // per lane: k row and swizzled chunk
 };
 
-// Requests the tiles of step kt into the LDS stage `dst` (one 1 KiB DMA per instruction).
-// `wv` is the wave index (uniform). BKM: B is stored [N][K] (k contiguous, like A).
-template <class CF, bool BKM = false>
-__device__ __forceinline__ void issue_stage(char* __restrict__ dst, const DmaSrc<CF>& S, int kt,
-                                            int N, int wv) {
+// Requests the A tile of step kt into `dst` (one 1 KiB DMA per instruction). `wv` is
+// the wave index (uniform).
+template <class CF>
+__device__ __forceinline__ void issue_a(char* __restrict__ dst, const DmaSrc<CF>& S, int kt, int wv) {
   const size_t ka = size_t(kt) * CF::BK * 2;
-  const size_t kb = BKM ? ka : size_t(kt) * CF::BK * size_t(N) * 2;
 #pragma unroll
   for (int t = 0; t < CF::A_INST; ++t) {
     const char* g = S.a + ka + S.ao[t];
     __builtin_amdgcn_global_load_lds(g, (lds_void*)(dst + (wv * CF::A_INST + t) * 1024), 16, 0, 0);
   }
+}
+
+// Requests the B tiles of step kt into `dst` (matrix q at q * BQ_BYTES). BKM: B is stored
+// [N][K] (k contiguous, like A).
+template <class CF, bool BKM = false>
+__device__ __forceinline__ void issue_b(char* __restrict__ dst, const DmaSrc<CF>& S, int kt, int N,
+                                        int wv) {
+  const size_t kb = BKM ? size_t(kt) * CF::BK * 2 : size_t(kt) * CF::BK * size_t(N) * 2;
 #pragma unroll
   for (int t = 0; t < CF::B_INST; ++t) {
     const int u = wv * CF::B_INST + t;
     const char* bq = (CF::NB > 1 && u / CF::B_IPQ) ? S.b[CF::NB - 1] : S.b[0];
     const char* g = bq + kb + S.bo[t];
     __builtin_amdgcn_global_load_lds(
-        g, (lds_void*)(dst + CF::A_BYTES + (u / CF::B_IPQ) * CF::BQ_BYTES + (u % CF::B_IPQ) * 1024),
-        16, 0, 0);
+        g, (lds_void*)(dst + (u / CF::B_IPQ) * CF::BQ_BYTES + (u % CF::B_IPQ) * 1024), 16, 0, 0);
   }
+}
+
+// Requests the tiles of step kt into the LDS stage `dst`: A, then B at A_BYTES.
+template <class CF, bool BKM = false>
+__device__ __forceinline__ void issue_stage(char* __restrict__ dst, const DmaSrc<CF>& S, int kt,
+                                            int N, int wv) {
+  issue_a<CF>(dst, S, kt, wv);
+  issue_b<CF, BKM>(dst + CF::A_BYTES, S, kt, N, wv);
 }
 
 // A tile of a grouped batch: problem, group (expert), first row and column, row count.
@@ -144,9 +157,10 @@ struct TileId {
 };
 
 // Decodes logical tile id `lid`: problems in order, then groups, then column tiles, then
-// row tiles (consecutive ids share a weight panel). M is the row count of the group.
+// row tiles (consecutive ids share a weight panel). M (the group's row count) is left at
+// 0: group_rows reads it.
 template <class CF>
-__device__ __forceinline__ TileId decode_tile(const GemmBatch& batch, int lid) {
+__device__ __forceinline__ TileId decode_tile_id(const GemmBatch& batch, int lid) {
   TileId t;
   t.pi = (batch.nprob > 1 && lid >= batch.p[0].tiles) ? 1 : 0;
   const GemmProblem& P = batch.p[t.pi];
@@ -156,10 +170,28 @@ __device__ __forceinline__ TileId decode_tile(const GemmBatch& batch, int lid) {
   rem -= t.g * per_group;
   const int nt = rem / P.m_tiles;
   const int mt = rem - nt * P.m_tiles;
-  // the same value in every lane: keep it (and all tile bookkeeping) in scalar registers
-  t.M = P.m_count ? __builtin_amdgcn_readfirstlane(P.m_count[t.g]) : P.m_const;
+  t.M = 0;
   t.m0 = mt * CF::BM;
   t.n0 = nt * CF::BNQ;
+  return t;
+}
+
+// The row count of tile t's group (a load when the problem has per-group counts).
+__device__ __forceinline__ int group_rows(const GemmProblem& P, const TileId& t) {
+  return P.m_count ? P.m_count[t.g] : P.m_const;
+}
+// The same as a scalar load (t uniform; the counts are only read during the kernel).
+__device__ __forceinline__ int group_rows_scalar(const GemmProblem& P, const TileId& t) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  return P.m_count ? ((cptr)P.m_count)[t.g] : P.m_const;
+}
+
+// decode_tile_id with M. The same value in every lane: keep it (and all tile bookkeeping)
+// in scalar registers.
+template <class CF>
+__device__ __forceinline__ TileId decode_tile(const GemmBatch& batch, int lid) {
+  TileId t = decode_tile_id<CF>(batch, lid);
+  t.M = __builtin_amdgcn_readfirstlane(group_rows(batch.p[t.pi], t));
   return t;
 }
 
@@ -182,8 +214,7 @@ __device__ __forceinline__ bool tile_nonempty(const GemmBatch& batch, int lid) {
 
 // The A source row of DMA load i of this lane for tile t: load i of wave wv fills LDS
 // rows (wv*A_INST + i)*K_RPI .. +K_RPI, this lane row (lane / K_CPR); rows past M repeat
-// row m0
-// (never stored); with a row map the row is the gathered token (or slot) row.
+// row m0 (never stored); with a row map the row is the gathered token (or slot) row.
 template <class CF>
 __device__ __forceinline__ int tile_a_row(const GemmProblem& P, const TileId& t, int wv, int lane,
                                           int i) {
@@ -193,24 +224,69 @@ __device__ __forceinline__ int tile_a_row(const GemmProblem& P, const TileId& t,
   return P.row_map ? P.row_map[size_t(t.g) * P.row_map_ld + r] / P.row_div : r;
 }
 
+// The row map entries of the A rows that wave wv stages for tile t, read with scalar
+// loads (the same for every lane; the map is only read during the kernel): rows
+// m0 + NR*wv .. +NR, NR = A_INST * K_RPI, or the last NR rows of the group's map when
+// that window runs past it (those rows are past M). `first` is the row of e[0]. Without
+// a map nothing is read.
+template <class CF>
+struct WaveRows {
+  static constexpr int NR = CF::A_INST * CF::K_RPI;
+  int e[NR];
+  int first;
+};
+
+template <class CF>
+__device__ __forceinline__ void wave_row_entries(const GemmProblem& P, const TileId& t, int wv,
+                                                 WaveRows<CF>& w) {
+  constexpr int NR = WaveRows<CF>::NR;
+  const int r0 = t.m0 + wv * NR;
+  w.first = r0;
+  if (!P.row_map) return;
+  const int last = P.row_map_ld - NR;  // row_map_ld >= NR (checked on the host)
+  if (r0 > last) w.first = last;
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  const cptr p = (cptr)(P.row_map + size_t(t.g) * P.row_map_ld + w.first);
+#pragma unroll
+  for (int j = 0; j < NR; ++j) w.e[j] = p[j];
+}
+
+// The source row of DMA load i of this lane from those entries: as tile_a_row, except
+// that gathered rows past M read row 0 (never stored either way).
+template <class CF>
+__device__ __forceinline__ int a_row_from_entries(const GemmProblem& P, const TileId& t, int wv,
+                                                  int lane, int i, const WaveRows<CF>& w) {
+  const int r = t.m0 + (wv * CF::A_INST + i) * CF::K_RPI + lane / CF::K_CPR;
+  if (!P.row_map) return r < t.M ? r : t.m0;
+  const int j = r - w.first;  // in [0, NR) for every row below M
+  int e = 0;
+#pragma unroll
+  for (int q = 0; q < WaveRows<CF>::NR; ++q) e = j == q ? w.e[q] : e;
+  return r < t.M ? e / P.row_div : 0;
+}
+
 // DMA sources of tile t from the A rows of tile_a_row. A: this lane's physical chunk
 // p = lane % K_CPR holds source chunk p ^ f(row). B: load i of wave wv is load
 // u = wv*B_INST + i overall: matrix u / B_IPQ, rows (u % B_IPQ) * B_RPI .. +B_RPI;
 // columns past N read column 0 (never stored). BKM (B stored [N][K]): B is staged like
 // A, [n][k] with K_RB-byte rows and the same chunk swizzle; load u covers the K_RPI rows
 // (u % B_IPQ) * K_RPI .. +K_RPI of its matrix, and rows past N read row 0.
-template <class CF, bool BKM = false>
-__device__ __forceinline__ void tile_sources_from_rows(const GemmProblem& P, const TileId& t,
-                                                       int wv, int lane, const int* rows,
-                                                       DmaSrc<CF>& S) {
+template <class CF>
+__device__ __forceinline__ void tile_a_sources(const GemmProblem& P, const TileId& t, int wv, int lane,
+                                               const int* rows, DmaSrc<CF>& S) {
   S.a = static_cast<const char*>(P.A) + size_t(t.g) * P.a_gstride * 2;
-  S.b[0] = static_cast<const char*>(P.B0) + size_t(t.g) * P.b_gstride * 2;
-  if constexpr (CF::NB > 1) S.b[CF::NB - 1] = static_cast<const char*>(P.B1) + size_t(t.g) * P.b_gstride * 2;
 #pragma unroll
   for (int i = 0; i < CF::A_INST; ++i) {
     const int row = (wv * CF::A_INST + i) * CF::K_RPI + lane / CF::K_CPR;
     S.ao[i] = uint32_t((size_t(rows[i]) * P.lda + 8 * ((lane % CF::K_CPR) ^ fswz<CF::K_RB>(row))) * 2);
   }
+}
+
+template <class CF, bool BKM = false>
+__device__ __forceinline__ void tile_b_sources(const GemmProblem& P, const TileId& t, int wv, int lane,
+                                               DmaSrc<CF>& S) {
+  S.b[0] = static_cast<const char*>(P.B0) + size_t(t.g) * P.b_gstride * 2;
+  if constexpr (CF::NB > 1) S.b[CF::NB - 1] = static_cast<const char*>(P.B1) + size_t(t.g) * P.b_gstride * 2;
   if constexpr (BKM) {
     static_assert(CF::B_IPQ * CF::K_RPI == CF::BNQ, "one 1 KiB load per K_RPI rows");
 #pragma unroll
@@ -233,6 +309,14 @@ __device__ __forceinline__ void tile_sources_from_rows(const GemmProblem& P, con
       S.bo[i] = uint32_t((size_t(k) * P.N + col) * 2);
     }
   }
+}
+
+template <class CF, bool BKM = false>
+__device__ __forceinline__ void tile_sources_from_rows(const GemmProblem& P, const TileId& t,
+                                                       int wv, int lane, const int* rows,
+                                                       DmaSrc<CF>& S) {
+  tile_a_sources<CF>(P, t, wv, lane, rows, S);
+  tile_b_sources<CF, BKM>(P, t, wv, lane, S);
 }
 
 template <class CF, bool BKM = false>
