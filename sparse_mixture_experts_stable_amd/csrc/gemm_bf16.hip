@@ -122,17 +122,18 @@ __device__ __forceinline__ void mma_step(const char* As, const char* Bs, int wm,
   }
 }
 
-// One K step: request step `nxt` into slot `nxt_slot`, then multiply the tiles in slot
-// `cur`. The two slots are distinct, which the restrict qualifiers state; that lets the
-// compiler order the LDS reads of `cur` freely against the DMA writes still in flight.
-
+// One K step: request step `nxt` into slot `nxt_slot` (if `issue`), then multiply the
+// tiles in slot `cur`. The two slots are distinct, which the restrict qualifiers state;
+// that lets the compiler order the LDS reads of `cur` freely against the DMA writes still
+// in flight.
 template <class CF, bool BKM>
 __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
                                                    char* __restrict__ nxt_slot,
                                                    const DmaSrc<CF>& S, int nxt, int N,
                                                    int wv, int wm, int wn, int lane,
-                                                   f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
-  issue_stage<CF, BKM>(nxt_slot, S, nxt, N, wv);
+                                                   f32x4 (&acc)[CF::NB][CF::TM][CF::TN],
+                                                   bool issue) {
+  if (issue) issue_stage<CF, BKM>(nxt_slot, S, nxt, N, wv);
   mma_step<CF, BKM>(cur, cur + CF::A_BYTES, wm, wn, lane, acc);
 }
 
@@ -158,18 +159,34 @@ __device__ __forceinline__ int list_entry(int l, int q) {
 
 }  // namespace
 
+// Operand slots: the large tiles (256 x 256, 64-wide K step) keep the A tile and the B
+// tiles of a K step in separate 32 KiB slots, five of them (the whole 160 KiB of a CU),
+// requested in the order B(0), A(0), B(1), A(1), ...: step s reads slots 2s % 5 (B) and
+// (2s + 1) % 5 (A), and while it is multiplied A(s + 1) and B(s + 2) are in flight. The
+// weights, which come from HBM, are thus requested two steps ahead and the A rows one
+// step ahead (three whole 64 KiB stages would not fit).
+constexpr int kSlotBytes = 32768;
+constexpr int kSlots = 5;
+constexpr int kPersistentLds = kSlots * kSlotBytes;
+template <class CF>
+constexpr bool uses_slots() {
+  return CF::STAGES == 2 && CF::A_BYTES == kSlotBytes && CF::NB * CF::BQ_BYTES == kSlotBytes;
+}
+
 // The 16-wave, 256-row tile with a bf16 output leaves through the LDS-staged epilogue.
 template <class CF, bool OF32>
 constexpr bool staged_epilogue() {
   return !OF32 && CF::WAVES == 16 && CF::BM == 256;
 }
-// Dynamic LDS of gemm_bf16_kernel: the ring, plus the block's bias columns (fp32) above
-// it when the staged epilogue, which uses the whole ring, needs a bias.
+// Dynamic LDS of gemm_bf16_kernel: the ring (or the slots), plus the block's bias columns
+// (fp32) above the ring when the staged epilogue, which uses the whole ring, needs a
+// bias (inside the fifth slot, free by then, with slots).
 template <class CF, int EPI, bool OF32>
 constexpr int kernel_lds() {
-  return CF::LDS + (staged_epilogue<CF, OF32>() && (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS)
-                        ? int(sizeof(float)) * CF::BNQ
-                        : 0);
+  constexpr int ring = CF::LDS + (staged_epilogue<CF, OF32>() && (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS)
+                                      ? int(sizeof(float)) * CF::BNQ
+                                      : 0);
+  return uses_slots<CF>() && ring < kPersistentLds ? kPersistentLds : ring;
 }
 
 // EPI: EPI_STORE / EPI_BIAS / EPI_GELU_BIAS / EPI_SWIGLU; OF32: store fp32 instead of bf16;
@@ -205,23 +222,59 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
 
   const int nk = K / CF::BK;
   const int last = nk - 1;
-  constexpr int NS = CF::STAGES;
+  if constexpr (uses_slots<CF>()) {
+    issue_b<CF, BKM>(smem, S, 0, N, wv);
+    issue_a<CF>(smem + kSlotBytes, S, 0, wv);
+    if (last >= 1) issue_b<CF, BKM>(smem + 2 * kSlotBytes, S, 1, N, wv);
+    int sb = 0, sa = 1;  // slots of the current step's B and A tiles
+    for (int kt = 0; kt < nk; ++kt) {
+      // step kt's loads have landed once at most the newest requests (B of step kt + 1,
+      // if there is one) are outstanding; after the barrier everyone's have, and every
+      // wave is done with step kt - 1, whose two slots the requests below reuse. Nothing
+      // is requested past the last step (no vector load is outstanding in this loop apart
+      // from the DMA, so the count depends on the step only).
+      if (kt + 1 <= last)
+        wait_vmcnt<CF::B_INST>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const int da = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;  // (2s + 3) % 5
+      const int db = sb + 4 < kSlots ? sb + 4 : sb + 4 - kSlots;  // (2s + 4) % 5
+      step_compute_issue_split<CF, BKM>(smem + sa * kSlotBytes, smem + sb * kSlotBytes,
+                                        smem + da * kSlotBytes, smem + db * kSlotBytes, S, S,
+                                        kt + 1, kt + 2, N, kt + 1 <= last, kt + 2 <= last, wv, wm,
+                                        wn, lane, acc);
+      sa = da;
+      sb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;
+    }
+  } else {
+    constexpr int NS = CF::STAGES;
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    issue_stage<CF, BKM>(smem + st * CF::STAGE, S, st <= last ? st : last, N, wv);
-  for (int kt = 0; kt < nk; ++kt) {
-    // this thread's loads for step kt have landed (S-2 later steps may still be in
-    // flight); after the barrier everyone's have, and every wave is done with step kt-1,
-    // whose slot the next request reuses
-    wait_vmcnt<CF::LOADS * (NS - 2)>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    const int nxt = kt + NS - 1 <= last ? kt + NS - 1 : last;
-    step_compute_issue<CF, BKM>(smem + (kt % NS) * CF::STAGE,
-                                smem + ((kt + NS - 1) % NS) * CF::STAGE, S, nxt, N, wv, wm, wn,
-                                lane, acc);
+    for (int st = 0; st < NS - 1; ++st)
+      if (st <= last) issue_stage<CF, BKM>(smem + st * CF::STAGE, S, st, N, wv);
+    for (int kt = 0; kt < nk; ++kt) {
+      // this thread's loads for step kt have landed once only those of the later steps
+      // already requested (up to S-2, none past the last step) are outstanding; after
+      // the barrier everyone's have, and every wave is done with step kt-1, whose slot
+      // the next request reuses
+      const int ahead = last - kt < NS - 2 ? last - kt : NS - 2;
+      if (NS > 3 && ahead >= 2)
+        wait_vmcnt<CF::LOADS * 2>();
+      else if (NS > 2 && ahead >= 1)
+        wait_vmcnt<CF::LOADS>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const int nxt = kt + NS - 1;
+      step_compute_issue<CF, BKM>(smem + (kt % NS) * CF::STAGE,
+                                  smem + ((kt + NS - 1) % NS) * CF::STAGE, S, nxt, N, wv, wm, wn,
+                                  lane, acc, nxt <= last);
+    }
   }
-  wait_vmcnt<0>();  // the clamped tail loads still target LDS
+  wait_vmcnt<0>();
   __syncthreads();
 
   constexpr bool STAGED = staged_epilogue<CF, OF32>();
@@ -238,10 +291,6 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
     store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, sbias, acc);
 }
 
-// LDS of the persistent kernel: five slots of 32 KiB, the whole 160 KiB of a CU.
-constexpr int kSlotBytes = 32768;
-constexpr int kSlots = 5;
-constexpr int kPersistentLds = kSlots * kSlotBytes;
 // Longest tile list a persistent block holds (one register per lane, 16-bit tile ids).
 constexpr int kPersistentListMax = 128;
 
@@ -253,15 +302,10 @@ constexpr int kPersistentListMax = 128;
 // so skewed groups (many nearly empty experts) still spread evenly over the XCD's blocks.
 // The list then moves to registers, since the operand ring takes the whole LDS.
 //
-// The ring: the A tile (256 gathered rows x 64 k) and the B tiles (gate and up, 64 k x
-// 128 columns each) of one K step take one 32 KiB slot each. The block's steps run on
-// as one stream across its tiles, and the slots are requested in the order B(0), A(0),
-// B(1), A(1), ..., so step s reads slots 2s % 5 (B) and (2s + 1) % 5 (A). While step s
-// is multiplied, A(s + 1) and B(s + 2) are in flight: the weights, which come from HBM,
-// are requested two steps ahead and the gathered x rows, which the router GEMM has just
-// read, one step ahead (three whole 64 KiB stages would not fit). Requests cross into
-// the block's next tile the same way, so its first steps stream in while the epilogue of
-// the current one runs. Every tile has at least two K steps (the host checks).
+// The operand slots (above): the block's steps run on as one stream across its tiles,
+// so the requests cross into the block's next tile the same way and its first steps
+// stream in while the epilogue of the current one runs. Every tile has at least two K
+// steps (the host checks).
 template <class CF, int EPI, bool OF32, bool BKM>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(GemmBatch batch) {
   static_assert(CF::A_BYTES == kSlotBytes && CF::NB * CF::BQ_BYTES == kSlotBytes,
