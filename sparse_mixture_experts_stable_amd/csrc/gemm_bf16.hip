@@ -137,17 +137,25 @@ __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
   mma_step<CF, BKM>(cur, cur + CF::A_BYTES, wm, wn, lane, acc);
 }
 
-// The same for the slot ring of the persistent kernel: request the A tile of step `ka`
-// into `dA` (if `ia`) and the B tiles of step `kb` into `dB` (if `ib`), then multiply the
-// A tile at `As` with the B tiles at `Bs`. The four slots are distinct.
-template <class CF, bool BKM>
+// The same for the operand slots: request the A tile of step `ka` into `dA` (if `ia`) and
+// the B tiles of step `kb` into `dB` (if `ib`), then multiply the A tile at `As` with the B
+// tiles at `Bs`. The four slots are distinct. STAGE_OUT (plain 256 x 256 tiles of the
+// persistent kernel): on a tile's last step (`last`) the output tile then leaves through
+// the two slots just read. Since all four slots are restrict parameters of this one
+// function, the compiler knows that the epilogue's LDS writes do not touch the slots the
+// requests in flight write to, and does not wait for those requests first.
+template <class CF, bool BKM, bool STAGE_OUT = false>
 __device__ __forceinline__ void step_compute_issue_split(
-    const char* __restrict__ As, const char* __restrict__ Bs, char* __restrict__ dA,
-    char* __restrict__ dB, const DmaSrc<CF>& SA, const DmaSrc<CF>& SB, int ka, int kb, int N,
-    bool ia, bool ib, int wv, int wm, int wn, int lane, f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+    char* __restrict__ As, char* __restrict__ Bs, char* __restrict__ dA, char* __restrict__ dB,
+    const DmaSrc<CF>& SA, const DmaSrc<CF>& SB, int ka, int kb, int N, bool ia, bool ib, int wv,
+    int wm, int wn, int lane, f32x4 (&acc)[CF::NB][CF::TM][CF::TN], bool last = false,
+    const GemmProblem* P = nullptr, const TileId* t = nullptr) {
   if (ia) issue_a<CF>(dA, SA, ka, wv);
   if (ib) issue_b<CF, BKM>(dB, SB, kb, N, wv);
   mma_step<CF, BKM, false>(As, Bs, wm, wn, lane, acc);
+  if constexpr (STAGE_OUT) {
+    if (last) store_tile_staged_2x32k<CF>(*P, *t, wm, wn, wv, lane, Bs, As, acc);
+  }
 }
 
 // Entry q of a block's tile list held in a register: lane j holds entries j (low 16 bits)
@@ -433,13 +441,17 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
       }
       const int da = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;  // (2s + 3) % 5
       const int db = sb + 4 < kSlots ? sb + 4 : sb + 4 - kSlots;  // (2s + 4) % 5
-      step_compute_issue_split<CF, BKM>(smem + sa * kSlotBytes, smem + sb * kSlotBytes,
-                                        smem + da * kSlotBytes, smem + db * kSlotBytes, SA, SB,
-                                        ka, kb, nb, ia, true, wv, wm, wn, lane, acc);
+      // plain bf16 tiles leave through the slots of their last step (staged); gated ones
+      // below, with direct stores
+      static_assert(CF::GATED || (EPI == EPI_STORE && !OF32), "plain bf16 tiles only");
+      step_compute_issue_split<CF, BKM, !CF::GATED>(
+          smem + sa * kSlotBytes, smem + sb * kSlotBytes, smem + da * kSlotBytes,
+          smem + db * kSlotBytes, SA, SB, ka, kb, nb, ia, true, wv, wm, wn, lane, acc,
+          kt == nk - 1, &P, &tl);
       sa = da;
       sb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;
     }
-    store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, nullptr, acc);
+    if constexpr (CF::GATED) store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, nullptr, acc);
     if (!more) break;
 #pragma unroll
     for (int q = 0; q < NB; ++q)
@@ -545,7 +557,9 @@ moe_status_t launch_epi(GemmBatch& b, const char* name, hipStream_t s) {
     return launch_cfg<CF, EPI_STORE, true, false>(b, name, s);
   }
   switch (epi) {
-    case EPI_STORE: return launch_cfg<CF, EPI_STORE, false, BKM>(b, name, s);
+    case EPI_STORE:
+      if constexpr (uses_slots<CF>()) return launch_persistent<CF, EPI_STORE, false, BKM>(b, name, s);
+      return launch_cfg<CF, EPI_STORE, false, BKM>(b, name, s);
     case EPI_BIAS: return launch_cfg<CF, EPI_BIAS, false, BKM>(b, name, s);
     case EPI_GELU_BIAS: return launch_cfg<CF, EPI_GELU_BIAS, false, BKM>(b, name, s);
     default: return MOE_ERR_UNSUPPORTED;

@@ -490,6 +490,68 @@ __device__ __forceinline__ void store_tile_staged(const GemmProblem& P, const Ti
   __syncthreads();  // every wave has read the stage back
 }
 
+// Epilogue of a 256 x 256 bf16 tile (EPI_STORE) through two separate 32 KiB LDS
+// buffers, in two rounds of 128 rows (rows 0-63 of a round in s0, 64-127 in s1): the
+// persistent kernel's last K step frees two operand slots while the next tile's first
+// requests are in flight in the other three. The rows leave as whole-row 16-byte
+// non-temporal stores, as in store_tile_staged. The barriers wait for LDS operations
+// only (the DMA requests in flight are left alone); the asm is also a compiler barrier
+// for memory accesses.
+template <class CF>
+__device__ __forceinline__ void store_tile_staged_2x32k(const GemmProblem& P, const TileId& t, int wm,
+                                                        int wn, int wv, int lane, char* s0, char* s1,
+                                                        const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  constexpr int RB = CF::BNQ * 2;  // bytes per output row
+  constexpr int CPR = RB / 16;     // 16-byte chunks per row
+  constexpr int R = 128;           // rows per round
+  constexpr int LPR = 64 / CPR;    // rows per wave instruction when reading back
+  static_assert(!CF::GATED && RB == 512 && CF::BM == 256 && CF::WROWS == 64 && CF::WAVES == 16,
+                "256 x 256 tile on 16 waves");
+  // the lane's addresses are formed here, not hoisted out of the caller's tile loop
+  // (where they would stay live across the K loop)
+  asm volatile("" : "+v"(lane));
+  const int fr = lane & 15, fc = lane >> 4;
+  char* Cb = static_cast<char*>(P.C);
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    // the K loop (round 0) or the previous round's read-back is done with the buffers
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wm / 2 == rd) {
+#pragma unroll
+      for (int i = 0; i < CF::TM; ++i) {
+        const int ml = (wm & 1) * CF::WROWS + i * 16 + fr;  // row within the round
+        char* sb = ml < 64 ? s0 : s1;
+        const int mr = ml & 63;
+        const int m = t.m0 + rd * R + ml;
+#pragma unroll
+        for (int j = 0; j < CF::TN; ++j) {
+          const int nl = wn * CF::WCOLS + j * 16 + fc * 4;
+          const int n = t.n0 + nl;
+          const bool in = m < t.M && n < P.N;
+          const f32x4 v = acc[0][i][j];
+          const int bc = nl * 2;  // byte column
+          *reinterpret_cast<uint2*>(sb + mr * RB + 16 * ((bc >> 4) ^ (mr & 15)) + (bc & 15)) =
+              in ? make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])) : make_uint2(0u, 0u);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < R / (16 * LPR); ++q) {
+      const int ml = wv * (R / 16) + q * LPR + lane / CPR;  // 16 waves, R/16 rows each
+      const int c = lane % CPR;
+      const char* sb = ml < 64 ? s0 : s1;
+      const int mr = ml & 63;
+      const int m = t.m0 + rd * R + ml;
+      const int n = t.n0 + 8 * c;
+      if (m < t.M && n < P.N)
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4*>(sb + mr * RB + 16 * (c ^ (mr & 15))),
+            reinterpret_cast<u32x4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2));
+    }
+  }
+}
+
 // Stages the bias of the block's BNQ columns in LDS as fp32 (zeros past N or without a
 // bias). The caller synchronises before the epilogue reads it.
 template <class CF>
