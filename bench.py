@@ -76,6 +76,11 @@ def parse():
                          "[E, F, D] (out_in, a torch Linear weight per expert; bf16 forward), "
                          "transposed once before timing. auto: out_in for the bf16 SwiGLU "
                          "forward, whose persistent gated GEMM runs faster on it; else in_out")
+    ap.add_argument("--w-out-layout", choices=["auto", "in_out", "out_in"], default="auto",
+                    help="storage of w_out: [E, F, D] (in_out) or [E, D, F] (out_in, a torch "
+                         "Linear weight per expert; bf16 forward), transposed once before "
+                         "timing. auto: out_in for the bf16 SwiGLU forward (GEMM-2 reads "
+                         "k-contiguous weight tiles); else in_out")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cold-cache pass (per-kernel timing with a 512 MiB device "
                          "write before every step); the warm per-kernel pass then gives the "
@@ -348,23 +353,34 @@ def main():
     layout = args.w_in_layout
     if layout == "auto":
         layout = "out_in" if w.dtype == "bf16" and w.kind == "swiglu" and not backward else "in_out"
-    out_in = layout == "out_in"
+    out_layout = args.w_out_layout
+    if out_layout == "auto":
+        out_layout = "out_in" if w.dtype == "bf16" and w.kind == "swiglu" and not backward else "in_out"
+    out_in, wout_t = layout == "out_in", out_layout == "out_in"
+    tr = lambda t: t.transpose(-1, -2).contiguous()
     ex = {"kind": w.kind}
     for key in ("w_in", "w_up", "w_out", "b_in", "b_out"):
         if key in g:
-            ex[key] = g[key].transpose(1, 2).contiguous() if out_in and key in ("w_in", "w_up") else g[key]
+            t = (out_in and key in ("w_in", "w_up")) or (wout_t and key == "w_out")
+            ex[key] = tr(g[key]) if t else g[key]
     shared = None
     if w.shared_F:
         shared = {"kind": "swiglu", "w_in": g["shared_w_in"][None], "w_up": g["shared_w_up"][None],
                   "w_out": g["shared_w_out"][None]}
         if out_in:
-            shared["w_in"] = shared["w_in"].transpose(1, 2).contiguous()
-            shared["w_up"] = shared["w_up"].transpose(1, 2).contiguous()
+            shared["w_in"], shared["w_up"] = tr(shared["w_in"]), tr(shared["w_up"])
             shared["w_in_layout"] = "out_in"
+        if wout_t:
+            shared["w_out"] = tr(shared["w_out"])
+            shared["w_out_layout"] = "out_in"
     if out_in:
         ex["w_in_layout"] = "out_in"
         for key in ("w_in", "w_up", "shared_w_in", "shared_w_up"):
             g.pop(key, None)  # the transposed copies replace them in device memory
+    if wout_t:
+        ex["w_out_layout"] = "out_in"
+        for key in ("w_out", "shared_w_out"):
+            g.pop(key, None)
     C = ops.capacity(w.T, w.k, w.E, w.cf)
     kw = {"logits": g["logits"]} if "logits" in g else {"w_router": g["w_router"]}
     out = ops.forward(g["x"], ex, k=w.k, capacity=C, shared=shared, use_residual=w.residual, **kw)
@@ -581,7 +597,7 @@ def main():
                    "expert": w.kind, "d_hidden": w.F, "shared_hidden": w.shared_F,
                    "capacity": C, "capacity_factor": w.cf, "kept_assignments": kept,
                    "step": "forward + backward" if backward else "forward",
-                   "router_grad": router_grad, "w_in_layout": layout,
+                   "router_grad": router_grad, "w_in_layout": layout, "w_out_layout": out_layout,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "gemms": gemms,

@@ -50,8 +50,8 @@
  *     bf16 operands are addressed with 32-bit byte offsets from each expert's base, so
  *     x (T rows of ldx), a hidden activation (C rows routed, T rows for the shared
  *     expert, of d_hidden) and one expert's weight matrix must each stay below 4 GiB.
- *     The OUT_IN weight layout needs bf16 experts, the forward, and (moe_forward) the
- *     same layout for the routed and the shared experts. The combine takes any d_model.
+ *     The OUT_IN weight layouts need bf16 experts, the forward, and (moe_forward) the
+ *     same layouts for the routed and the shared experts. The combine takes any d_model.
  *     Anything else returns MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H_
@@ -85,11 +85,12 @@ typedef enum {
                                swiglu_expert); Wg, Wu [E,D,F], Wd [E,F,D], no bias     */
 } moe_expert_kind_t;
 
-/* Storage of w_in and w_up (moe_experts_t.w_in_layout). IN_OUT is [E, in, out] as
-   written above (the einsum form of "Sparse MoE Layer in NumPy" and "Module 7");
-   OUT_IN is [E, out, in], each expert's matrix as a torch Linear stores its weight
-   (llm-atlas "Mixture of Experts", Expert): W1/Wg/Wu [E, F, D], LINEAR W [E, D, D]
-   transposed. The product is the same; OUT_IN is taken by the bf16 forward only. */
+/* Storage of w_in and w_up (moe_experts_t.w_in_layout) and of w_out (w_out_layout).
+   IN_OUT is [E, in, out] as written above (the einsum form of "Sparse MoE Layer in
+   NumPy" and "Module 7"); OUT_IN is [E, out, in], each expert's matrix as a torch
+   Linear stores its weight (llm-atlas "Mixture of Experts", Expert): W1/Wg/Wu
+   [E, F, D], W2/Wd [E, D, F], LINEAR W [E, D, D] transposed. The product is the same;
+   OUT_IN is taken by the bf16 forward only. */
 typedef enum { MOE_LAYOUT_IN_OUT = 0, MOE_LAYOUT_OUT_IN = 1 } moe_layout_t;
 
 /* A set of experts of one kind and dtype. All pointers are device pointers. */
@@ -105,7 +106,9 @@ typedef struct {
   const void* b_in;     /* GELU b1 (may be NULL = no bias), else NULL               */
   const void* b_out;    /* GELU b2 (may be NULL = no bias), else NULL               */
   int32_t w_in_layout;  /* moe_layout_t of w_in and w_up (0, the zero default:
-                           IN_OUT); w_out is always [E, F, D]                       */
+                           IN_OUT)                                                  */
+  int32_t w_out_layout; /* moe_layout_t of w_out (0: IN_OUT, [E, F, D]); ignored for
+                           LINEAR experts, which have no w_out                      */
 } moe_experts_t;
 
 /*

@@ -44,7 +44,7 @@ sz = ctypes.c_size_t
 class Experts(ctypes.Structure):
     _fields_ = [("kind", i32), ("dtype", i32), ("num_experts", i32), ("d_model", i32),
                 ("d_hidden", i32), ("w_in", vp), ("w_up", vp), ("w_out", vp), ("b_in", vp),
-                ("b_out", vp), ("w_in_layout", i32)]
+                ("b_out", vp), ("w_in_layout", i32), ("w_out_layout", i32)]
 
 
 class RouterOpts(ctypes.Structure):

@@ -81,9 +81,13 @@ moe_status_t check_experts(const moe_experts_t* ex) {
   if (ex->kind == MOE_EXPERT_GELU_MLP && !ex->w_out) return MOE_ERR_INVALID_ARG;
   if (ex->w_in_layout != MOE_LAYOUT_IN_OUT && ex->w_in_layout != MOE_LAYOUT_OUT_IN)
     return MOE_ERR_INVALID_ARG;
+  if (ex->w_out_layout != MOE_LAYOUT_IN_OUT && ex->w_out_layout != MOE_LAYOUT_OUT_IN)
+    return MOE_ERR_INVALID_ARG;
   const int q = ex->dtype == MOE_BF16 ? 64 : 16;
   if (ex->d_model % q || ex->d_hidden % q) return MOE_ERR_UNSUPPORTED;
-  if (ex->w_in_layout == MOE_LAYOUT_OUT_IN && ex->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((ex->w_in_layout == MOE_LAYOUT_OUT_IN || ex->w_out_layout == MOE_LAYOUT_OUT_IN) &&
+      ex->dtype != MOE_BF16)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -163,6 +167,7 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
       b.m_tiles_rows = rows;
       b.B0 = ex->w_out;
       b.b_gstride = int64_t(F) * D;
+      b.b_kmajor = ex->w_out_layout == MOE_LAYOUT_OUT_IN;
       b.bias = ex->kind == MOE_EXPERT_GELU_MLP ? ex->b_out : nullptr;
       b.bias_gstride = D;
       b.K = F;
@@ -577,7 +582,8 @@ moe_status_t check_forward(const moe_forward_args_t* a) {
     if (st != MOE_OK) return st;
     if (a->shared.kind != MOE_EXPERT_SWIGLU || a->shared.num_experts != 1 ||
         a->shared.dtype != a->experts.dtype || a->shared.d_model != D ||
-        a->shared.w_in_layout != a->experts.w_in_layout)
+        a->shared.w_in_layout != a->experts.w_in_layout ||
+        a->shared.w_out_layout != a->experts.w_out_layout)
       return MOE_ERR_UNSUPPORTED;
   }
   return MOE_OK;

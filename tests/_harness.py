@@ -44,24 +44,40 @@ def _out_in(t):
     return t.transpose(-1, -2).contiguous()
 
 
+def _layouts(layout):
+    """(w_in / w_up transposed, w_out transposed) for a layout name: "in_out" (the pages'
+    einsum form), "out_in" (w_in / w_up as torch Linear weights), "out_in_wout" (w_out
+    only), "out_in_all" (every weight as a torch Linear weight)."""
+    assert layout in ("in_out", "out_in", "out_in_wout", "out_in_all"), layout
+    return layout in ("out_in", "out_in_all"), layout in ("out_in_wout", "out_in_all")
+
+
 def experts_dict(w, g, layout="in_out"):
+    tin, tout = _layouts(layout)
     ex = {"kind": w.kind}
     for key in ("w_in", "w_up", "w_out", "b_in", "b_out"):
         if key in g:
-            ex[key] = _out_in(g[key]) if layout == "out_in" and key in ("w_in", "w_up") else g[key]
-    if layout == "out_in":
+            t = (tin and key in ("w_in", "w_up")) or (tout and key == "w_out")
+            ex[key] = _out_in(g[key]) if t else g[key]
+    if tin:
         ex["w_in_layout"] = "out_in"
+    if tout:
+        ex["w_out_layout"] = "out_in"
     return ex
 
 
 def shared_dict(w, g, layout="in_out"):
     if not w.shared_F:
         return None
+    tin, tout = _layouts(layout)
     sh = {"kind": "swiglu", "w_in": g["shared_w_in"][None], "w_up": g["shared_w_up"][None],
           "w_out": g["shared_w_out"][None]}
-    if layout == "out_in":
+    if tin:
         sh["w_in"], sh["w_up"] = _out_in(sh["w_in"]), _out_in(sh["w_up"])
         sh["w_in_layout"] = "out_in"
+    if tout:
+        sh["w_out"] = _out_in(sh["w_out"])
+        sh["w_out_layout"] = "out_in"
     return sh
 
 
@@ -77,8 +93,8 @@ def oracle_shared(inp):
 
 
 def run_forward(w, inp, g=None, layout="in_out"):
-    """moe_forward on the workload's inputs; layout "out_in" hands w_in / w_up over
-    transposed ([E, F, D]) with the OUT_IN layout flag (same products)."""
+    """moe_forward on the workload's inputs; the layouts other than "in_out" hand the
+    weights named by _layouts over transposed, with their OUT_IN flags (same products)."""
     from sparse_mixture_experts_stable_amd import ops
     g = g if g is not None else gpu_inputs(inp)
     C = ops.capacity(w.T, w.k, w.E, w.cf)

@@ -183,6 +183,29 @@ def test_weight_layout_validation():
     assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
 
 
+def test_w_out_layout_validation():
+    """w_out_layout: values other than IN_OUT / OUT_IN are invalid; OUT_IN needs bf16
+    experts (forward only) and the shared expert in the same layout."""
+    lib = L.lib()
+    p = ctypes.c_void_p(1 << 21)
+    mk = lambda dt, lay, E=4: L.Experts(
+        kind=L.MOE_EXPERT_SWIGLU, dtype=dt, num_experts=E, d_model=128, d_hidden=128, w_in=p,
+        w_up=p, w_out=p, w_out_layout=lay)
+    outs = {f: p for f in ("topk_idx", "topk_gate", "expert_count", "prob_sum", "aux_loss", "slot",
+                           "kept", "slot_assign", "expert_used", "expert_overflow", "token_drops",
+                           "expert_out", "y")}
+    fwd = lambda ex, sh=L.Experts(): L.ForwardArgs(x=p, ldx=128, T=8, logits=p, experts=ex,
+                                                   shared=sh, k=2, capacity=4, **outs)
+    assert lib.moe_forward(ctypes.byref(fwd(mk(L.MOE_BF16, 3))), p, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(ctypes.byref(fwd(mk(L.MOE_F32, L.MOE_LAYOUT_OUT_IN))), p, 1 << 30,
+                           None) == L.MOE_ERR_UNSUPPORTED
+    mixed = fwd(mk(L.MOE_BF16, L.MOE_LAYOUT_OUT_IN), mk(L.MOE_BF16, L.MOE_LAYOUT_IN_OUT, E=1))
+    assert lib.moe_forward(ctypes.byref(mixed), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    b = L.BackwardArgs(dy=p, x=p, ld=128, T=8, logits=p, experts=mk(L.MOE_F32, L.MOE_LAYOUT_OUT_IN),
+                       k=2, capacity=4)
+    assert lib.moe_backward(ctypes.byref(b), p, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+
+
 def test_bf16_shapes_past_32bit_row_offsets_are_rejected():
     """The bf16 tile loader addresses rows with 32-bit byte offsets from each group's
     base; shapes whose rows start 4 GiB or more from it (x of 2^20 tokens at d_model

@@ -151,7 +151,7 @@ MID = {
 }
 
 
-@pytest.mark.parametrize("layout", ["in_out", "out_in"])
+@pytest.mark.parametrize("layout", ["in_out", "out_in", "out_in_all"])
 @pytest.mark.parametrize("case", sorted(MID))
 def test_forward_mid_size_large_tiles(case, layout):
     w = MID[case]
@@ -184,32 +184,36 @@ def test_forward_full_size_zipf_pmf_variant():
 
 
 # ---------------------------------------------------------------------------------
-# w_in / w_up stored [E, F, D] (the OUT_IN layout): same products, k-contiguous B tiles
+# w_in / w_up stored [E, F, D] and w_out [E, D, F] (the OUT_IN layouts): same products,
+# k-contiguous B tiles
 # ---------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("layout", ["out_in", "out_in_wout", "out_in_all"])
 @pytest.mark.parametrize("case", ["swiglu_shared", "gelu_bias", "bf16_linear", "one_token"])
-def test_forward_out_in_layout_small(case):
+def test_forward_out_in_layout_small(case, layout):
     w = {"swiglu_shared": SMALL[3], "gelu_bias": SMALL[2],
          "bf16_linear": DEGENERATE["bf16_linear"], "one_token": DEGENERATE["one_token"]}[case]
     inp = make_inputs(w)
-    out, _ = H.run_forward(w, inp, layout="out_in")
+    out, _ = H.run_forward(w, inp, layout=layout)
     h = H.host(out)
     r, d = H.check_routing_dispatch(w, inp, h)
     H.check_outputs(w, inp, h, r, d)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_forward_out_in_layout_full_size(cfg):
+@pytest.mark.parametrize("cfg,layout", [(2, "out_in"), (3, "out_in"), (4, "out_in"),
+                                        (2, "out_in_all"), (3, "out_in_all")])
+def test_forward_out_in_layout_full_size(cfg, layout):
     w = WORKLOADS[cfg]
     inp = make_inputs(w)
-    out, _ = H.run_forward(w, inp, layout="out_in")
+    out, _ = H.run_forward(w, inp, layout=layout)
     h = H.host(out)
     r, d = H.check_routing_dispatch(w, inp, h)
     H.check_outputs(w, inp, h, r, d)
 
 
 def test_out_in_layout_rejections():
-    """OUT_IN is bf16-forward only, and the routed and shared experts must agree."""
+    """OUT_IN (w_in / w_up, or w_out) is bf16-forward only, and the routed and shared
+    experts must agree."""
     ops = _ops()
     from sparse_mixture_experts_stable_amd import _lib as L
     w = SMALL[3]
@@ -226,6 +230,18 @@ def test_out_in_layout_rejections():
     with pytest.raises(L.MoeError) as e:
         ops.forward(g32["x"], H.experts_dict(w32, g32, "out_in"), k=w32.k,
                     capacity=ops.capacity(w32.T, w32.k, w32.E, w32.cf), w_router=g32["w_router"])
+    assert e.value.status == L.MOE_ERR_UNSUPPORTED
+    # w_out: the same two rules
+    with pytest.raises(L.MoeError) as e:
+        ops.forward(g["x"], H.experts_dict(w, g, "out_in_all"), k=w.k, capacity=C,
+                    shared=H.shared_dict(w, g, "out_in"), w_router=g["w_router"])
+    assert e.value.status == L.MOE_ERR_UNSUPPORTED
+    w32g = WORKLOADS[1].scaled(T=64)
+    inp32g = make_inputs(w32g)
+    g32g = H.gpu_inputs(inp32g)
+    with pytest.raises(L.MoeError) as e:
+        ops.forward(g32g["x"], H.experts_dict(w32g, g32g, "out_in_wout"), k=w32g.k,
+                    capacity=ops.capacity(w32g.T, w32g.k, w32g.E, w32g.cf), w_router=g32g["w_router"])
     assert e.value.status == L.MOE_ERR_UNSUPPORTED
 
 
