@@ -154,7 +154,7 @@ __device__ __forceinline__ void step_compute_issue_split(
   if (ib) issue_b<CF, BKM>(dB, SB, kb, N, wv);
   mma_step<CF, BKM, false>(As, Bs, wm, wn, lane, acc);
   if constexpr (STAGE_OUT) {
-    if (last) store_tile_staged_2x32k<CF>(*P, *t, wm, wn, wv, lane, Bs, As, acc);
+    if (last) store_tile_wave_staged<CF>(*P, *t, wm, wn, wv, lane, Bs, As, acc);
   }
 }
 
@@ -402,6 +402,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
       wave_row_entries<CF>(batch.p[tl2.pi], tl2, wv, wr2);
     }
     const int nk = P.K / CF::BK;
+    // not peeled (a copy of the step body per iteration kind would exhaust the registers)
+#pragma clang loop unroll(disable)
     for (int kt = 0; kt < nk; ++kt) {
       // the current step's loads have landed once at most the B loads of the next step
       // (the newest requests) are outstanding; after the barrier everyone's have, and

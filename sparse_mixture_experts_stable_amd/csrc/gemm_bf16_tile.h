@@ -490,64 +490,57 @@ __device__ __forceinline__ void store_tile_staged(const GemmProblem& P, const Ti
   __syncthreads();  // every wave has read the stage back
 }
 
-// Epilogue of a 256 x 256 bf16 tile (EPI_STORE) through two separate 32 KiB LDS
-// buffers, in two rounds of 128 rows (rows 0-63 of a round in s0, 64-127 in s1): the
-// persistent kernel's last K step frees two operand slots while the next tile's first
-// requests are in flight in the other three. The rows leave as whole-row 16-byte
-// non-temporal stores, as in store_tile_staged. The barriers wait for LDS operations
-// only (the DMA requests in flight are left alone); the asm is also a compiler barrier
-// for memory accesses.
+// Epilogue of a 256 x 256 bf16 tile (EPI_STORE) of the persistent kernel, through the
+// two 32 KiB slots its last K step read (the other three hold the next tile's first
+// requests). After one block-wide barrier (every wave is done reading those slots) each
+// wave stages its own 64 x 64 sub-tile, 32 rows at a time, in a 4 KiB area of s0 (waves
+// 0-7) or s1 (waves 8-15), and writes it back as whole 128-byte row pieces with 16-byte
+// non-temporal stores. A wave reads back only what it wrote (LDS operations of one wave
+// run in order), so no further barrier is needed; four block-wide rounds were 15 us
+// slower on workload 3's GEMM-2. The barrier waits for LDS operations only (the DMA
+// requests in flight are left alone) and is also a compiler barrier for memory
+// accesses. Staged rows: 128 bytes, 16-byte chunk c of row r at c ^ (r % 8).
 template <class CF>
-__device__ __forceinline__ void store_tile_staged_2x32k(const GemmProblem& P, const TileId& t, int wm,
-                                                        int wn, int wv, int lane, char* s0, char* s1,
-                                                        const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
-  constexpr int RB = CF::BNQ * 2;  // bytes per output row
-  constexpr int CPR = RB / 16;     // 16-byte chunks per row
-  constexpr int R = 128;           // rows per round
-  constexpr int LPR = 64 / CPR;    // rows per wave instruction when reading back
-  static_assert(!CF::GATED && RB == 512 && CF::BM == 256 && CF::WROWS == 64 && CF::WAVES == 16,
-                "256 x 256 tile on 16 waves");
+__device__ __forceinline__ void store_tile_wave_staged(const GemmProblem& P, const TileId& t, int wm,
+                                                       int wn, int wv, int lane, char* s0, char* s1,
+                                                       const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  static_assert(!CF::GATED && CF::WROWS == 64 && CF::WCOLS == 64 && CF::TM == 4 && CF::TN == 4 &&
+                    CF::WAVES == 16,
+                "64 x 64 per wave on 16 waves");
+  constexpr int RB = CF::WCOLS * 2;  // 128 bytes per staged row
   // the lane's addresses are formed here, not hoisted out of the caller's tile loop
-  // (where they would stay live across the K loop)
   asm volatile("" : "+v"(lane));
   const int fr = lane & 15, fc = lane >> 4;
+  char* buf = (wv < 8 ? s0 : s1) + (wv & 7) * 4096;
   char* Cb = static_cast<char*>(P.C);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int rd = 0; rd < 2; ++rd) {
-    // the K loop (round 0) or the previous round's read-back is done with the buffers
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (wm / 2 == rd) {
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int i = 0; i < CF::TM; ++i) {
-        const int ml = (wm & 1) * CF::WROWS + i * 16 + fr;  // row within the round
-        char* sb = ml < 64 ? s0 : s1;
-        const int mr = ml & 63;
-        const int m = t.m0 + rd * R + ml;
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const int i = 2 * h + i2;
+      const int r = i2 * 16 + fr;  // staged row 0..31
+      const int m = t.m0 + wm * CF::WROWS + i * 16 + fr;
 #pragma unroll
-        for (int j = 0; j < CF::TN; ++j) {
-          const int nl = wn * CF::WCOLS + j * 16 + fc * 4;
-          const int n = t.n0 + nl;
-          const bool in = m < t.M && n < P.N;
-          const f32x4 v = acc[0][i][j];
-          const int bc = nl * 2;  // byte column
-          *reinterpret_cast<uint2*>(sb + mr * RB + 16 * ((bc >> 4) ^ (mr & 15)) + (bc & 15)) =
-              in ? make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])) : make_uint2(0u, 0u);
-        }
+      for (int j = 0; j < CF::TN; ++j) {
+        const int bc = (j * 16 + fc * 4) * 2;  // byte column within the 128-byte row
+        const int n = t.n0 + wn * CF::WCOLS + j * 16 + fc * 4;
+        const bool in = m < t.M && n < P.N;
+        const f32x4 v = acc[0][i][j];
+        *reinterpret_cast<uint2*>(buf + r * RB + 16 * ((bc >> 4) ^ (r & 7)) + (bc & 15)) =
+            in ? make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])) : make_uint2(0u, 0u);
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int q = 0; q < R / (16 * LPR); ++q) {
-      const int ml = wv * (R / 16) + q * LPR + lane / CPR;  // 16 waves, R/16 rows each
-      const int c = lane % CPR;
-      const char* sb = ml < 64 ? s0 : s1;
-      const int mr = ml & 63;
-      const int m = t.m0 + rd * R + ml;
-      const int n = t.n0 + 8 * c;
+    for (int q = 0; q < 4; ++q) {
+      const int r = q * 8 + (lane >> 3);  // staged row
+      const int c = lane & 7;             // 16-byte chunk
+      const int m = t.m0 + wm * CF::WROWS + h * 32 + r;
+      const int n = t.n0 + wn * CF::WCOLS + 8 * c;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(buf + r * RB + 16 * (c ^ (r & 7)));
       if (m < t.M && n < P.N)
         __builtin_nontemporal_store(
-            *reinterpret_cast<const u32x4*>(sb + mr * RB + 16 * (c ^ (mr & 15))),
-            reinterpret_cast<u32x4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2));
+            val, reinterpret_cast<u32x4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2));
     }
   }
 }
