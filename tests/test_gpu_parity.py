@@ -163,6 +163,27 @@ def test_forward_mid_size_large_tiles(case, layout):
     H.check_outputs(w, inp, h, r, d)
 
 
+# Large-tile cases whose K is a single 64-wide step in one GEMM: the persistent kernel
+# needs two K steps per tile, so that GEMM runs one block per tile (with the operand
+# slots) instead. d_model 64: GEMM-1 (gated, large tiles); d_hidden 64: GEMM-2.
+ONE_STEP = {
+    "gemm1_k64": (WORKLOADS[3].scaled(T=8192, D=64, E=8, k=2, F=512, shared_F=512), 0),
+    "gemm2_k64": (WORKLOADS[3].scaled(T=8192, D=512, E=8, k=2, F=64, shared_F=64), 1),
+}
+
+
+@pytest.mark.parametrize("layout", ["in_out", "out_in_all"])
+@pytest.mark.parametrize("case", sorted(ONE_STEP))
+def test_forward_large_tiles_single_k_step(case, layout):
+    w, which = ONE_STEP[case]
+    assert _gemm_large_tiles(w)[which], "case must select the 256 x 256 tiles"
+    inp = make_inputs(w)
+    out, _ = H.run_forward(w, inp, layout=layout)
+    h = H.host(out)
+    r, d = H.check_routing_dispatch(w, inp, h)
+    H.check_outputs(w, inp, h, r, d)
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_forward_full_size(cfg):
     w = WORKLOADS[cfg]
