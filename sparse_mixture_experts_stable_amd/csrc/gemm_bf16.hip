@@ -26,11 +26,12 @@
 //
 // Tiles: the large tile is 256 rows x 256 staged B columns (SwiGLU: 128 gate + 128 up
 // columns of the same outputs) on 16 waves (4 x 4, four per SIMD, each 64 rows x 64
-// staged columns) with a two-stage ring (128 KiB of LDS; 160 KiB in five slots for the
-// persistent form): large enough that each byte staged feeds 128 FLOPs. The small tile (128 x 128, 4 waves, three stages) serves
-// narrow problems. The gated variant holds gate and up accumulators of the same outputs
-// in one lane, so silu(x Wg) * (x Wu) is formed in the epilogue and only the product is
-// written.
+// staged columns) with five 32 KiB operand slots (160 KiB of LDS, below): large enough
+// that each byte staged feeds 128 FLOPs. The small tile (128 x 128, three stages) serves
+// narrow problems, on 8 waves (64 x 32 each) for plain products such as the router GEMM
+// (4.5 us faster there than 4 waves of 64 x 64) and on 4 for gated ones. The gated
+// variant holds gate and up accumulators of the same outputs in one lane, so
+// silu(x Wg) * (x Wu) is formed in the epilogue and only the product is written.
 //
 // The MFMA is issued with the B fragment as its first operand, which yields C^T per
 // tile: each lane then holds 4 consecutive output columns of one row, so the epilogue
@@ -578,18 +579,19 @@ moe_status_t launch_layout(GemmBatch& b, bool gated, bool large, const char* nam
                  : launch_cfg<TileCfg<128, 128, true, 2, 2, 3>, EPI_SWIGLU, false, BKM>(b, name, s);
   }
   return large ? launch_epi<TileCfg<256, 256, false, 4, 4, 2>, BKM>(b, name, s)
-               : launch_epi<TileCfg<128, 128, false, 2, 2, 3>, BKM>(b, name, s);
+               : launch_epi<TileCfg<128, 128, false, 2, 4, 3>, BKM>(b, name, s);
 }
 }  // namespace
 
 moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStream_t s) {
-  // Large tiles (256 x 256, 16 waves, two stages) when every problem has enough rows per
-  // group and the grid has at least 128 of them (half the CUs: the large tile's higher
-  // rate per CU outweighs the idle CUs, e.g. 192 tiles with K = 4096 run in 115 us against
-  // 139 us as 640 small tiles); else 128 x 128 tiles. The
-  // gated (SwiGLU) GEMM, with long K loops and small output tiles, runs persistent blocks;
-  // the others (K as short as d_hidden, 128 KiB output tiles) run one block per tile with
-  // the LDS-staged epilogue, whose stores overlap the next block's start.
+  // Large tiles (256 x 256, 16 waves, operand slots) when every problem has enough rows
+  // per group and the grid has at least 128 of them (half the CUs: the large tile's
+  // higher rate per CU outweighs the idle CUs, e.g. 192 tiles with K = 4096 run in 115 us
+  // against 139 us as 640 small tiles); else 128 x 128 tiles. On the large tiles the
+  // gated (SwiGLU) GEMM and the plain one without bias run persistent blocks (skipping
+  // empty tiles, the next tile's first steps requested during the epilogue); with a bias,
+  // one block per tile with the LDS-staged epilogue, whose stores overlap the next
+  // block's start.
   using Large = TileCfg<256, 256, true, 4, 4, 2>;
   bool large = true;
   long tiles = 0;
