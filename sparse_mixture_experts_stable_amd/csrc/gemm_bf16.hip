@@ -7,11 +7,11 @@
 // LDS tiles from x without a separate gather pass.
 //
 // Data movement. Both operands go from HBM straight into LDS with
-// global_load_lds_dwordx4 (no register staging), through a ring of stages: with S
-// stages the tiles of step k+S-1 are requested while step k is multiplied, so S-1 steps
-// of MFMA cover the memory latency and one barrier per step publishes the next tiles.
-// The persistent kernel splits its ring into per-operand slots so that the weights can
-// be requested two steps ahead (see there).
+// global_load_lds_dwordx4 (no register staging), with one barrier per K step to publish
+// the next tiles. The small tile uses a ring of S stages: the tiles of step k+S-1 are
+// requested while step k is multiplied, so S-1 steps of MFMA cover the memory latency.
+// The large tile keeps its A and B tiles in separate operand slots so that the weights
+// can be requested two steps ahead (see kSlotBytes).
 //   A (expert rows, k contiguous) is stored [m][k], 128 bytes per row (BK = 64), and
 //   read as one 16-byte fragment per lane. Each lane fetches the source chunk
 //   c ^ (m % 8), so that the lanes of a fragment read hit distinct bank groups.
@@ -38,9 +38,10 @@
 // stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.
 //
 // Block scheduling: the hardware deals workgroups to the 8 XCDs round-robin; the
-// kernel remaps the hardware id so that each XCD works through a contiguous range of
+// kernels remap the hardware id so that each XCD works through a contiguous range of
 // tiles. Consecutive tiles belong to the same expert, so the tiles of one expert share
-// their weight panels in one XCD's L2.
+// their weight panels in one XCD's L2. The persistent kernel runs one block per CU over
+// the non-empty tiles of its XCD's range.
 
 #include "gemm_bf16_tile.h"
 
@@ -303,8 +304,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
 // Longest tile list a persistent block holds (one register per lane, 16-bit tile ids).
 constexpr int kPersistentListMax = 128;
 
-// Persistent form of the large gated tile: one block per CU works through a list of
-// tiles. XCD x (hardware blocks x, x+8, ...) owns a contiguous range of logical tiles, so
+// Persistent form of the large tile (gated, or plain without bias): one block per CU
+// works through a list of tiles. XCD x (hardware blocks x, x+8, ...) owns a contiguous range of logical tiles, so
 // the blocks running together on one XCD work on neighbouring tiles, which share weight
 // panels in that XCD's L2. At the start the block ranks the non-empty tiles of its XCD's
 // range in order (a block-wide prefix count) and keeps those of rank bi, bi + nb_x, ...;
@@ -313,8 +314,9 @@ constexpr int kPersistentListMax = 128;
 //
 // The operand slots (above): the block's steps run on as one stream across its tiles,
 // so the requests cross into the block's next tile the same way and its first steps
-// stream in while the epilogue of the current one runs. Every tile has at least two K
-// steps (the host checks).
+// stream in while the epilogue of the current one runs (gated tiles: direct stores;
+// plain tiles: staged in the two slots the last step read). Every tile has at least two
+// K steps (the host checks).
 template <class CF, int EPI, bool OF32, bool BKM>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(GemmBatch batch) {
   static_assert(CF::A_BYTES == kSlotBytes && CF::NB * CF::BQ_BYTES == kSlotBytes,
