@@ -35,7 +35,8 @@
 //
 // The MFMA is issued with the B fragment as its first operand, which yields C^T per
 // tile: each lane then holds 4 consecutive output columns of one row, so the epilogue
-// stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.
+// stores 8 (bf16) or 16 (fp32) contiguous bytes per lane; the persistent kernel first
+// pairs those pieces across lanes into 16-byte chunks (store_tile_swapped).
 //
 // Block scheduling: the hardware deals workgroups to the 8 XCDs round-robin; the
 // kernels remap the hardware id so that each XCD works through a contiguous range of
@@ -141,23 +142,16 @@ __device__ __forceinline__ void step_compute_issue(const char* __restrict__ cur,
 
 // The same for the operand slots: request the A tile of step `ka` into `dA` (if `ia`) and
 // the B tiles of step `kb` into `dB` (if `ib`), then multiply the A tile at `As` with the B
-// tiles at `Bs`. The four slots are distinct. STAGE_OUT (plain 256 x 256 tiles of the
-// persistent kernel): on a tile's last step (`last`) the output tile then leaves through
-// the two slots just read. Since all four slots are restrict parameters of this one
-// function, the compiler knows that the epilogue's LDS writes do not touch the slots the
-// requests in flight write to, and does not wait for those requests first.
-template <class CF, bool BKM, bool STAGE_OUT = false>
+// tiles at `Bs`. The four slots are distinct (restrict: the compiler need not wait for the
+// requests before the fragment reads).
+template <class CF, bool BKM>
 __device__ __forceinline__ void step_compute_issue_split(
     char* __restrict__ As, char* __restrict__ Bs, char* __restrict__ dA, char* __restrict__ dB,
     const DmaSrc<CF>& SA, const DmaSrc<CF>& SB, int ka, int kb, int N, bool ia, bool ib, int wv,
-    int wm, int wn, int lane, f32x4 (&acc)[CF::NB][CF::TM][CF::TN], bool last = false,
-    const GemmProblem* P = nullptr, const TileId* t = nullptr) {
+    int wm, int wn, int lane, f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
   if (ia) issue_a<CF>(dA, SA, ka, wv);
   if (ib) issue_b<CF, BKM>(dB, SB, kb, N, wv);
   mma_step<CF, BKM, false>(As, Bs, wm, wn, lane, acc);
-  if constexpr (STAGE_OUT) {
-    if (last) store_tile_wave_staged<CF>(*P, *t, wm, wn, wv, lane, Bs, As, acc);
-  }
 }
 
 // Entry q of a block's tile list held in a register: lane j holds entries j (low 16 bits)
@@ -314,8 +308,9 @@ constexpr int kPersistentListMax = 128;
 //
 // The operand slots (above): the block's steps run on as one stream across its tiles,
 // so the requests cross into the block's next tile the same way and its first steps
-// stream in while the epilogue of the current one runs (gated tiles: direct stores;
-// plain tiles: staged in the two slots the last step read). Every tile has at least two
+// stream in while the epilogue of the current one runs. The epilogue needs no LDS and
+// no barrier: lanes pair their pieces into 16-byte chunks and store them from registers
+// (store_tile_swapped; 128-byte rows for the plain tile). Every tile has at least two
 // K steps (the host checks).
 template <class CF, int EPI, bool OF32, bool BKM>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(GemmBatch batch) {
@@ -446,17 +441,15 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
       }
       const int da = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;  // (2s + 3) % 5
       const int db = sb + 4 < kSlots ? sb + 4 : sb + 4 - kSlots;  // (2s + 4) % 5
-      // plain bf16 tiles leave through the slots of their last step (staged); gated ones
-      // below, with direct stores
-      static_assert(CF::GATED || (EPI == EPI_STORE && !OF32), "plain bf16 tiles only");
-      step_compute_issue_split<CF, BKM, !CF::GATED>(
-          smem + sa * kSlotBytes, smem + sb * kSlotBytes, smem + da * kSlotBytes,
-          smem + db * kSlotBytes, SA, SB, ka, kb, nb, ia, true, wv, wm, wn, lane, acc,
-          kt == nk - 1, &P, &tl);
+      step_compute_issue_split<CF, BKM>(smem + sa * kSlotBytes, smem + sb * kSlotBytes,
+                                        smem + da * kSlotBytes, smem + db * kSlotBytes, SA, SB,
+                                        ka, kb, nb, ia, true, wv, wm, wn, lane, acc);
       sa = da;
       sb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;
     }
-    if constexpr (CF::GATED) store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, nullptr, acc);
+    // straight from registers, no LDS: the next tile's first requests are in flight
+    static_assert((EPI == EPI_SWIGLU || EPI == EPI_STORE) && !OF32, "bf16 SwiGLU or plain tiles");
+    store_tile_swapped<CF, EPI, !CF::GATED>(P, tl, wm, wn, lane, acc);
     if (!more) break;
 #pragma unroll
     for (int q = 0; q < NB; ++q)

@@ -490,57 +490,75 @@ __device__ __forceinline__ void store_tile_staged(const GemmProblem& P, const Ti
   __syncthreads();  // every wave has read the stage back
 }
 
-// Epilogue of a 256 x 256 bf16 tile (EPI_STORE) of the persistent kernel, through the
-// two 32 KiB slots its last K step read (the other three hold the next tile's first
-// requests). After one block-wide barrier (every wave is done reading those slots) each
-// wave stages its own 64 x 64 sub-tile, 32 rows at a time, in a 4 KiB area of s0 (waves
-// 0-7) or s1 (waves 8-15), and writes it back as whole 128-byte row pieces with 16-byte
-// non-temporal stores. A wave reads back only what it wrote (LDS operations of one wave
-// run in order), so no further barrier is needed; four block-wide rounds were 15 us
-// slower on workload 3's GEMM-2. The barrier waits for LDS operations only (the DMA
-// requests in flight are left alone) and is also a compiler barrier for memory
-// accesses. Staged rows: 128 bytes, 16-byte chunk c of row r at c ^ (r % 8).
-template <class CF>
-__device__ __forceinline__ void store_tile_wave_staged(const GemmProblem& P, const TileId& t, int wm,
-                                                       int wn, int wv, int lane, char* s0, char* s1,
-                                                       const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
-  static_assert(!CF::GATED && CF::WROWS == 64 && CF::WCOLS == 64 && CF::TM == 4 && CF::TN == 4 &&
-                    CF::WAVES == 16,
-                "64 x 64 per wave on 16 waves");
-  constexpr int RB = CF::WCOLS * 2;  // 128 bytes per staged row
+// Epilogue of a bf16 tile without LDS: EPI_STORE (plain) or EPI_SWIGLU (gated) outputs,
+// 16-byte stores straight from registers. After the MFMAs lane (r, g) (r = lane % 16,
+// g = lane / 16) holds columns 16 j + 4 g .. + 3 of row r of every 16 x 16 tile j. For a
+// pair of tiles j0 = 2 p, j1 = j0 + 1 one v_permlane16_swap per dword exchanges the odd
+// 16-lane groups' j0 pieces with the even groups' j1 pieces, after which lane (r, g) holds
+// the 8 consecutive columns 16 (j0 + g % 2) + 8 (g / 2) .. + 7 of row r: one 16-byte
+// chunk per pair. With two pairs (64 columns per wave) lanes r and r + 8 then trade one
+// chunk (a DPP rotation by 8 within each 16-lane row), so that each store instruction
+// covers 8 whole 128-byte rows rather than 16 half rows. Every lane takes part in the
+// exchanges (they read other lanes); stores past M or N are skipped. NT: non-temporal
+// stores (an output read once, later, by a streaming kernel).
+template <class CF, int EPI, bool NT>
+__device__ __forceinline__ void store_tile_swapped(const GemmProblem& P, const TileId& t, int wm,
+                                                   int wn, int lane,
+                                                   const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  static_assert(CF::TN == 2 || CF::TN == 4, "one or two pairs of tiles");
+  static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU, "no bias in this epilogue");
+  constexpr int NP = CF::TN / 2;
   // the lane's addresses are formed here, not hoisted out of the caller's tile loop
   asm volatile("" : "+v"(lane));
   const int fr = lane & 15, fc = lane >> 4;
-  char* buf = (wv < 8 ? s0 : s1) + (wv & 7) * 4096;
+  const bool lo = fr < 8;
   char* Cb = static_cast<char*>(P.C);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int n = t.n0 + wn * CF::WCOLS + 8 * (fc >> 1) + 16 * (fc & 1) + (NP == 2 && !lo ? 32 : 0);
+  auto put = [&](int m, const u32x4& val) {
+    if (m < t.M && n < P.N) {
+      u32x4* dst = reinterpret_cast<u32x4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2);
+      if constexpr (NT)
+        __builtin_nontemporal_store(val, dst);
+      else
+        *dst = val;
+    }
+  };
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int i = 0; i < CF::TM; ++i) {
+    u32x4 ch[NP];
 #pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2) {
-      const int i = 2 * h + i2;
-      const int r = i2 * 16 + fr;  // staged row 0..31
-      const int m = t.m0 + wm * CF::WROWS + i * 16 + fr;
+    for (int p = 0; p < NP; ++p) {
+      uint32_t w[2][2];
 #pragma unroll
-      for (int j = 0; j < CF::TN; ++j) {
-        const int bc = (j * 16 + fc * 4) * 2;  // byte column within the 128-byte row
-        const int n = t.n0 + wn * CF::WCOLS + j * 16 + fc * 4;
-        const bool in = m < t.M && n < P.N;
-        const f32x4 v = acc[0][i][j];
-        *reinterpret_cast<uint2*>(buf + r * RB + 16 * ((bc >> 4) ^ (r & 7)) + (bc & 15)) =
-            in ? make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])) : make_uint2(0u, 0u);
+      for (int h = 0; h < 2; ++h) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[0][i][2 * p + h][r];
+          if constexpr (EPI == EPI_SWIGLU) v[r] = silu(v[r]) * acc[CF::NB - 1][i][2 * p + h][r];
+        }
+        w[h][0] = pack_bf16x2(v[0], v[1]);
+        w[h][1] = pack_bf16x2(v[2], v[3]);
+      }
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(w[0][d], w[1][d], false, false);
+        ch[p][d] = sw[0];      // columns + 0..3 of the lane's chunk
+        ch[p][2 + d] = sw[1];  // columns + 4..7
       }
     }
+    const int m = t.m0 + wm * CF::WROWS + i * 16;
+    if constexpr (NP == 1) {
+      put(m + fr, ch[0]);
+    } else {
+      // lane r < 8 keeps its first chunk (row r) and sends its second (row r) to lane
+      // r + 8; lane r + 8 keeps its second (row r + 8) and sends its first to lane r
+      u32x4 got;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = q * 8 + (lane >> 3);  // staged row
-      const int c = lane & 7;             // 16-byte chunk
-      const int m = t.m0 + wm * CF::WROWS + h * 32 + r;
-      const int n = t.n0 + wn * CF::WCOLS + 8 * c;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(buf + r * RB + 16 * (c ^ (r & 7)));
-      if (m < t.M && n < P.N)
-        __builtin_nontemporal_store(
-            val, reinterpret_cast<u32x4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2));
+      for (int d = 0; d < 4; ++d)
+        got[d] = uint32_t(__builtin_amdgcn_update_dpp(0, int(lo ? ch[1][d] : ch[0][d]), 0x128, 0xF, 0xF, false));
+      put(m + (fr & 7), lo ? ch[0] : got);
+      put(m + 8 + (fr & 7), lo ? got : ch[1]);
     }
   }
 }
