@@ -177,20 +177,10 @@ constexpr bool uses_slots() {
   return CF::STAGES == 2 && CF::A_BYTES == kSlotBytes && CF::NB * CF::BQ_BYTES == kSlotBytes;
 }
 
-// The 16-wave, 256-row tile with a bf16 output leaves through the LDS-staged epilogue.
-template <class CF, bool OF32>
-constexpr bool staged_epilogue() {
-  return !OF32 && CF::WAVES == 16 && CF::BM == 256;
-}
-// Dynamic LDS of gemm_bf16_kernel: the ring (or the slots), plus the block's bias columns
-// (fp32) above the ring when the staged epilogue, which uses the whole ring, needs a
-// bias (inside the fifth slot, free by then, with slots).
+// Dynamic LDS of gemm_bf16_kernel: the ring, or the five operand slots.
 template <class CF, int EPI, bool OF32>
 constexpr int kernel_lds() {
-  constexpr int ring = CF::LDS + (staged_epilogue<CF, OF32>() && (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS)
-                                      ? int(sizeof(float)) * CF::BNQ
-                                      : 0);
-  return uses_slots<CF>() && ring < kPersistentLds ? kPersistentLds : ring;
+  return uses_slots<CF>() ? kPersistentLds : CF::LDS;
 }
 
 // EPI: EPI_STORE / EPI_BIAS / EPI_GELU_BIAS / EPI_SWIGLU; OF32: store fp32 instead of bf16;
@@ -281,16 +271,17 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
   wait_vmcnt<0>();
   __syncthreads();
 
-  constexpr bool STAGED = staged_epilogue<CF, OF32>();
   // bias of this block's columns, staged once in LDS (in the ring, free after the main
-  // loop; above it when the staged epilogue uses the whole ring)
-  float* sbias = reinterpret_cast<float*>(smem + (STAGED ? CF::LDS : 0));
+  // loop)
+  float* sbias = reinterpret_cast<float*>(smem);
   if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
     stage_bias<CF>(P, tl, tid, sbias);
     __syncthreads();
   }
-  if constexpr (STAGED)
-    store_tile_staged<CF, EPI>(P, tl, wm, wn, wv, lane, sbias, smem, acc);
+  // bf16: lane pairs into 16-byte chunks (non-temporal for the large plain tiles, whose
+  // outputs the combine or GEMM-2 stream once); fp32: 16 bytes per lane as they are
+  if constexpr (!OF32)
+    store_tile_swapped<CF, EPI, !CF::GATED && CF::BM == 256>(P, tl, wm, wn, lane, sbias, acc);
   else
     store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, sbias, acc);
 }
@@ -449,7 +440,7 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
     }
     // straight from registers, no LDS: the next tile's first requests are in flight
     static_assert((EPI == EPI_SWIGLU || EPI == EPI_STORE) && !OF32, "bf16 SwiGLU or plain tiles");
-    store_tile_swapped<CF, EPI, !CF::GATED>(P, tl, wm, wn, lane, acc);
+    store_tile_swapped<CF, EPI, !CF::GATED>(P, tl, wm, wn, lane, nullptr, acc);
     if (!more) break;
 #pragma unroll
     for (int q = 0; q < NB; ++q)
@@ -585,8 +576,7 @@ moe_status_t launch_gemm_bf16(GemmBatch& b, bool gated, const char* name, hipStr
   // against 139 us as 640 small tiles); else 128 x 128 tiles. On the large tiles the
   // gated (SwiGLU) GEMM and the plain one without bias run persistent blocks (skipping
   // empty tiles, the next tile's first steps requested during the epilogue); with a bias,
-  // one block per tile with the LDS-staged epilogue, whose stores overlap the next
-  // block's start.
+  // one block per tile (the bias is staged in LDS after the K loop).
   using Large = TileCfg<256, 256, true, 4, 4, 2>;
   bool large = true;
   long tiles = 0;

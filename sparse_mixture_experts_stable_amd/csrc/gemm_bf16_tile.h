@@ -386,112 +386,9 @@ __device__ __forceinline__ void store_tile(const GemmProblem& P, const TileId& t
   }
 }
 
-// The epilogue math for 4 consecutive outputs n..n+3 of row m: SwiGLU product, bias
-// (staged `sbias` or, when null, read from the problem's bias vector), GELU.
-template <class CF, int EPI>
-__device__ __forceinline__ void epi_math(const GemmProblem& P, const TileId& t, int nl, int n,
-                                         const float* sbias, const float (&a)[4],
-                                         const float (&b)[4], float (&v)[4]) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = a[r];
-  if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = silu(a[r]) * b[r];
-  }
-  if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
-    if (sbias) {
-      const float4 bb = *reinterpret_cast<const float4*>(sbias + nl);
-      v[0] += bb.x;
-      v[1] += bb.y;
-      v[2] += bb.z;
-      v[3] += bb.w;
-    } else if (P.bias) {
-      // n .. n+3 < N: N is a multiple of 64
-      const uint2 bw = *reinterpret_cast<const uint2*>(
-          static_cast<const bf16_t*>(P.bias) + size_t(t.g) * P.bias_gstride + n);
-      v[0] += bf16_to_f32(bf16_t(bw.x & 0xffff));
-      v[1] += bf16_to_f32(bf16_t(bw.x >> 16));
-      v[2] += bf16_to_f32(bf16_t(bw.y & 0xffff));
-      v[3] += bf16_to_f32(bf16_t(bw.y >> 16));
-    }
-  }
-  if constexpr (EPI == EPI_GELU_BIAS) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
-  }
-}
-
-// bf16 epilogue through LDS: the tile is written to `stage` (the whole LDS ring,
-// CF::LDS bytes, free once the K loop is done) in rounds of R = min(BM, CF::LDS / (2 BNQ))
-// rows (one round for the 256-row tiles: every wave writes its accumulators at once), each
-// lane's 8-byte pieces placed with the 16-byte chunk index XORed by (row % 16), then
-// read back as 16 bytes per lane along whole rows and stored (non-temporal), so every
-// store instruction writes complete row segments. All threads of the block take part
-// (it synchronises); `stage` must be free on entry and is free again on return.
-template <class CF, int EPI>
-__device__ __forceinline__ void store_tile_staged(const GemmProblem& P, const TileId& t, int wm,
-                                                  int wn, int wv, int lane, const float* sbias,
-                                                  char* stage,
-                                                  const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
-  constexpr int RB = CF::BNQ * 2;         // bytes per output row
-  constexpr int CPR = RB / 16;            // 16-byte chunks per row
-  constexpr int R = CF::LDS / RB < CF::BM ? CF::LDS / RB : CF::BM;  // rows per round
-  constexpr int ROUNDS = CF::BM / R;
-  constexpr int LPR = 64 / CPR;           // rows per wave instruction when reading back
-  static_assert(CPR >= 16 && R % CF::WROWS == 0 && CF::BM % R == 0 && CF::WAVES == 16,
-                "staged epilogue shape");
-  const int fr = lane & 15, fc = lane >> 4;
-  char* Cb = static_cast<char*>(P.C);
-#pragma unroll
-  for (int rd = 0; rd < ROUNDS; ++rd) {
-    __syncthreads();  // stage free (previous round stored, or the K loop done with it)
-    if (wm * CF::WROWS >= rd * R && wm * CF::WROWS < (rd + 1) * R) {
-#pragma unroll
-      for (int i = 0; i < CF::TM; ++i) {
-        const int ml = wm * CF::WROWS + i * 16 + fr - rd * R;
-        const int m = t.m0 + rd * R + ml;
-#pragma unroll
-        for (int j = 0; j < CF::TN; ++j) {
-          const int nl = wn * CF::WCOLS + j * 16 + fc * 4;
-          const int n = t.n0 + nl;
-          float a[4], b[4], v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            a[r] = acc[0][i][j][r];
-            b[r] = acc[CF::NB - 1][i][j][r];
-          }
-          if (m < t.M && n < P.N) {
-            epi_math<CF, EPI>(P, t, nl, n, sbias, a, b, v);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = 0.f;
-          }
-          const int bc = nl * 2;  // byte column
-          *reinterpret_cast<uint2*>(stage + ml * RB + 16 * ((bc >> 4) ^ (ml & 15)) + (bc & 15)) =
-              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < R / (16 * LPR); ++q) {
-      const int ml = (wv * (R / 16)) + q * LPR + lane / CPR;  // 16 waves, R/16 rows each
-      const int c = lane % CPR;
-      const int m = t.m0 + rd * R + ml;
-      const int n = t.n0 + 8 * c;
-      // non-temporal: the tile is read back once, by a later kernel, long after this
-      // launch has streamed far more than the caches hold
-      if (m < t.M && n < P.N)
-        __builtin_nontemporal_store(
-            *reinterpret_cast<const u32x4*>(stage + ml * RB + 16 * (c ^ (ml & 15))),
-            reinterpret_cast<u32x4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2));
-    }
-  }
-  __syncthreads();  // every wave has read the stage back
-}
-
-// Epilogue of a bf16 tile without LDS: EPI_STORE (plain) or EPI_SWIGLU (gated) outputs,
-// 16-byte stores straight from registers. After the MFMAs lane (r, g) (r = lane % 16,
+// Epilogue of a bf16 tile without LDS staging: 16-byte stores straight from registers,
+// after the epilogue math (bias from `sbias`, the block's BNQ columns staged in LDS as
+// fp32 with zeros past N; GELU; SwiGLU). After the MFMAs lane (r, g) (r = lane % 16,
 // g = lane / 16) holds columns 16 j + 4 g .. + 3 of row r of every 16 x 16 tile j. For a
 // pair of tiles j0 = 2 p, j1 = j0 + 1 one v_permlane16_swap per dword exchanges the odd
 // 16-lane groups' j0 pieces with the even groups' j1 pieces, after which lane (r, g) holds
@@ -503,10 +400,9 @@ __device__ __forceinline__ void store_tile_staged(const GemmProblem& P, const Ti
 // stores (an output read once, later, by a streaming kernel).
 template <class CF, int EPI, bool NT>
 __device__ __forceinline__ void store_tile_swapped(const GemmProblem& P, const TileId& t, int wm,
-                                                   int wn, int lane,
+                                                   int wn, int lane, const float* sbias,
                                                    const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
   static_assert(CF::TN == 2 || CF::TN == 4, "one or two pairs of tiles");
-  static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU, "no bias in this epilogue");
   constexpr int NP = CF::TN / 2;
   // the lane's addresses are formed here, not hoisted out of the caller's tile loop
   asm volatile("" : "+v"(lane));
@@ -536,6 +432,17 @@ __device__ __forceinline__ void store_tile_swapped(const GemmProblem& P, const T
         for (int r = 0; r < 4; ++r) {
           v[r] = acc[0][i][2 * p + h][r];
           if constexpr (EPI == EPI_SWIGLU) v[r] = silu(v[r]) * acc[CF::NB - 1][i][2 * p + h][r];
+        }
+        if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
+          const float4 bb = *reinterpret_cast<const float4*>(sbias + wn * CF::WCOLS + (2 * p + h) * 16 + fc * 4);
+          v[0] += bb.x;
+          v[1] += bb.y;
+          v[2] += bb.z;
+          v[3] += bb.w;
+        }
+        if constexpr (EPI == EPI_GELU_BIAS) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
         }
         w[h][0] = pack_bf16x2(v[0], v[1]);
         w[h][1] = pack_bf16x2(v[2], v[3]);
