@@ -27,9 +27,10 @@
 // Tiles: the large tile is 256 rows x 256 staged B columns (SwiGLU: 128 gate + 128 up
 // columns of the same outputs) on 16 waves (4 x 4, four per SIMD, each 64 rows x 64
 // staged columns) with five 32 KiB operand slots (160 KiB of LDS, below): large enough
-// that each byte staged feeds 128 FLOPs. The small tile (128 x 128, three stages) serves
-// narrow problems, on 8 waves (64 x 32 each) for plain products such as the router GEMM
-// (4.5 us faster there than 4 waves of 64 x 64) and on 4 for gated ones. The gated
+// that each byte staged feeds 128 FLOPs. The small tile (128 x 128) serves narrow
+// problems, on 8 waves (64 x 32 each) with four stages for plain products such as the
+// router GEMM (4.5 us faster there than 4 waves of 64 x 64; four stages 30.3 us, three
+// 31.7, two 34.7) and on 4 waves with three stages for gated ones. The gated
 // variant holds gate and up accumulators of the same outputs in one lane, so
 // silu(x Wg) * (x Wu) is formed in the epilogue and only the product is written.
 //
@@ -565,7 +566,7 @@ moe_status_t launch_layout(GemmBatch& b, bool gated, bool large, const char* nam
                  : launch_cfg<TileCfg<128, 128, true, 2, 2, 3>, EPI_SWIGLU, false, BKM>(b, name, s);
   }
   return large ? launch_epi<TileCfg<256, 256, false, 4, 4, 2>, BKM>(b, name, s)
-               : launch_epi<TileCfg<128, 128, false, 2, 4, 3>, BKM>(b, name, s);
+               : launch_epi<TileCfg<128, 128, false, 2, 4, 4>, BKM>(b, name, s);
 }
 }  // namespace
 
