@@ -120,9 +120,11 @@ struct ExpertPlan {
   bool two_stage;
 };
 
+// h_pieces: the hidden activation is the library's own (not a caller's hidden_cache),
+// so the bf16 GEMMs keep it in 32-column pieces (GemmProblem::c_pstride / a_pstride).
 void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, int k, int C,
                   const int32_t* slot_assign, const int32_t* used, void* hidden, void* out,
-                  ExpertPlan& pl) {
+                  bool h_pieces, ExpertPlan& pl) {
   const bool dense = slot_assign == nullptr;
   const int rows = dense ? T : C;
   const int E = ex->num_experts, D = ex->d_model, F = ex->d_hidden;
@@ -154,12 +156,15 @@ void plan_experts(const moe_experts_t* ex, const void* x, int64_t ldx, int T, in
     a.C = pl.two_stage ? hidden : out;
     a.ldc = a.N;
     a.c_gstride = int64_t(rows) * a.N;
+    const int64_t pieces = pl.two_stage && h_pieces ? int64_t(rows) * 32 : 0;
+    a.c_pstride = pieces;
     pl.g1 = a;
     if (pl.two_stage) {
       GemmProblem b{};
       b.A = hidden;
       b.lda = F;
       b.a_gstride = int64_t(rows) * F;
+      b.a_pstride = pieces;
       b.row_map = nullptr;
       b.row_div = 1;
       b.m_count = dense ? nullptr : used;
@@ -504,7 +509,8 @@ moe_status_t moe_expert_mlp(const moe_experts_t* ex, const void* x, int64_t ldx,
   }
   if (rows == 0) return MOE_OK;
   ExpertPlan pl;
-  plan_experts(ex, x, ldx, T, k, C, slot_assign, expert_used, hidden, expert_out, pl);
+  plan_experts(ex, x, ldx, T, k, C, slot_assign, expert_used, hidden, expert_out,
+               hidden_cache == nullptr, pl);
   const moe_experts_t* exs[1] = {ex};
   return run_experts(&pl, exs, 1, S(stream));
 }
@@ -621,14 +627,15 @@ moe_status_t moe_forward(const moe_forward_args_t* a, void* ws, size_t ws_bytes,
   int n = 0;
   if (C > 0) {
     plan_experts(&a->experts, a->x, a->ldx, T, k, C, a->slot_assign, a->expert_used,
-                 a->hidden_cache ? a->hidden_cache : f.hidden, a->expert_out, plans[n]);
+                 a->hidden_cache ? a->hidden_cache : f.hidden, a->expert_out,
+                 a->hidden_cache == nullptr, plans[n]);
     exs[n++] = &a->experts;
   }
   void* shared_out = nullptr;
   if (a->shared.w_in) {
     shared_out = a->shared_out ? a->shared_out : f.shared_out;
     plan_experts(&a->shared, a->x, a->ldx, T, 1, 0, nullptr, nullptr, f.shared_hidden,
-                 shared_out, plans[n]);
+                 shared_out, true, plans[n]);
     exs[n++] = &a->shared;
   }
   if (n) {

@@ -111,6 +111,7 @@ template <class CF>
 struct DmaSrc {
   const char* a;              // A of the group (uniform)
   const char* b[CF::NB];      // B matrices of the group (uniform)
+  uint32_t ka_step;           // bytes from one K step of A to the next (uniform)
   uint32_t ao[CF::A_INST];    // per lane: gathered row and swizzled chunk
   uint32_t bo[CF::B_INST];    // per lane: k row and swizzled chunk
 };
@@ -119,7 +120,7 @@ struct DmaSrc {
 // the wave index (uniform).
 template <class CF>
 __device__ __forceinline__ void issue_a(char* __restrict__ dst, const DmaSrc<CF>& S, int kt, int wv) {
-  const size_t ka = size_t(kt) * CF::BK * 2;
+  const size_t ka = size_t(kt) * S.ka_step;
 #pragma unroll
   for (int t = 0; t < CF::A_INST; ++t) {
     const char* g = S.a + ka + S.ao[t];
@@ -275,10 +276,14 @@ template <class CF>
 __device__ __forceinline__ void tile_a_sources(const GemmProblem& P, const TileId& t, int wv, int lane,
                                                const int* rows, DmaSrc<CF>& S) {
   S.a = static_cast<const char*>(P.A) + size_t(t.g) * P.a_gstride * 2;
+  const int64_t ps = P.a_pstride;
+  S.ka_step = ps ? uint32_t(ps * (CF::BK / 32) * 2) : uint32_t(CF::BK * 2);
 #pragma unroll
   for (int i = 0; i < CF::A_INST; ++i) {
     const int row = (wv * CF::A_INST + i) * CF::K_RPI + lane / CF::K_CPR;
-    S.ao[i] = uint32_t((size_t(rows[i]) * P.lda + 8 * ((lane % CF::K_CPR) ^ fswz<CF::K_RB>(row))) * 2);
+    const int c = (lane % CF::K_CPR) ^ fswz<CF::K_RB>(row);  // source chunk of 8 columns
+    S.ao[i] = ps ? uint32_t((size_t(c >> 2) * ps + size_t(rows[i]) * 32 + 8 * (c & 3)) * 2)
+                 : uint32_t((size_t(rows[i]) * P.lda + 8 * c) * 2);
   }
 }
 
@@ -397,7 +402,9 @@ __device__ __forceinline__ void store_tile(const GemmProblem& P, const TileId& t
 // chunk (a DPP rotation by 8 within each 16-lane row), so that each store instruction
 // covers 8 whole 128-byte rows rather than 16 half rows. Every lane takes part in the
 // exchanges (they read other lanes); stores past M or N are skipped. NT: non-temporal
-// stores (an output read once, later, by a streaming kernel).
+// stores (an output read once, later, by a streaming kernel). With C in 32-column pieces
+// (c_pstride) the same chunks land in that layout: the 16 rows of one 32-column strip
+// are then 1 KiB of contiguous memory, one store instruction.
 template <class CF, int EPI, bool NT>
 __device__ __forceinline__ void store_tile_swapped(const GemmProblem& P, const TileId& t, int wm,
                                                    int wn, int lane, const float* sbias,
@@ -410,9 +417,11 @@ __device__ __forceinline__ void store_tile_swapped(const GemmProblem& P, const T
   const bool lo = fr < 8;
   char* Cb = static_cast<char*>(P.C);
   const int n = t.n0 + wn * CF::WCOLS + 8 * (fc >> 1) + 16 * (fc & 1) + (NP == 2 && !lo ? 32 : 0);
+  const int64_t cps = P.c_pstride;
   auto put = [&](int m, const u32x4& val) {
     if (m < t.M && n < P.N) {
-      u32x4* dst = reinterpret_cast<u32x4*>(Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 2);
+      const size_t e = cps ? size_t(n >> 5) * cps + size_t(m) * 32 + (n & 31) : size_t(m) * P.ldc + n;
+      u32x4* dst = reinterpret_cast<u32x4*>(Cb + (size_t(t.g) * P.c_gstride + e) * 2);
       if constexpr (NT)
         __builtin_nontemporal_store(val, dst);
       else

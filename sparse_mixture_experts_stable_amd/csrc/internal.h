@@ -109,6 +109,14 @@ struct GemmProblem {
   int32_t out_f32;  // bf16 kernel: 1 = store fp32 (router logits)
   int32_t tiles;    // groups * m_tiles * n_tiles (filled by the launcher)
   int32_t b_kmajor; // bf16 kernel: B stored [N][K] per group (k contiguous), else [K][N]
+  // bf16 kernel: A (a_pstride) or C (c_pstride) stored in 32-column pieces when nonzero,
+  // element (r, c) of group g at g*gstride + (c / 32)*pstride + r*32 + c % 32, pstride =
+  // 32 * rows of the group's buffer (lda / ldc unused). The hidden activation between the
+  // two expert GEMMs when it stays inside the library: a 32-column output strip of a wave
+  // then fills whole 128-byte lines, two rows each, and the next GEMM still reads whole
+  // lines per K step.
+  int64_t a_pstride;
+  int64_t c_pstride;
 };
 
 struct GemmBatch {

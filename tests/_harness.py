@@ -92,9 +92,11 @@ def oracle_shared(inp):
             "w_out": to_numpy_f32(inp["shared_w_out"])}
 
 
-def run_forward(w, inp, g=None, layout="in_out"):
+def run_forward(w, inp, g=None, layout="in_out", keep_hidden=False):
     """moe_forward on the workload's inputs; the layouts other than "in_out" hand the
-    weights named by _layouts over transposed, with their OUT_IN flags (same products)."""
+    weights named by _layouts over transposed, with their OUT_IN flags (same products).
+    keep_hidden: pass a hidden_cache (returned as "hidden"); without one the hidden
+    activation stays in the workspace, as in the benchmark."""
     from sparse_mixture_experts_stable_amd import ops
     g = g if g is not None else gpu_inputs(inp)
     C = ops.capacity(w.T, w.k, w.E, w.cf)
@@ -105,7 +107,7 @@ def run_forward(w, inp, g=None, layout="in_out"):
         kw["w_router"] = g["w_router"]
     out = ops.forward(g["x"], experts_dict(w, g, layout), k=w.k, capacity=C,
                       shared=shared_dict(w, g, layout), use_residual=w.residual,
-                      keep_hidden=True, keep_shared_out=True, **kw)
+                      keep_hidden=keep_hidden, keep_shared_out=True, **kw)
     torch.cuda.synchronize()
     return out, g
 

@@ -163,6 +163,35 @@ def test_forward_mid_size_large_tiles(case, layout):
     H.check_outputs(w, inp, h, r, d)
 
 
+@pytest.mark.parametrize("case", ["swiglu_shared_k8", "gelu_bias"])
+def test_forward_hidden_cache_layout(case):
+    """With a caller's hidden_cache the hidden activation is written row-major ([E, C, F]);
+    without one the library keeps it in 32-column pieces. Both runs give the same outputs
+    bit for bit (the same products in the same order), and the returned hidden rows
+    reproduce the expert outputs: expert_out[e] = hidden[e] W_out[e] (+ b_out) in
+    float64, to the bf16 tolerance ("Sparse MoE Layer in NumPy", section 2 forward)."""
+    w = MID[case]
+    inp = make_inputs(w)
+    a, g = H.run_forward(w, inp)
+    b, _ = H.run_forward(w, inp, g=g, keep_hidden=True)
+    used = a["expert_used"].cpu().numpy()
+    assert torch.equal(b["expert_used"], a["expert_used"])
+    for key in ("y", "shared_out"):
+        if a.get(key) is not None:
+            assert torch.equal(a[key], b[key]), key
+    for e in range(w.E):
+        assert torch.equal(a["expert_out"][e, : used[e]], b["expert_out"][e, : used[e]]), e
+    wts = H.oracle_weights(inp)
+    hid = b["hidden"].float().cpu().numpy().astype(np.float64)
+    out = b["expert_out"].float().cpu().numpy()
+    for e in sorted({0, w.E // 2, w.E - 1, int(np.argmax(used))}):
+        u = int(used[e])
+        want = hid[e, :u] @ wts["w_out"][e].astype(np.float64)
+        if w.kind == "gelu":
+            want = want + wts["b_out"][e].astype(np.float64)
+        H.assert_close(out[e, :u], want, H.RTOL["bf16"], f"expert_out[{e}] from hidden")
+
+
 # Large-tile cases whose K is a single 64-wide step in one GEMM: the persistent kernel
 # needs two K steps per tile, so that GEMM runs one block per tile (with the operand
 # slots) instead. d_model 64: GEMM-1 (gated, large tiles); d_hidden 64: GEMM-2.

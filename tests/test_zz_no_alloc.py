@@ -35,7 +35,7 @@ def _run_both(w):
     from sparse_mixture_experts_stable_amd import _lib as L
     from sparse_mixture_experts_stable_amd import ops
     inp = make_inputs(w)
-    ref, g = H.run_forward(w, inp)
+    ref, g = H.run_forward(w, inp, keep_hidden=True)
     a = ref["_call"].args
     b = L.ForwardArgs.from_buffer_copy(a)
     got = {}
