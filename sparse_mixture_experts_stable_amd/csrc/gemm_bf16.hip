@@ -281,10 +281,12 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_kernel(GemmBatch bat
   }
   // bf16: lane pairs into 16-byte chunks (non-temporal for the large plain tiles, whose
   // outputs the combine or GEMM-2 stream once); fp32: 16 bytes per lane as they are
-  if constexpr (!OF32)
+  if constexpr (!OF32) {
     store_tile_swapped<CF, EPI, !CF::GATED && CF::BM == 256>(P, tl, wm, wn, lane, sbias, acc);
-  else
-    store_tile<CF, EPI, OF32>(P, tl, wm, wn, lane, sbias, acc);
+  } else {
+    static_assert(EPI == EPI_STORE, "fp32 output without epilogue math");
+    store_tile_f32<CF>(P, tl, wm, wn, lane, acc);
+  }
 }
 
 // Longest tile list a persistent block holds (one register per lane, 16-bit tile ids).

@@ -333,60 +333,29 @@ __device__ __forceinline__ void tile_sources(const GemmProblem& P, const TileId&
   tile_sources_from_rows<CF, BKM>(P, t, wv, lane, rows, S);
 }
 
-// Epilogue: lane holds C[m][n..n+3] of every MFMA tile (the MFMA ran with B as its first
-// operand, so each tile comes out transposed). For EPI_BIAS / EPI_GELU_BIAS the bias
-// comes from `sbias` (the block's BNQ values staged in LDS) or, when `sbias` is null,
-// straight from the problem's bias vector.
-template <class CF, int EPI, bool OF32>
-__device__ __forceinline__ void store_tile(const GemmProblem& P, const TileId& t, int wm, int wn,
-                                           int lane, const float* sbias,
-                                           const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+// fp32 epilogue (the router logits, EPI_STORE): lane holds C[m][n..n+3] of every MFMA
+// tile (the MFMA ran with B as its first operand, so each tile comes out transposed),
+// stored as 16 bytes per lane.
+template <class CF>
+__device__ __forceinline__ void store_tile_f32(const GemmProblem& P, const TileId& t, int wm,
+                                               int wn, int lane,
+                                               const f32x4 (&acc)[CF::NB][CF::TM][CF::TN]) {
+  static_assert(!CF::GATED, "plain products only");
   const int fr = lane & 15, fc = lane >> 4;
   char* Cb = static_cast<char*>(P.C);
-  constexpr int es = OF32 ? 4 : 2;
 #pragma unroll
   for (int i = 0; i < CF::TM; ++i) {
     const int m = t.m0 + wm * CF::WROWS + i * 16 + fr;
     if (m >= t.M) continue;
 #pragma unroll
     for (int j = 0; j < CF::TN; ++j) {
-      const int nl = wn * CF::WCOLS + j * 16 + fc * 4;
-      const int n = t.n0 + nl;
+      const int n = t.n0 + wn * CF::WCOLS + j * 16 + fc * 4;
       if (n >= P.N) continue;
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = acc[0][i][j][r];
-      if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = silu(v[r]) * acc[CF::NB - 1][i][j][r];
-      }
-      if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU_BIAS) {
-        if (sbias) {
-          const float4 bb = *reinterpret_cast<const float4*>(sbias + nl);
-          v[0] += bb.x;
-          v[1] += bb.y;
-          v[2] += bb.z;
-          v[3] += bb.w;
-        } else if (P.bias) {
-          // n .. n+3 < N: N is a multiple of 64
-          const uint2 bw = *reinterpret_cast<const uint2*>(
-              static_cast<const bf16_t*>(P.bias) + size_t(t.g) * P.bias_gstride + n);
-          v[0] += bf16_to_f32(bf16_t(bw.x & 0xffff));
-          v[1] += bf16_to_f32(bf16_t(bw.x >> 16));
-          v[2] += bf16_to_f32(bf16_t(bw.y & 0xffff));
-          v[3] += bf16_to_f32(bf16_t(bw.y >> 16));
-        }
-      }
-      if constexpr (EPI == EPI_GELU_BIAS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = gelu_erf(v[r]);
-      }
-      char* dst = Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * es;
-      if constexpr (OF32) {
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
+      char* dst = Cb + (size_t(t.g) * P.c_gstride + size_t(m) * P.ldc + n) * 4;
+      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
