@@ -98,6 +98,23 @@ def parse():
                          "--kernel-trace CSV (kernel_trace.csv), over the last --last dispatches "
                          "of each kernel name")
     ap.add_argument("--last", type=int, default=40)
+    ap.add_argument("--summarize-traffic", nargs=2, default=None, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="instead of running: HBM bytes per launch of every moe kernel from two "
+                         "rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE; "
+                         "counter_collection.csv), calibrated on the largest device copy of the "
+                         "run (--calib-copy-mib), as a markdown table")
+    ap.add_argument("--record", default=None, metavar="KEY=KERNEL",
+                    help="with --summarize-traffic: store the bytes per launch of the kernel "
+                         "whose name contains KERNEL in profiles/traffic.json under KEY (with "
+                         "the current GEMM source hash)")
+    ap.add_argument("--summarize-mfma", default=None, metavar="CSV",
+                    help="instead of running: MFMA work, MFMA busy fraction and engine clock per "
+                         "GEMM dispatch from a rocprofv3 --pmc pass over "
+                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES "
+                         "GRBM_GUI_ACTIVE, as a markdown table")
+    ap.add_argument("--algo", action="append", default=[], metavar="KERNEL=GFLOP",
+                    help="with --summarize-mfma: algorithmic GFLOP per launch of the kernel "
+                         "whose name contains KERNEL")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MiB (a "
                          "known-size reference for hardware byte counters)")
@@ -316,10 +333,109 @@ def summarize_trace(path, last):
               f"{max(tail):.1f} | {statistics.mean(ds):.1f} |")
 
 
+def _short_name(n):
+    return n.replace("void ", "").split("(")[0]
+
+
+def _pmc_rows(path):
+    import csv
+    return list(csv.DictReader(open(path)))
+
+
+def summarize_traffic(fetch_csv, write_csv, record=None):
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
+    by what the counter reads for the run's largest device copy (a copy of G bytes reads
+    G and writes G): average over every profiled launch of each moe kernel."""
+    import statistics
+
+    def per_kernel(path):
+        out = {}
+        for r in _pmc_rows(path):
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    fe, wr = per_kernel(fetch_csv), per_kernel(write_csv)
+
+    def copy_counter(vals):
+        c = [x for n, v in vals.items() if n.startswith("__amd_rocclr_copyBuffer") for x in v]
+        if not c:
+            sys.exit("no device copy in the counter pass (run it with --calib-copy-mib)")
+        return max(c)
+
+    cf, cw = copy_counter(fe), copy_counter(wr)
+    gib_kib = (1 << 30) / 1024.0
+    ffac, wfac = gib_kib / cf, gib_kib / cw   # calibrated KiB per counter unit (1 GiB copy)
+    rows = []
+    for n in fe:
+        if "moe::" not in n:
+            continue
+        rd = statistics.mean(fe[n]) * ffac * 1024
+        wt = statistics.mean(wr.get(n, [0.0])) * wfac * 1024
+        rows.append((n, len(fe[n]), rd, wt))
+    rows.sort(key=lambda r: -(r[2] + r[3]))
+    print(f"Calibration: the 1 GiB device copy (`__amd_rocclr_copyBuffer`, 1 GiB read and 1 GiB "
+          f"written) reads FETCH_SIZE = {cf:.0f} KiB and WRITE_SIZE = {cw:.0f} KiB, so measured "
+          f"bytes = FETCH_SIZE x {ffac:.3f} KiB and WRITE_SIZE x {wfac:.3f} KiB.\n")
+    print("| kernel | launches | read MB (calibrated) | written MB (calibrated) |")
+    print("|---|---|---|---|")
+    for n, c, rd, wt in rows:
+        print(f"| `{_short_name(n)}` | {c} | {rd / 1e6:.1f} | {wt / 1e6:.1f} |")
+    if record:
+        key, sub = record.split("=", 1)
+        hit = [r for r in rows if sub in r[0]]
+        if len(hit) != 1:
+            sys.exit(f"--record: {len(hit)} kernels match {sub!r}")
+        name, _, rd, wt = hit[0]
+        srcs = ("gemm_f32.hip",) if "gemm_f32" in name else ("gemm_bf16.hip", "gemm_bf16_tile.h")
+        p = os.path.join(ROOT, "profiles", "traffic.json")
+        recs = json.load(open(p)) if os.path.exists(p) else {}
+        recs[key] = {"bytes_per_launch": int(rd + wt), "read_bytes": int(rd), "written_bytes": int(wt),
+                     "source_hash": source_hash(*srcs),
+                     "calibration": {"fetch_kib_factor": round(ffac, 4), "write_kib_factor": round(wfac, 4)}}
+        with open(p, "w") as f:
+            json.dump(recs, f, indent=1)
+            f.write("\n")
+
+
+def summarize_mfma(path, algo):
+    """Per GEMM kernel, over its last 6 profiled dispatches: MFMA FLOPs (MOPS x 512),
+    MFMA busy against 2.4 GHz and against the engine clock of the dispatch
+    (GRBM_GUI_ACTIVE / 8 XCDs / duration)."""
+    import statistics
+    d = {}
+    for r in _pmc_rows(path):
+        e = d.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "start": int(r["Start_Timestamp"]),
+                                             "end": int(r["End_Timestamp"])})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    per = {}
+    for e in d.values():
+        if "moe::" in e["name"] and "gemm" in e["name"]:
+            per.setdefault(_short_name(e["name"]), []).append(e)
+    algo = dict(a.split("=", 1) for a in algo)
+    print("| kernel | launches | MFMA FLOPs (G) | algorithmic (G) | duration (us) | MFMA busy | "
+          "clock (GHz) | busy at that clock |")
+    print("|---|---|---|---|---|---|---|---|")
+    for n, es in sorted(per.items(), key=lambda kv: -statistics.mean(x["end"] - x["start"] for x in kv[1])):
+        es = es[-6:]
+        dur = statistics.mean((x["end"] - x["start"]) * 1e-9 for x in es)
+        fl = statistics.mean(x.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for x in es) * 512
+        busy = statistics.mean(x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in es)
+        clk = statistics.mean(x.get("GRBM_GUI_ACTIVE", 0.0) for x in es) / 8 / dur
+        a = next((v for k, v in algo.items() if k in n), "-")
+        print(f"| `{n}` | {len(es)} | {fl / 1e9:.1f} | {a} | {dur * 1e6:.1f} | "
+              f"{busy / (1024 * 2.4e9 * dur):.1%} | {clk / 1e9:.2f} | {busy / (1024 * clk * dur):.1%} |")
+
+
 def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.last)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, record=args.record)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.algo)
         return
     if args.vendor_gemm:
         vendor_gemm(args.steps)
