@@ -212,7 +212,8 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t
  * num_experts must be 1, expert_used ignored, outputs are [T, ...]).
  *   x            device, [T, ldx] of ex->dtype.
  *   hidden_cache device, [E, C, F] of ex->dtype (the activation fed to the second
- *                GEMM), or NULL to keep it in the workspace. Ignored for LINEAR.
+ *                GEMM), or NULL to keep it in the workspace (bf16: in an internal
+ *                layout of 32-column pieces, not meant to be read). Ignored for LINEAR.
  *   expert_out   device, [E, C, D] of ex->dtype, ungated.
  *   ws           >= moe_expert_mlp_workspace_size(ex, rows) bytes, rows = C or T.
  */
