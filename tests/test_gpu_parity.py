@@ -148,6 +148,10 @@ MID = {
     # skewed routing (Zipf bias, quarter-grid ties): most experts far below one row tile,
     # a few full; C = 2048
     "swiglu_zipf": WORKLOADS[4].scaled(T=16384, D=512, E=16, F=512),
+    # widths that are not multiples of the tile: d_model and d_hidden 320 (five K steps,
+    # a last column tile a quarter or half full, partial 32-column hidden pieces per tile)
+    "swiglu_ragged_n": WORKLOADS[3].scaled(T=8192, D=320, E=8, k=2, F=320, shared_F=320),
+    "gelu_ragged_n": WORKLOADS[2].scaled(T=8192, D=320, E=8, F=320),
 }
 
 
