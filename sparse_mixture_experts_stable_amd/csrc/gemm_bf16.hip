@@ -441,9 +441,11 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_bf16_persistent_kernel(Ge
       sa = da;
       sb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;
     }
-    // straight from registers, no LDS: the next tile's first requests are in flight
+    // straight from registers, no LDS: the next tile's first requests are in flight.
+    // Non-temporal: H and the expert outputs are read once, by the next kernel (H with
+    // normal stores held L2 lines the operand loads share: GEMM-1 about 1% slower).
     static_assert((EPI == EPI_SWIGLU || EPI == EPI_STORE) && !OF32, "bf16 SwiGLU or plain tiles");
-    store_tile_swapped<CF, EPI, !CF::GATED>(P, tl, wm, wn, lane, nullptr, acc);
+    store_tile_swapped<CF, EPI, true>(P, tl, wm, wn, lane, nullptr, acc);
     if (!more) break;
 #pragma unroll
     for (int q = 0; q < NB; ++q)
