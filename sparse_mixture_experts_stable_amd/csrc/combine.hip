@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ resi
     const int rows_per_block = 256 / per_row;
     t = blockIdx.x * rows_per_block + threadIdx.x / per_row;
     col = (threadIdx.x % per_row) * V;
-    if (threadIdx.x >= rows_per_block * per_row) return;
+    if (int(threadIdx.x) >= rows_per_block * per_row) return;
   }
   if (t >= T_) return;
   float acc[V];
